@@ -1,0 +1,243 @@
+/*
+ * Plain CPU oracle for the blockwise 4-bit skinny GEMM and its bf16 sibling.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the CPU-baseline leg of the benchmark may load this library.  The GPU
+ * library never links, includes or calls it, and it shares no code with the
+ * GPU library (no headers, tables or helpers).
+ *
+ * Everything here is written for obviousness, not speed: scalar loops, fp64
+ * accumulation in increasing k, one output element at a time.  The only
+ * concession to run time is an OpenMP loop over output columns, which does not
+ * change any result (each element is still one sequential sum).
+ *
+ * Sources (web pages, by title and section):
+ *  - "[ROCm] Optimize kgemm_4bit_inference_naive for ROCm, use it for batch
+ *    sizes other than 1" (bitsandbytes pull request 1920), sections "Technical
+ *    details" and the maintainer's comment on the replacement kernel: the
+ *    computation is a fused dequantize + matmul over blockwise 4-bit weights
+ *    looked up in a 16-entry NF4/FP4 table, blocksize 64 by default, fp32
+ *    accumulation, "TN" inference layout A[M,K] * W[N,K]^T.
+ *  - "Support N=5 in wvSplitK skinny GEMM kernels for speculative decoding"
+ *    (vLLM pull request 40687 report), section "关键源码片段": bf16 skinny GEMM of
+ *    a weight W[out,K] with 1..5 token rows and an optional bias.
+ *
+ * Readings where the pages are silent (each is also listed in the design
+ * notes):
+ *  - nibble order: the low nibble of byte j holds even k = 2j, the high nibble
+ *    holds odd k = 2j + 1;
+ *  - a quantization block runs along K inside one row (K % blocksize == 0), so
+ *    block b of row n covers k in [b*bs, (b+1)*bs) and its scale is
+ *    absmax[n * (K/bs) + b];
+ *  - a dequantized weight is one IEEE binary32 product codebook[code]*absmax;
+ *    the bf16 dequantized weight is that product rounded to bf16 with
+ *    round-to-nearest-even;
+ *  - activations, weights and bias in bf16 are widened exactly to fp32/fp64.
+ *
+ * Compiled with -O2 -ffp-contract=off (no fused multiply-add anywhere) and
+ * without -ffast-math, so fp32 denormals are kept.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+/* A bf16 value is the top half of an fp32 bit pattern: widening is exact. */
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ---- O1: unpack one 4-bit code ------------------------------------------ */
+/* Row n of the packed matrix holds K/2 bytes.  Byte j carries k = 2j in its
+ * low nibble and k = 2j + 1 in its high nibble. */
+int oracle_code(const uint8_t *Wpacked, int64_t K, int64_t n, int64_t k)
+{
+    uint8_t byte = Wpacked[n * (K / 2) + k / 2];
+    if (k % 2 == 0)
+        return byte & 0x0F;
+    return (byte >> 4) & 0x0F;
+}
+
+void oracle_unpack(const uint8_t *Wpacked, int64_t N, int64_t K, uint8_t *codes)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            codes[n * K + k] = (uint8_t)oracle_code(Wpacked, K, n, k);
+}
+
+/* ---- O2: which absmax scales element (n, k) ----------------------------- */
+int64_t oracle_block_index(int64_t K, int64_t bs, int64_t n, int64_t k)
+{
+    return n * (K / bs) + k / bs;
+}
+
+/* ---- O3: fp32 dequantized weight ---------------------------------------- */
+/* One binary32 multiply, rounded to nearest even (the C default).  The
+ * volatile store keeps the product a separate, rounded fp32 value. */
+float oracle_w32(const uint8_t *Wpacked, const float *absmax, const float *codebook,
+                 int64_t K, int64_t bs, int64_t n, int64_t k)
+{
+    int code = oracle_code(Wpacked, K, n, k);
+    float scale = absmax[oracle_block_index(K, bs, n, k)];
+    volatile float w = codebook[code] * scale;
+    return w;
+}
+
+void oracle_dequant_f32(const uint8_t *Wpacked, const float *absmax, const float *codebook,
+                        int64_t N, int64_t K, int64_t bs, float *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            out[n * K + k] = oracle_w32(Wpacked, absmax, codebook, K, bs, n, k);
+}
+
+/* ---- O4: fp32 -> bf16, round to nearest, ties to even ------------------- */
+/* Keep the top 16 bits of the fp32 pattern.  The discarded low half decides:
+ * above half an ulp rounds up, below rounds down, exactly half rounds to the
+ * even neighbour.  A NaN stays a NaN (quiet bit forced).  Rounding up may
+ * carry into the exponent, which correctly yields the next binade or inf. */
+uint16_t oracle_f32_to_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint32_t exp_bits = (u >> 23) & 0xFF;
+    uint32_t man_bits = u & 0x7FFFFF;
+    if (exp_bits == 0xFF && man_bits != 0)
+        return (uint16_t)((u >> 16) | 0x0040);
+    uint32_t upper = u >> 16;
+    uint32_t lower = u & 0xFFFF;
+    if (lower > 0x8000 || (lower == 0x8000 && (upper & 1) != 0))
+        upper += 1;
+    return (uint16_t)upper;
+}
+
+void oracle_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f32_to_bf16(x[i]);
+}
+
+void oracle_dequant_bf16(const uint8_t *Wpacked, const float *absmax, const float *codebook,
+                         int64_t N, int64_t K, int64_t bs, uint16_t *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            out[n * K + k] = oracle_f32_to_bf16(oracle_w32(Wpacked, absmax, codebook, K, bs, n, k));
+}
+
+/* ---- O5: the fused 4-bit GEMM, judged reference ------------------------- */
+/* C[m, j] = sum over k of a[m,k] * w32(cols[j], k), summed in fp64 in
+ * increasing k.  Every product is exact in fp64 (8-bit by 24-bit
+ * significands), so the only rounding is in the running fp64 sum.  S[m, j] is
+ * the same sum over absolute values, the scale of the tolerance.  cols lists
+ * the output columns to compute (NULL = all N, in order); C and S are
+ * [M, ncols] row-major. */
+void oracle_q4_gemm(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                    const float *codebook, int64_t M, int64_t N, int64_t K, int64_t bs,
+                    const int64_t *cols, int64_t ncols, double *C, double *S)
+{
+    if (cols == NULL)
+        ncols = N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0, sum_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double a = bf16_to_double(A[m * K + k]);
+                double w = (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k);
+                double p = a * w;
+                sum += p;
+                sum_abs += fabs(p);
+            }
+            C[m * ncols + j] = sum;
+            if (S)
+                S[m * ncols + j] = sum_abs;
+        }
+    }
+}
+
+/* ---- O7: the same GEMM on bf16-rounded weights (split-path diagnostic) --- */
+void oracle_q4_gemm_w16(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                        const float *codebook, int64_t M, int64_t N, int64_t K, int64_t bs,
+                        const int64_t *cols, int64_t ncols, double *C, double *S)
+{
+    if (cols == NULL)
+        ncols = N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0, sum_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double a = bf16_to_double(A[m * K + k]);
+                uint16_t w16 = oracle_f32_to_bf16(
+                    oracle_w32(Wpacked, absmax, codebook, K, bs, n, k));
+                double p = a * bf16_to_double(w16);
+                sum += p;
+                sum_abs += fabs(p);
+            }
+            C[m * ncols + j] = sum;
+            if (S)
+                S[m * ncols + j] = sum_abs;
+        }
+    }
+}
+
+/* ---- O6: bf16 GEMM with optional bias ----------------------------------- */
+/* C[m, j] = sum over k of a[m,k] * W[cols[j], k] (+ bias[cols[j]]), fp64 in
+ * increasing k, bias added last.  S includes |bias|. */
+void oracle_bf16_gemm(const uint16_t *A, const uint16_t *W, const uint16_t *bias,
+                      int64_t M, int64_t N, int64_t K, const int64_t *cols, int64_t ncols,
+                      double *C, double *S)
+{
+    if (cols == NULL)
+        ncols = N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0, sum_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = bf16_to_double(A[m * K + k]) * bf16_to_double(W[n * K + k]);
+                sum += p;
+                sum_abs += fabs(p);
+            }
+            if (bias) {
+                double b = bf16_to_double(bias[n]);
+                sum += b;
+                sum_abs += fabs(b);
+            }
+            C[m * ncols + j] = sum;
+            if (S)
+                S[m * ncols + j] = sum_abs;
+        }
+    }
+}
+
+/* ---- O8 building block: plain fp64 GEMM over an fp32 weight matrix ------ */
+/* Used to check that dequantize-then-multiply equals the fused oracle. */
+void oracle_gemm_f32w(const uint16_t *A, const float *W, int64_t M, int64_t N, int64_t K,
+                      double *C)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; k++)
+                sum += bf16_to_double(A[m * K + k]) * (double)W[n * K + k];
+            C[m * N + n] = sum;
+        }
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

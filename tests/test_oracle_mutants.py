@@ -1,0 +1,65 @@
+"""Each plausible mistake planted in a copy of oracle.c must trip a pin.
+
+The copies are compiled on the CPU into a temporary directory; the real oracle
+is never modified.  A mutant that passes every pin would mean the pins cannot
+tell that mistake from the correct oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "nibble_order_swapped": ("if (k % 2 == 0)\n        return byte & 0x0F;",
+                             "if (k % 2 == 1)\n        return byte & 0x0F;"),
+    "row_stride_in_codes": ("Wpacked[n * (K / 2) + k / 2]", "Wpacked[n * K / 4 + k / 2]"),
+    "block_index_by_byte": ("return n * (K / bs) + k / bs;", "return n * (K / bs) + (k / 2) / bs;"),
+    "block_index_transposed": ("return n * (K / bs) + k / bs;", "return n + (k / bs) * (K / bs);"),
+    "absmax_dropped": ("volatile float w = codebook[code] * scale;",
+                       "volatile float w = codebook[code] + 0.0f * scale;"),
+    "code_off_by_one": ("volatile float w = codebook[code] * scale;",
+                        "volatile float w = codebook[(code + 1) & 15] * scale;"),
+    "product_at_bf16_precision": ("volatile float w = codebook[code] * scale;",
+                                  "union { float f; uint32_t u; } cvt = { codebook[code] * scale };\n"
+                                  "    cvt.u &= 0xFFFF0000u;\n    volatile float w = cvt.f;"),
+    "bf16_truncates": ("if (lower > 0x8000 || (lower == 0x8000 && (upper & 1) != 0))",
+                       "if (0)"),
+    "bf16_ties_away": ("if (lower > 0x8000 || (lower == 0x8000 && (upper & 1) != 0))",
+                       "if (lower >= 0x8000)"),
+    "bf16_nan_to_inf": ("return (uint16_t)((u >> 16) | 0x0040);", "return (uint16_t)(u >> 16);"),
+    "q4_sum_in_float": ("double sum = 0.0, sum_abs = 0.0;\n            for (int64_t k = 0; k < K; k++) {\n                double a = bf16_to_double(A[m * K + k]);\n                double w = (double)oracle_w32",
+                        "float sum = 0.0, sum_abs = 0.0;\n            for (int64_t k = 0; k < K; k++) {\n                double a = bf16_to_double(A[m * K + k]);\n                double w = (double)oracle_w32"),
+    "q4_a_transposed": ("double a = bf16_to_double(A[m * K + k]);\n                double w = (double)oracle_w32",
+                        "double a = bf16_to_double(A[k * M + m]);\n                double w = (double)oracle_w32"),
+    "q4_skips_last_k": ("double w = (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k);\n                double p = a * w;",
+                        "double w = (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k);\n                double p = (k == K - 1) ? 0.0 : a * w;"),
+    "bias_dropped": ("sum += b;", "sum += 0.0 * b;"),
+    "bf16_w_transposed": ("bf16_to_double(W[n * K + k])", "bf16_to_double(W[k * N + n])"),
+    "w16_not_rounded": ("double p = a * bf16_to_double(w16);",
+                        "double p = a * (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k) + 0.0 * w16;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) >= 1, "mutation anchor not found: " + name
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new, 1))
+    lib = oracle.compile_c(str(src), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, "no pin notices the planted mistake " + name
