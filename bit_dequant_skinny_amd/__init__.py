@@ -1,0 +1,184 @@
+"""Python binding of the q4skinny HIP library (MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libq4skinny.so``.  torch provides device memory and the current
+stream.  There is no CPU fallback: if the library is missing, importing the
+functions below raises.
+
+Entry points (same names as the C ABI in include/q4skinny.h):
+  q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize=64, out=None, path="auto")
+  bf16_gemm_skinny(A, W, bias=None, out=None)
+  q4_dequant(Wpacked, absmax, codebook, blocksize=64, out_dtype=torch.bfloat16, out=None)
+  q4_get_crossover_m() / q4_set_crossover_m(m) / q4_release_workspace()
+  q4_copy_probe(src, dst) / q4_version()
+``lib()`` returns the raw ctypes handle for callers that pass pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4skinny.so")
+
+Q4_OK, Q4_ERR_INVALID_ARGUMENT, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = 0, 1, 2, 3
+Q4_DTYPE_BF16, Q4_DTYPE_FP32 = 0, 1
+PATHS = {"auto": 0, "fused": 1, "split": 2}
+FUSED_MAX_M = 16
+
+# Every symbol include/q4skinny.h declares.
+EXPORTS = (
+    "q4_gemm_skinny", "q4_gemm_skinny_path", "bf16_gemm_skinny", "q4_dequant",
+    "q4_get_crossover_m", "q4_set_crossover_m", "q4_release_workspace", "q4_last_error",
+    "q4_copy_probe", "q4_version",
+)
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("q4skinny status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libq4skinny.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libq4skinny.so is not built; run python -m bit_dequant_skinny_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.q4_gemm_skinny.argtypes = [P, P, P, P, I, I, I, I, P, P]
+        L.q4_gemm_skinny_path.argtypes = [P, P, P, P, I, I, I, I, P, P, I]
+        L.bf16_gemm_skinny.argtypes = [P, P, P, I, I, I, P, P]
+        L.q4_dequant.argtypes = [P, P, P, I, I, I, P, I, P]
+        L.q4_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
+        L.q4_set_crossover_m.argtypes = [I]
+        for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "bf16_gemm_skinny", "q4_dequant",
+                     "q4_copy_probe", "q4_set_crossover_m", "q4_release_workspace"):
+            getattr(L, name).restype = ctypes.c_int
+        L.q4_get_crossover_m.restype = ctypes.c_int
+        L.q4_last_error.restype = ctypes.c_char_p
+        L.q4_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != Q4_OK:
+        raise Q4Error(status, lib().q4_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, name, dtype):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, path: str = "auto"):
+    """C[M,N] = A[M,K] * dequant(W)[N,K]^T in bf16 (fp32 accumulation)."""
+    torch = _torch()
+    if A.dim() != 2 or Wpacked.dim() != 2:
+        raise ValueError("A must be [M, K] and Wpacked [N, K/2]")
+    M, K = A.shape
+    N = Wpacked.shape[0]
+    if Wpacked.shape[1] * 2 != K:
+        raise ValueError("Wpacked must be [N, K/2]")
+    if blocksize > 0 and K % blocksize == 0 and tuple(absmax.shape) != (N, K // blocksize):
+        raise ValueError("absmax must be [N, K/blocksize]")
+    if codebook.numel() != 16:
+        raise ValueError("codebook must hold 16 entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check(lib().q4_gemm_skinny_path(
+        _dev(A, "A", torch.bfloat16), _dev(Wpacked, "Wpacked", torch.uint8),
+        _dev(absmax, "absmax", torch.float32), _dev(codebook, "codebook", torch.float32),
+        M, N, K, blocksize, _dev(out, "out", torch.bfloat16), _stream(A), PATHS[path]))
+    return out
+
+
+def bf16_gemm_skinny(A, W, bias=None, out=None):
+    """C[M,N] = A[M,K] * W[N,K]^T (+ bias) in bf16, M <= 5."""
+    torch = _torch()
+    if A.dim() != 2 or W.dim() != 2 or A.shape[1] != W.shape[1]:
+        raise ValueError("A must be [M, K] and W [N, K]")
+    M, K = A.shape
+    N = W.shape[0]
+    if bias is not None and tuple(bias.shape) != (N,):
+        raise ValueError("bias must be [N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    bptr = None if bias is None else _dev(bias, "bias", torch.bfloat16)
+    _check(lib().bf16_gemm_skinny(
+        _dev(A, "A", torch.bfloat16), _dev(W, "W", torch.bfloat16), bptr, M, N, K,
+        _dev(out, "out", torch.bfloat16), _stream(A)))
+    return out
+
+
+def q4_dequant(Wpacked, absmax, codebook, blocksize: int = 64, out_dtype=None, out=None):
+    """W[N,K] = codebook[code] * absmax, as bf16 (default) or fp32."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    N, K = Wpacked.shape[0], Wpacked.shape[1] * 2
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=Wpacked.device)
+    elif tuple(out.shape) != (N, K) or out.dtype != out_dtype:
+        raise ValueError("out must be [N, K] of out_dtype")
+    code = Q4_DTYPE_BF16 if out_dtype == torch.bfloat16 else Q4_DTYPE_FP32
+    _check(lib().q4_dequant(
+        _dev(Wpacked, "Wpacked", torch.uint8), _dev(absmax, "absmax", torch.float32),
+        _dev(codebook, "codebook", torch.float32), N, K, blocksize, _dev(out, "out", out_dtype),
+        code, _stream(Wpacked)))
+    return out
+
+
+def q4_copy_probe(src, dst):
+    torch = _torch()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib().q4_copy_probe(_dev(src, "src", src.dtype), _dev(dst, "dst", dst.dtype), nbytes,
+                               _stream(src)))
+    del torch
+    return dst
+
+
+def q4_get_crossover_m() -> int:
+    return int(lib().q4_get_crossover_m())
+
+
+def q4_set_crossover_m(m: int) -> None:
+    _check(lib().q4_set_crossover_m(int(m)))
+
+
+def q4_release_workspace() -> None:
+    _check(lib().q4_release_workspace())
+
+
+def q4_version() -> str:
+    return lib().q4_version().decode()

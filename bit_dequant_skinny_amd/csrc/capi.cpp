@@ -1,0 +1,344 @@
+// C-ABI layer of q4skinny: argument validation, path dispatch, split-path
+// workspace, HIP error capture.  Declared in include/q4skinny.h.
+//
+// Error convention (after the bitsandbytes int8 pull request "Cache the
+// hipBLASLt int8 matmul algo per problem on ROCm", which returns a status code
+// the caller acts on and drains the sticky HIP error after a failed launch):
+// every entry point validates all arguments before touching the runtime,
+// returns a q4_status, and leaves a message for q4_last_error().
+#include "q4skinny.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "launch.h"
+
+namespace {
+
+// Fused-versus-split threshold measured on MI355X (fused when M <= value).
+constexpr int kDefaultCrossoverM = 16;
+
+thread_local std::string tl_error;
+
+q4_status fail(q4_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    tl_error = buf;
+    return st;
+}
+
+q4_status ok() {
+    tl_error.clear();
+    return Q4_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- test hook: Q4_TEST_FAIL_LAUNCH=<fused|dequant|gemm|copy>[:count] -------
+// Makes the next `count` launches of that kernel report a launch failure
+// without launching, so tests can check the error path and the recovery.
+std::once_flag g_hook_once;
+std::string g_hook_kernel;
+std::atomic<int> g_hook_left{0};
+
+bool injected_failure(const char *kernel) {
+    std::call_once(g_hook_once, [] {
+        const char *v = std::getenv("Q4_TEST_FAIL_LAUNCH");
+        if (!v || !*v) return;
+        std::string s(v);
+        int count = 1;
+        const size_t colon = s.find(':');
+        if (colon != std::string::npos) {
+            count = std::atoi(s.c_str() + colon + 1);
+            s.resize(colon);
+        }
+        g_hook_kernel = s;
+        g_hook_left.store(count);
+    });
+    if (g_hook_left.load() <= 0 || g_hook_kernel != kernel) return false;
+    return g_hook_left.fetch_sub(1) > 0;
+}
+
+q4_status check_launch(hipError_t e, const char *kernel) {
+    if (injected_failure(kernel)) {
+        (void)hipGetLastError();
+        return fail(Q4_ERR_HIP, "%s: injected launch failure (Q4_TEST_FAIL_LAUNCH)", kernel);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // drain the sticky error so the next call starts clean
+        return fail(Q4_ERR_HIP, "%s: %s", kernel, hipGetErrorString(e));
+    }
+    return Q4_OK;
+}
+
+// ---- crossover -------------------------------------------------------------
+std::atomic<int> g_crossover{-1};
+
+int crossover() {
+    int v = g_crossover.load();
+    if (v >= 0) return v;
+    int init = kDefaultCrossoverM;
+    if (const char *e = std::getenv("Q4_CROSSOVER_M")) {
+        char *end = nullptr;
+        const long x = std::strtol(e, &end, 10);
+        if (end != e && *end == '\0' && x >= 0 && x <= Q4_FUSED_MAX_M) init = (int)x;
+    }
+    int expected = -1;
+    g_crossover.compare_exchange_strong(expected, init);
+    return g_crossover.load();
+}
+
+// ---- split-path workspace: one buffer per (device, stream) ------------------
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+q4_status workspace(int device, hipStream_t s, size_t bytes, void **out) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[{device, s}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // The old buffer may still be read by work queued on `s`.
+            hipError_t e = hipStreamSynchronize(s);
+            if (e == hipSuccess) e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(Q4_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+            }
+        }
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(Q4_ERR_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+        }
+        w.ptr = p;
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return Q4_OK;
+}
+
+// ---- validation ---------------------------------------------------------------
+int log2_exact(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return ((1 << l) == v) ? l : -1;
+}
+
+q4_status check_q4_shape(int N, int K, int blocksize, int *bs_log2) {
+    if (N < 0 || K < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (N=%d, K=%d)", N, K);
+    if (K == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "K must be positive");
+    if (blocksize <= 0 || (blocksize & 1))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "blocksize %d must be positive and even", blocksize);
+    if (K % blocksize)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "K=%d is not a multiple of blocksize %d", K, blocksize);
+    if (blocksize != 32 && blocksize != 64 && blocksize != 128 && blocksize != 256)
+        return fail(Q4_ERR_UNSUPPORTED, "blocksize %d not in {32, 64, 128, 256}", blocksize);
+    if ((int64_t)N * (int64_t)K > (int64_t(1) << 41))
+        return fail(Q4_ERR_UNSUPPORTED, "N*K=%lld too large", (long long)N * K);
+    *bs_log2 = log2_exact(blocksize);
+    return Q4_OK;
+}
+
+q4_status drain_prior_error() {
+    (void)hipGetLastError();
+    return Q4_OK;
+}
+
+q4_status run_fused(const void *A, const uint8_t *Wp, const float *am, const float *cb, int M,
+                    int N, int K, int bs_log2, void *C, hipStream_t s) {
+    hipError_t e = q4::launch_q4_fused(static_cast<const uint16_t *>(A), Wp, am, cb, M, N, K,
+                                       bs_log2, static_cast<uint16_t *>(C), s);
+    return check_launch(e, "fused");
+}
+
+q4_status run_split(const void *A, const uint8_t *Wp, const float *am, const float *cb, int M,
+                    int N, int K, int bs_log2, void *C, hipStream_t s) {
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(Q4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    void *ws = nullptr;
+    const size_t bytes = (size_t)N * (size_t)K * 2;
+    q4_status st = workspace(device, s, bytes, &ws);
+    if (st != Q4_OK) return st;
+    e = q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, true, s);
+    st = check_launch(e, "dequant");
+    if (st != Q4_OK) return st;
+    e = q4::launch_bf16_gemm(static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(ws),
+                             nullptr, M, N, K, static_cast<uint16_t *>(C), s);
+    return check_launch(e, "gemm");
+}
+
+}  // namespace
+
+namespace q4 {
+
+DeviceInfo device_info() {
+    static std::atomic<int> cus[256];  // 0 = not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) {
+        (void)hipGetLastError();
+        return DeviceInfo{0, 256};
+    }
+    int n = cus[dev].load();
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus[dev].store(n);
+    }
+    return DeviceInfo{dev, n};
+}
+
+}  // namespace q4
+
+extern "C" {
+
+q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
+                              const float *codebook, int M, int N, int K, int blocksize,
+                              void *C, void *stream, int path) {
+    if (path != Q4_PATH_AUTO && path != Q4_PATH_FUSED && path != Q4_PATH_SPLIT)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+    if (M < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d)", M);
+    int bs_log2 = 0;
+    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
+    if (st != Q4_OK) return st;
+    if (path == Q4_PATH_FUSED && M > Q4_FUSED_MAX_M)
+        return fail(Q4_ERR_UNSUPPORTED, "fused path supports M <= %d (M=%d)", Q4_FUSED_MAX_M, M);
+    if ((int64_t)M * K > (int64_t(1) << 40))
+        return fail(Q4_ERR_UNSUPPORTED, "M*K too large");
+    if (M == 0 || N == 0) return ok();
+    if (!A || !Wpacked || !absmax || !codebook || !C)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(A, 16) || !aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) ||
+        !aligned(C, 2))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "A, Wpacked and absmax must be 16-byte aligned, C 2-byte aligned");
+    drain_prior_error();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool fused;
+    if (path == Q4_PATH_FUSED) fused = true;
+    else if (path == Q4_PATH_SPLIT) fused = false;
+    else fused = M <= crossover() && M <= Q4_FUSED_MAX_M;
+    st = fused ? run_fused(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s)
+               : run_split(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+    return st == Q4_OK ? ok() : st;
+}
+
+q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *absmax,
+                         const float *codebook, int M, int N, int K, int blocksize, void *C,
+                         void *stream) {
+    return q4_gemm_skinny_path(A, Wpacked, absmax, codebook, M, N, K, blocksize, C, stream,
+                               Q4_PATH_AUTO);
+}
+
+q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M, int N, int K,
+                           void *C, void *stream) {
+    if (M < 0 || N < 0 || K < 0)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d, N=%d, K=%d)", M, N, K);
+    if (K == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "K must be positive");
+    if (K % 8) return fail(Q4_ERR_INVALID_ARGUMENT, "K=%d must be a multiple of 8", K);
+    if (M > 5) return fail(Q4_ERR_UNSUPPORTED, "bf16 skinny GEMM supports M <= 5 (M=%d)", M);
+    if ((int64_t)N * (int64_t)K > (int64_t(1) << 40))
+        return fail(Q4_ERR_UNSUPPORTED, "N*K too large");
+    if (M == 0 || N == 0) return ok();
+    if (!A || !W || !C) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 2) || (bias && !aligned(bias, 2)))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "A and W must be 16-byte aligned, C and bias 2-byte aligned");
+    drain_prior_error();
+    hipError_t e = q4::launch_bf16_gemm(
+        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W),
+        static_cast<const uint16_t *>(bias), M, N, K, static_cast<uint16_t *>(C),
+        static_cast<hipStream_t>(stream));
+    q4_status st = check_launch(e, "gemm");
+    return st == Q4_OK ? ok() : st;
+}
+
+q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook, int N,
+                     int K, int blocksize, void *out, int out_dtype, void *stream) {
+    if (out_dtype != Q4_DTYPE_BF16 && out_dtype != Q4_DTYPE_FP32)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
+    int bs_log2 = 0;
+    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
+    if (st != Q4_OK) return st;
+    if (N == 0) return ok();
+    if (!Wpacked || !absmax || !codebook || !out)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) || !aligned(out, 16))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "Wpacked, absmax and out must be 16-byte aligned");
+    drain_prior_error();
+    hipError_t e = q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, out,
+                                      out_dtype == Q4_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    st = check_launch(e, "dequant");
+    return st == Q4_OK ? ok() : st;
+}
+
+int q4_get_crossover_m(void) { return crossover(); }
+
+q4_status q4_set_crossover_m(int m) {
+    if (m < 0 || m > Q4_FUSED_MAX_M)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "crossover %d not in 0..%d", m, Q4_FUSED_MAX_M);
+    g_crossover.store(m);
+    return ok();
+}
+
+q4_status q4_release_workspace(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    q4_status st = Q4_OK;
+    for (auto &kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        int prev = 0;
+        (void)hipGetDevice(&prev);
+        hipError_t e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess) e = hipStreamSynchronize(kv.first.second);
+        if (e == hipSuccess) e = hipFree(kv.second.ptr);
+        (void)hipSetDevice(prev);
+        if (e != hipSuccess && st == Q4_OK) {
+            (void)hipGetLastError();
+            st = fail(Q4_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+        }
+    }
+    g_ws.clear();
+    return st == Q4_OK ? ok() : st;
+}
+
+const char *q4_last_error(void) { return tl_error.c_str(); }
+
+q4_status q4_copy_probe(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "bytes and pointers must be multiples of 16");
+    drain_prior_error();
+    hipError_t e = q4::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream));
+    q4_status st = check_launch(e, "copy");
+    return st == Q4_OK ? ok() : st;
+}
+
+const char *q4_version(void) { return "q4skinny 0.1.0 (gfx950)"; }
+
+}  // extern "C"

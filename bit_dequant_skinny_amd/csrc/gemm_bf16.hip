@@ -1,0 +1,133 @@
+// bf16 skinny GEMM on the matrix cores: C[M,N] = A[M,K] * W[N,K]^T (+ bias).
+//
+// Serves two steps of the path:
+//  * the unquantized skinny GEMM for 1..5 token rows described in the report
+//    on vLLM pull request 40687 "Support N=5 in wvSplitK skinny GEMM kernels
+//    for speculative decoding" (section "关键源码片段": K % 8 == 0, optional
+//    bias, a per-token-count tile);
+//  * the GEMM half of the split path (dequantize to bf16, then GEMM) of the
+//    bitsandbytes pull request "[ROCm] Optimize kgemm_4bit_inference_naive
+//    ..." (section "Fused path support for M > 1").
+//
+// One wave computes a 16-feature x (16*MT)-token tile with
+// v_mfma_f32_16x16x32_bf16.  Tokens go in the A operand (row i = lane % 16),
+// weights in the B operand (column j = lane % 16); lane group g = lane / 16
+// supplies 8 consecutive k of the 32 each instruction consumes, read with one
+// 16-byte load per lane, so each weight row is read 64 contiguous bytes at a
+// time and every weight byte exactly once.  Token rows >= M feed zeros.  At
+// M <= 16 the arithmetic intensity is <= 16 flop/byte, far below the MFMA
+// ridge: the kernel is HBM-bound and the matrix cores only remove the VALU
+// work (no bf16 -> fp32 conversion, no per-element FMA).
+//
+// When N is small the waves of a workgroup split K and combine their fp32
+// tiles through LDS in a fixed order (deterministic, no atomics).
+#include "device.h"
+#include "launch.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
+    const uint16_t *__restrict__ bias, int M, int N, int K, int ksplit,
+    uint16_t *__restrict__ C) {
+    __shared__ floatx4 red[kWaves][MT][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tiles_per_block = kWaves / ksplit;
+    const int tile = blockIdx.x * tiles_per_block + wave / ksplit;
+    const int kpart = wave % ksplit;
+    const int n0 = tile * 16;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int n = (n0 + j < N) ? n0 + j : N - 1;  // clamped rows are computed and discarded
+
+    const int steps = (K + 31) >> 5;
+    const int s_begin = (kpart * steps) / ksplit;
+    const int s_end = ((kpart + 1) * steps) / ksplit;
+
+    floatx4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t *wrow = W + (size_t)n * K;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+
+    for (int s = s_begin; s < s_end; ++s) {
+        const int k = (s << 5) + (g << 3);
+        const bool kin = k < K;  // K % 8 == 0: a lane's 8 values are all in or all out
+        const uint4 wv = kin ? ld128(wrow + k) : zero;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int tok = t * 16 + j;
+            const uint4 av = (kin && tok < M) ? ld128(A + (size_t)tok * K + k) : zero;
+            acc[t] = mfma_bf16_16x16x32(as_bf16x8(av), as_bf16x8(wv), acc[t]);
+        }
+    }
+
+    if (ksplit > 1) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+        __syncthreads();
+        if (kpart != 0) return;
+        for (int p = 1; p < ksplit; ++p)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const floatx4 o = red[wave + p][t][lane];
+                acc[t][0] += o[0]; acc[t][1] += o[1]; acc[t][2] += o[2]; acc[t][3] += o[3];
+            }
+    }
+
+    if (n0 + j >= N) return;
+    const float b = bias ? bf16_lo(bias[n0 + j]) : 0.f;
+    // D layout: lane holds feature j and tokens 4*g + r of each 16-token tile.
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = t * 16 + g * 4 + r;
+            if (tok < M) C[(size_t)tok * N + n0 + j] = (uint16_t)f32_to_bf16_rne(acc[t][r] + b);
+        }
+}
+
+template <int MT>
+hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const uint16_t *bias, int M, int N,
+                     int K, uint16_t *C, hipStream_t s) {
+    const int tiles = (N + 15) / 16;
+    const DeviceInfo info = device_info();
+    // Split K across the waves of a workgroup when there are too few feature
+    // tiles to give every SIMD of the chip a few waves.
+    int ksplit = 1;
+    if (tiles < info.num_cus * 8) ksplit = 2;
+    if (tiles < info.num_cus * 2) ksplit = 4;
+    const int tiles_per_block = kWaves / ksplit;
+    const int blocks = (tiles + tiles_per_block - 1) / tiles_per_block;
+    bf16_gemm_kernel<MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K, ksplit, C);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_gemm(const uint16_t *A, const uint16_t *W, const uint16_t *bias, int M,
+                            int N, int K, uint16_t *C, hipStream_t s) {
+    // Token tiles of 16; above 64 tokens the weight is streamed once per
+    // 64-token slab.
+    for (int m0 = 0; m0 < M; m0 += 64) {
+        const int mm = (M - m0) < 64 ? (M - m0) : 64;
+        const uint16_t *Am = A + (size_t)m0 * K;
+        uint16_t *Cm = C + (size_t)m0 * N;
+        hipError_t e;
+        if (mm <= 16) e = launch_mt<1>(Am, W, bias, mm, N, K, Cm, s);
+        else if (mm <= 32) e = launch_mt<2>(Am, W, bias, mm, N, K, Cm, s);
+        else e = launch_mt<4>(Am, W, bias, mm, N, K, Cm, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace q4

@@ -1,0 +1,165 @@
+/*
+ * q4skinny: small-batch weight-streaming GEMMs of LLM decode on MI355X (gfx950).
+ *
+ * C ABI.  Callers need neither HIP nor torch headers: device buffers are
+ * passed as plain pointers, a HIP stream as `void *` (NULL = the default
+ * stream), sizes as int.
+ *
+ * Notation: M = token rows of A and C, N = output features (rows of W),
+ * K = reduction length.  Every matrix is row-major and contiguous.  The
+ * product is the "TN" inference layout C[M,N] = A[M,K] * W[N,K]^T named in
+ * the maintainer's comment on the bitsandbytes pull request "[ROCm] Optimize
+ * kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1".
+ *
+ * Common conventions
+ *  - Pointers are device pointers owned by the caller; the library never
+ *    frees them.  Outputs must not alias inputs.
+ *  - Calls are asynchronous: they enqueue work on `stream` and return.
+ *  - Arguments are validated before anything is launched.  On any error
+ *    status nothing has been launched and the outputs are untouched.
+ *  - Empty shapes (M == 0 or N == 0) return Q4_OK and launch nothing.
+ *  - A HIP launch failure returns Q4_ERR_HIP; the sticky HIP error is read
+ *    and cleared with hipGetLastError() so that the next call starts clean.
+ *  - q4_last_error() returns a message for the last failing call on the
+ *    calling thread (empty after a successful call).
+ *  - Results are deterministic: the same inputs, shape and path give
+ *    bit-identical outputs (no atomics; fixed reduction orders).
+ *  - Thread safety: every entry point may be called from several threads;
+ *    the crossover setter changes a process-wide value.
+ */
+#ifndef Q4SKINNY_H
+#define Q4SKINNY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum q4_status {
+    Q4_OK = 0,
+    Q4_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, misalignment, K not a multiple */
+    Q4_ERR_UNSUPPORTED = 2,      /* a legal request this library has no kernel for */
+    Q4_ERR_HIP = 3               /* the HIP runtime reported an error (see q4_last_error) */
+} q4_status;
+
+enum { Q4_DTYPE_BF16 = 0, Q4_DTYPE_FP32 = 1 };
+enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
+
+/* Largest M the fused 4-bit kernels handle; larger M always takes the split path. */
+#define Q4_FUSED_MAX_M 16
+
+/*
+ * q4_gemm_skinny: C = A * dequant(W)^T with W blockwise 4-bit quantized.
+ *
+ * Defined by the bitsandbytes pull request "[ROCm] Optimize
+ * kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1"
+ * (sections "Technical details" and "Fused path support for M > 1"): a fused
+ * dequantize + matmul for small multi-row inputs, falling back to dequantize
+ * + GEMM above a per-GPU crossover M.
+ *
+ *  A        bf16 [M, K]   activations.
+ *  Wpacked  uint8 [N, K/2] two 4-bit codes per byte; byte j of a row holds
+ *           k = 2j in its low nibble and k = 2j + 1 in its high nibble.
+ *  absmax   fp32 [N, K/blocksize]  one scale per block of `blocksize`
+ *           consecutive k inside a row.
+ *  codebook fp32 [16]     the value of each code (device memory).
+ *  C        bf16 [M, N]   output, round-to-nearest-even of the fp32 result.
+ *
+ *  The weight of element (n, k) is codebook[code] * absmax[n, k / blocksize]
+ *  (an fp32 product); products with A accumulate in fp32.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL A/Wpacked/absmax/codebook/C, M/N/K < 0,
+ *    K == 0, blocksize <= 0 or odd, K % blocksize != 0, A, Wpacked, absmax or
+ *    C not 16-byte aligned.
+ *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}; M or N above
+ *    2^30/K-sized limits (N * K / 2 must fit in 2^40 bytes).
+ *  Which kernel runs: M <= q4_get_crossover_m() and M <= Q4_FUSED_MAX_M take
+ *  the fused kernel; other M take the split path (dequantize to bf16 into a
+ *  library-owned workspace of N*K*2 bytes, then an MFMA bf16 GEMM).
+ */
+q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *absmax,
+                         const float *codebook, int M, int N, int K, int blocksize,
+                         void *C, void *stream);
+
+/*
+ * q4_gemm_skinny_path: q4_gemm_skinny with the path forced (Q4_PATH_AUTO,
+ * Q4_PATH_FUSED or Q4_PATH_SPLIT).  Used by the crossover measurement and
+ * the tests.  Q4_PATH_FUSED with M > Q4_FUSED_MAX_M is Q4_ERR_UNSUPPORTED;
+ * an unknown path value is Q4_ERR_INVALID_ARGUMENT.
+ */
+q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
+                              const float *codebook, int M, int N, int K, int blocksize,
+                              void *C, void *stream, int path);
+
+/*
+ * bf16_gemm_skinny: C = A * W^T (+ bias) for unquantized bf16 weights.
+ *
+ * Defined by the report on vLLM pull request 40687 "Support N=5 in wvSplitK
+ * skinny GEMM kernels for speculative decoding" (section "关键源码片段"): the
+ * skinny bf16 GEMM serves 1..5 token rows (one token plus four draft tokens
+ * of speculative-decode verification), needs K % 8 == 0, takes an optional
+ * bias and rejects token counts it has no kernel for.  (That page calls the
+ * token count n and the output features m; here they are M and N.)
+ *
+ *  A    bf16 [M, K], W bf16 [N, K], bias bf16 [N] or NULL, C bf16 [M, N].
+ *  Accumulates in fp32; the bias is added to the fp32 sum before the single
+ *  rounding to bf16.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL A/W/C, M/N/K < 0, K == 0, K % 8 != 0,
+ *    A, W or C not 16-byte aligned, bias not 2-byte aligned.
+ *  Q4_ERR_UNSUPPORTED: M > 5.
+ */
+q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M, int N,
+                           int K, void *C, void *stream);
+
+/*
+ * q4_dequant: out[n, k] = codebook[code(n, k)] * absmax[n, k / blocksize].
+ *
+ * The dequantize step of the split path in the bitsandbytes pull request
+ * "[ROCm] Optimize kgemm_4bit_inference_naive ..." (section "Fused path
+ * support for M > 1": "split dequantize + GEMM").  Same packed layout as
+ * q4_gemm_skinny.  out_dtype Q4_DTYPE_FP32 writes the fp32 product,
+ * Q4_DTYPE_BF16 writes it rounded to bf16 (nearest-even; NaN stays NaN).
+ * Bit-exact: one fp32 multiply per element, denormals kept.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, N/K < 0, K == 0, bad blocksize
+ *    (as above), out_dtype unknown, Wpacked/absmax/out not 16-byte aligned.
+ *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}.
+ */
+q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
+                     int N, int K, int blocksize, void *out, int out_dtype, void *stream);
+
+/*
+ * Crossover control.  The fused-versus-split threshold (fused when
+ * M <= crossover) starts at the value measured on MI355X and compiled in,
+ * unless the environment variable Q4_CROSSOVER_M holds an integer at the
+ * first call.  q4_set_crossover_m accepts 0..Q4_FUSED_MAX_M (0 = always split).
+ */
+int q4_get_crossover_m(void);
+q4_status q4_set_crossover_m(int m);
+
+/* Frees the split-path workspaces of every device and stream (synchronises
+ * the devices that own them).  Safe to call at any time between calls. */
+q4_status q4_release_workspace(void);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *q4_last_error(void);
+
+/*
+ * q4_copy_probe: dst[i] = src[i] for `bytes` bytes (a multiple of 16, both
+ * pointers 16-byte aligned) with the same 128-bit streaming loads as the
+ * GEMM kernels.  A measurement aid: it gives the achievable HBM copy rate
+ * and scales hardware byte counters against a transfer of known size.
+ */
+q4_status q4_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Library version string. */
+const char *q4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4SKINNY_H */

@@ -23,7 +23,9 @@ tensor 2 for W, 3 for the bias and 10*M + 1 for A, so an M sweep reuses one W.
 """
 from __future__ import annotations
 
+import os
 import statistics
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -90,7 +92,7 @@ def weights_f32(N: int, K: int, s: int, std: float = 0.02) -> np.ndarray:
     return (g.standard_normal((N, K), dtype=np.float32) * np.float32(std)).astype(np.float32)
 
 
-def quantize_blockwise(W: np.ndarray, codebook: np.ndarray, bs: int, rows_per_chunk: int = 2048):
+def quantize_blockwise(W: np.ndarray, codebook: np.ndarray, bs: int, rows_per_chunk: int = 1024):
     """Blockwise absmax quantization to the nearest codebook entry.
 
     Returns (codes uint8 [N, K], absmax float32 [N, K // bs]).
@@ -108,7 +110,8 @@ def quantize_blockwise(W: np.ndarray, codebook: np.ndarray, bs: int, rows_per_ch
     nb = K // bs
     codes = np.empty((N, K), dtype=np.uint8)
     absmax = np.empty((N, nb), dtype=np.float32)
-    for r0 in range(0, N, rows_per_chunk):
+
+    def work(r0):
         r1 = min(N, r0 + rows_per_chunk)
         blk = W[r0:r1].reshape(r1 - r0, nb, bs)
         am = np.abs(blk).max(axis=2)
@@ -119,6 +122,15 @@ def quantize_blockwise(W: np.ndarray, codebook: np.ndarray, bs: int, rows_per_ch
         c = np.searchsorted(mids, x, side="left").astype(np.uint8)
         c[am64 == 0] = zero_code
         codes[r0:r1] = c.reshape(r1 - r0, K)
+
+    # Row chunks are independent and numpy releases the GIL inside them.
+    starts = range(0, N, rows_per_chunk)
+    if N > rows_per_chunk:
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+            list(pool.map(work, starts))
+    else:
+        for r0 in starts:
+            work(r0)
     return codes, absmax
 
 

@@ -1,0 +1,93 @@
+"""Helpers for the GPU tests: moving seeded numpy inputs to the device, the
+elementwise acceptance rule, and cached full-size problems."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import synth
+
+# |C_gpu - C_ref| <= 2^-7 |C_ref| + 1e-3 * sum_k |a_k w_k|: 2^-7 is twice the bf16
+# output rounding, 1e-3 * S covers fp32 accumulation (chains up to ~4096 terms)
+# and, on the split path, the bf16 rounding of the weights on random data.
+REL = 2.0 ** -7
+ABS_S = 1e-3
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def dev():
+    t = torch()
+    assert t.cuda.is_available(), "GPU tests need an MI355X; none is visible"
+    return t.device("cuda:0")
+
+
+def to_dev(arr: np.ndarray, kind: str):
+    t = torch()
+    if kind == "bf16":
+        x = t.from_numpy(np.ascontiguousarray(arr, np.uint16).view(np.int16)).view(t.bfloat16)
+    elif kind == "u8":
+        x = t.from_numpy(np.ascontiguousarray(arr, np.uint8))
+    elif kind == "f32":
+        x = t.from_numpy(np.ascontiguousarray(arr, np.float32))
+    else:
+        raise ValueError(kind)
+    return x.to(dev())
+
+
+def q4_to_dev(p: dict):
+    return (to_dev(p["A"], "bf16"), to_dev(p["Wpacked"], "u8"), to_dev(p["absmax"], "f32"),
+            to_dev(p["codebook"], "f32"))
+
+
+def bf16_host(x) -> np.ndarray:
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    t = torch()
+    return x.contiguous().view(t.int16).cpu().numpy().view(np.uint16)
+
+
+def as_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_within_tolerance(C_gpu_bits, C_ref, S, what=""):
+    got = as_f64(C_gpu_bits)
+    assert got.shape == C_ref.shape, (got.shape, C_ref.shape)
+    bound = REL * np.abs(C_ref) + ABS_S * S
+    err = np.abs(got - C_ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        ratio = float(np.max(np.where(bound > 0, err / np.maximum(bound, 1e-300), np.inf)))
+        raise AssertionError("%s: %d of %d outside tolerance (worst err/bound %.3g); first %s: "
+                             "got %s ref %s S %s" % (
+                                 what, int(bad.sum()), bad.size, ratio, idx.tolist(),
+                                 got[tuple(idx.T)].tolist(), C_ref[tuple(idx.T)].tolist(),
+                                 S[tuple(idx.T)].tolist()))
+    return float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
+
+
+def sample_cols(N: int, count: int, seed: int) -> np.ndarray:
+    """Sorted sample of output columns that always includes both ends and the
+    last 16-wide tile."""
+    g = synth.rng(seed)
+    pick = g.choice(N, size=min(count, N), replace=False)
+    ends = np.array([0, 1, N - 1] + list(range(max(0, N - 17), N)), dtype=np.int64)
+    return np.unique(np.concatenate([pick.astype(np.int64), ends]))
+
+
+@functools.lru_cache(maxsize=4)
+def q4_weights(N: int, K: int, bs: int, config: int, shape: int):
+    """Seeded packed weights for a full-size 4-bit workload (cached)."""
+    p = synth.q4_problem(1, N, K, bs, config=config, shape=shape)
+    return p["Wpacked"], p["absmax"], p["codebook"]
+
+
+@functools.lru_cache(maxsize=2)
+def bf16_weights(N: int, K: int, config: int, shape: int):
+    return (synth.bf16_weights(N, K, synth.seed(config, shape, 2)),
+            synth.bias_bf16(N, synth.seed(config, shape, 3)))

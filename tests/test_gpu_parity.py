@@ -1,0 +1,235 @@
+"""GPU parity against the CPU oracle on small and ragged shapes.
+
+Every call goes through the binding into the C ABI.  Dequantize must match the
+oracle bit for bit; GEMMs must meet the elementwise tolerance
+|C_gpu - C_ref| <= 2^-7 |C_ref| + 1e-3 * sum |a*w| against the fp64 oracle.
+Shapes span several tiles and end in ragged tails (N not a multiple of the
+row/feature tile, K/32 not a multiple of 64 lanes).
+"""
+import numpy as np
+import pytest
+
+import bit_dequant_skinny_amd as q4
+import oracle
+import synth
+from gpu_util import (as_f64, assert_within_tolerance, bf16_host, dev, q4_to_dev, to_dev,
+                      torch)
+
+pytestmark = pytest.mark.gpu
+
+CODEBOOKS = {"nf4style": synth.nf4_style_codebook(), "random": synth.random_codebook(77)}
+
+
+def _sync():
+    torch().cuda.synchronize()
+
+
+# ----------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("N,K,bs", [(1, 32, 32), (3, 64, 64), (17, 640, 64), (5, 256, 128),
+                                    (7, 1024, 256), (64, 4096, 64), (33, 96, 32)])
+@pytest.mark.parametrize("cbname", sorted(CODEBOOKS))
+def test_dequant_bit_exact(N, K, bs, cbname):
+    t = torch()
+    p = synth.q4_problem(1, N, K, bs, config=50, shape=N, codebook=CODEBOOKS[cbname])
+    _, Wp, am, cb = q4_to_dev(p)
+    w16 = q4.q4_dequant(Wp, am, cb, bs, out_dtype=t.bfloat16)
+    w32 = q4.q4_dequant(Wp, am, cb, bs, out_dtype=t.float32)
+    _sync()
+    ref16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
+    ref32 = oracle.dequant_f32(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
+    assert np.array_equal(bf16_host(w16), ref16)
+    assert np.array_equal(w32.cpu().numpy().view(np.uint32), ref32.view(np.uint32))
+
+
+def test_dequant_special_scales_bit_exact():
+    """Zero, denormal-producing, denormal and huge scales, ties in bf16 rounding."""
+    t = torch()
+    N, K, bs = 4, 512, 64
+    g = synth.rng(3)
+    codes = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    am = np.array([[0.0, 1e-39, 1.17549435e-38, 3e-44, 2.0 ** 120, 1.0, 0.0625, 7.1e-3]] * N,
+                  dtype=np.float32)
+    am[1] *= np.float32(3.0)
+    cb = CODEBOOKS["random"]
+    Wp = synth.pack_nibbles(codes)
+    w16 = q4.q4_dequant(to_dev(Wp, "u8"), to_dev(am, "f32"), to_dev(cb, "f32"), bs)
+    w32 = q4.q4_dequant(to_dev(Wp, "u8"), to_dev(am, "f32"), to_dev(cb, "f32"), bs,
+                        out_dtype=t.float32)
+    _sync()
+    assert np.array_equal(bf16_host(w16), oracle.dequant_bf16(Wp, am, cb, N, K, bs))
+    assert np.array_equal(w32.cpu().numpy().view(np.uint32),
+                          oracle.dequant_f32(Wp, am, cb, N, K, bs).view(np.uint32))
+
+
+# ----------------------------------------------------------------- fused 4-bit
+FUSED_SHAPES = [(37, 640, 64), (100, 4096, 64), (9, 2112, 32), (70, 2560, 128), (3, 256, 256),
+                (1, 64, 64)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16])
+@pytest.mark.parametrize("N,K,bs", FUSED_SHAPES)
+def test_fused_parity(M, N, K, bs):
+    p = synth.q4_problem(M, N, K, bs, config=51, shape=N % 7, codebook=CODEBOOKS["random"])
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused")
+    _sync()
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(bf16_host(C), Cr, S, "fused M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_one_hot_rows_return_dequantized_rows(path):
+    """A one-hot row of A selects one dequantized weight per output exactly."""
+    N, K, bs = 48, 1024, 64
+    p = synth.q4_problem(1, N, K, bs, config=52, codebook=CODEBOOKS["nf4style"])
+    js = [0, 1, 31, 32, 63, 64, 511, 1023]
+    A = np.zeros((len(js), K), np.uint16)
+    for m, j in enumerate(js):
+        A[m, j] = 0x3F80
+    _, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(to_dev(A, "bf16"), Wp, am, cb, bs, path=path)
+    _sync()
+    w16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
+    assert np.array_equal(bf16_host(C), w16[:, js].T)
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_scaling_a_by_two_scales_c_exactly(path, M):
+    N, K, bs = 40, 2048, 64
+    p = synth.q4_problem(M, N, K, bs, config=53)
+    A, Wp, am, cb = q4_to_dev(p)
+    C1 = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path=path)
+    C2 = q4.q4_gemm_skinny((A.float() * 2).to(A.dtype), Wp, am, cb, bs, path=path)
+    _sync()
+    assert np.array_equal(as_f64(bf16_host(C2)), 2 * as_f64(bf16_host(C1)))
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_deterministic(path):
+    M, N, K, bs = 8, 300, 4096, 64
+    p = synth.q4_problem(M, N, K, bs, config=54)
+    A, Wp, am, cb = q4_to_dev(p)
+    outs = [bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path=path)) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_zero_scale_blocks_and_zero_activations():
+    N, K, bs = 20, 512, 64
+    p = synth.q4_problem(3, N, K, bs, config=55)
+    p["absmax"][::3, 1] = 0.0
+    p["A"][1] = 0
+    A, Wp, am, cb = q4_to_dev(p)
+    for path in ("fused", "split"):
+        C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path=path)
+        _sync()
+        Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], 3, N, K, bs)
+        got = bf16_host(C)
+        assert np.all(as_f64(got[1]) == 0.0)
+        assert_within_tolerance(got, Cr, S, path)
+
+
+# ----------------------------------------------------------------- split path
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 33, 64, 70])
+@pytest.mark.parametrize("N,K,bs", [(37, 640, 64), (130, 2048, 128), (16, 4096, 64)])
+def test_split_parity(M, N, K, bs):
+    p = synth.q4_problem(M, N, K, bs, config=56, shape=N % 5)
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="split")
+    _sync()
+    got = bf16_host(C)
+    # against the bf16-weight diagnostic: only fp32 accumulation and output rounding differ
+    C7, S7 = oracle.q4_gemm_w16(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(got, C7, S7, "split vs bf16-weight oracle")
+    # against the judged reference: bf16 weight rounding passes on random data
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(got, Cr, S, "split vs fused oracle")
+
+
+def test_auto_path_routes_large_m_to_split():
+    M, N, K, bs = 24, 64, 512, 64
+    p = synth.q4_problem(M, N, K, bs, config=57)
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs)
+    Cs = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="split")
+    _sync()
+    assert np.array_equal(bf16_host(C), bf16_host(Cs))
+
+
+def test_auto_path_follows_crossover():
+    M, N, K, bs = 4, 64, 512, 64
+    p = synth.q4_problem(M, N, K, bs, config=58)
+    A, Wp, am, cb = q4_to_dev(p)
+    old = q4.q4_get_crossover_m()
+    try:
+        q4.q4_set_crossover_m(0)
+        Ca = bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs))
+        Cs = bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="split"))
+        q4.q4_set_crossover_m(16)
+        Cb = bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs))
+        Cf = bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused"))
+    finally:
+        q4.q4_set_crossover_m(old)
+    assert np.array_equal(Ca, Cs) and np.array_equal(Cb, Cf)
+
+
+def test_empty_shapes_leave_output_untouched():
+    t = torch()
+    d = dev()
+    C = t.full((0, 8), 1.0, dtype=t.bfloat16, device=d)
+    Wp = t.zeros((8, 32), dtype=t.uint8, device=d)
+    am = t.zeros((8, 1), dtype=t.float32, device=d)
+    cb = t.zeros(16, dtype=t.float32, device=d)
+    A = t.zeros((0, 64), dtype=t.bfloat16, device=d)
+    q4.q4_gemm_skinny(A, Wp, am, cb, 64, out=C)
+    sentinel = t.full((2, 0), 3.0, dtype=t.bfloat16, device=d)
+    q4.bf16_gemm_skinny(t.zeros((2, 64), dtype=t.bfloat16, device=d),
+                        t.zeros((0, 64), dtype=t.bfloat16, device=d), out=sentinel)
+    _sync()
+
+
+def test_workspace_release_and_regrow():
+    M, N, K, bs = 20, 64, 1024, 64
+    p = synth.q4_problem(M, N, K, bs, config=59)
+    A, Wp, am, cb = q4_to_dev(p)
+    C1 = bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="split"))
+    q4.q4_release_workspace()
+    C2 = bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="split"))
+    assert np.array_equal(C1, C2)
+
+
+# ----------------------------------------------------------------- bf16 skinny
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("N,K", [(1, 8), (96, 2560), (100, 40), (37, 1000), (300, 4104)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_bf16_skinny_parity(M, N, K, with_bias):
+    p = synth.bf16_problem(M, N, K, with_bias, config=60, shape=N % 3)
+    A, W = to_dev(p["A"], "bf16"), to_dev(p["W"], "bf16")
+    b = to_dev(p["bias"], "bf16") if with_bias else None
+    C = q4.bf16_gemm_skinny(A, W, b)
+    _sync()
+    Cr, S = oracle.bf16_gemm(p["A"], p["W"], p["bias"], M, N, K)
+    assert_within_tolerance(bf16_host(C), Cr, S, "bf16 M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_bf16_skinny_rejects_six_tokens():
+    t = torch()
+    d = dev()
+    A = t.zeros((6, 64), dtype=t.bfloat16, device=d)
+    W = t.zeros((8, 64), dtype=t.bfloat16, device=d)
+    with pytest.raises(q4.Q4Error) as e:
+        q4.bf16_gemm_skinny(A, W)
+    assert e.value.status == q4.Q4_ERR_UNSUPPORTED
+    # the failure left no sticky error behind: the next call works
+    C = q4.bf16_gemm_skinny(A[:5], W)
+    _sync()
+    assert C.shape == (5, 8)
+
+
+def test_copy_probe_copies():
+    t = torch()
+    src = t.arange(1 << 20, dtype=t.int32, device=dev())
+    dst = t.empty_like(src)
+    q4.q4_copy_probe(src, dst)
+    _sync()
+    assert t.equal(src, dst)
