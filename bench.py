@@ -1,0 +1,339 @@
+"""Benchmark of the fused 4-bit skinny GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+
+Workload (the headline): C = A * dequant(W)^T with K=8192, N=28672 (an FFN
+up-projection), blocksize 64, fp32 absmax, for M = 1, 2, 4, 8 token rows.  One
+step = one dispatcher-routed q4_gemm_skinny call per M.  Inputs are seeded
+synthetic data resident in HBM before timing starts.  Each launch reads a
+different copy of the packed weights: the copies total >= 1 GiB, four times
+the 256 MB Infinity Cache, so every timed launch streams its weights from HBM.
+
+Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time
+of the K timed steps), per-M kernel times from HIP events on the launch
+stream, the roofline of the M=1 kernel, a CPU-oracle baseline on a bounded
+sample, and (unless --quick) the other decode workloads: the 4096x4096 GEMV,
+the decode layer set with its fused-vs-split crossover, the bf16 skinny GEMM
+and the large-vocabulary projection.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "achieved HBM GB/s and % of peak, fused 4-bit skinny GEMM at M=1/2/4/8"
+PEAK_GBS = 8000.0  # MI355X HBM3E
+BS = 64
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 1 << 30
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_q4_m1_k8192_n28672.traffic.md")
+FUSED_SOURCE = os.path.join(ROOT, "bit_dequant_skinny_amd", "csrc", "fused.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def q4_bytes(M, N, K, bs=BS):
+    """Algorithmic bytes of one fused call: packed W, fp32 absmax, A, C, codebook."""
+    return N * K // 2 + 4 * N * K // bs + 2 * M * K + 2 * M * N + 64
+
+
+def bf16_bytes(M, N, K, bias):
+    return 2 * N * K + 2 * M * K + 2 * M * N + (2 * N if bias else 0)
+
+
+class Dev:
+    def __init__(self):
+        import torch
+        self.t = torch
+        self.dev = torch.device("cuda:0")
+
+    def bf16(self, a):
+        t = self.t
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t.bfloat16).to(self.dev)
+
+    def raw(self, a):
+        return self.t.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def copies(self, tensors, nbytes):
+        """At least one copy; enough copies to exceed 1 GiB in total."""
+        r = max(1, math.ceil(ROTATE_BYTES / max(1, nbytes)))
+        out = [tensors]
+        for _ in range(r - 1):
+            out.append(tuple(x.clone() for x in tensors))
+        return out
+
+    def time_launches(self, fns, reps, warmup=3):
+        """Average HIP-event duration of each launch in fns over `reps` rounds,
+        each round calling the functions in order (on torch's current stream,
+        which the library launches on)."""
+        t = self.t
+        for _ in range(warmup):
+            for f in fns:
+                f(0)
+        t.cuda.synchronize()
+        evs = [[(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
+                for _ in fns] for _ in range(reps)]
+        for r in range(reps):
+            for i, f in enumerate(fns):
+                evs[r][i][0].record()
+                f(r)
+                evs[r][i][1].record()
+        t.cuda.synchronize()
+        return [float(np.mean([evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)])) * 1e3
+                for i in range(len(fns))]  # microseconds
+
+
+def traffic_from_profile(achieved_us):
+    """HBM bytes per launch of the M=1 kernel from the committed counter
+    summary, if it was taken on the current fused-kernel source."""
+    try:
+        text = open(PROFILE_TRAFFIC).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = hashlib.sha256(open(FUSED_SOURCE, "rb").read()).hexdigest()
+    if fields.get("fused.hip sha256") != src:
+        return None
+    try:
+        return float(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, M_list, target_s=12.0):
+    """The oracle as it stands, on a bounded column sample of the workload."""
+    import oracle
+    orc = oracle.default()
+    N, K = p["N"], p["K"]
+    g = synth.rng(123)
+    ncols = 64
+    total_bytes = 0.0
+    t_used = 0.0
+    while True:
+        cols = np.sort(g.choice(N, size=ncols, replace=False))
+        t0 = time.perf_counter()
+        for M in M_list:
+            orc.q4_gemm(p["A"][M][:M], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, BS, cols=cols)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or ncols >= N:
+            t_used = dt
+            total_bytes = sum(q4_bytes(M, N, K) * ncols / N for M in M_list)
+            break
+        ncols = min(N, int(ncols * max(2.0, (target_s / 4) / max(dt, 1e-3))))
+    return {
+        "value": total_bytes / t_used / 1e9,
+        "unit": "GB/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d output columns at M=%s, K=%d (algorithmic bytes scaled by the "
+                  "column fraction), %.1f s" % (ncols, N, "/".join(map(str, M_list)), K, t_used),
+    }
+
+
+def headline(d, args):
+    import bit_dequant_skinny_amd as q4
+    t = d.t
+    N, K = 28672, 8192
+    M_list = [1, 2, 4, 8]
+    log("generating the K=%d N=%d workload" % (K, N))
+    p = synth.q4_problem(1, N, K, BS, config=1, shape=0)
+    p["A"] = {M: synth.activations_bf16(M, K, synth.seed(1, 0, 10 * M + 1)) for M in M_list}
+    w = (d.raw(p["Wpacked"]), d.raw(p["absmax"]))
+    cb = d.raw(p["codebook"])
+    sets = d.copies(w, q4_bytes(1, N, K))
+    R = len(sets)
+    A = {M: d.bf16(p["A"][M]) for M in M_list}
+    C = {M: t.empty((M, N), dtype=t.bfloat16, device=d.dev) for M in M_list}
+
+    def launch(M, i):
+        Wp, am = sets[i % R]
+        q4.q4_gemm_skinny(A[M], Wp, am, cb, BS, out=C[M])
+
+    n = 0
+    for _ in range(args.warmup):
+        for M in M_list:
+            launch(M, n)
+            n += 1
+    t.cuda.synchronize()
+    evs = []
+    t.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for M in M_list:
+            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            e0.record()
+            launch(M, n)
+            e1.record()
+            evs.append((M, e0, e1))
+            n += 1
+    t.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_m_us = {M: float(np.mean([a.elapsed_time(b) for (m, a, b) in evs if m == M])) * 1e3
+                for M in M_list}
+    total = args.steps * sum(q4_bytes(M, N, K) for M in M_list)
+    per_m = {}
+    for M in M_list:
+        gbs = q4_bytes(M, N, K) / (per_m_us[M] * 1e-6) / 1e9
+        per_m[str(M)] = {"us": round(per_m_us[M], 2), "GB/s": round(gbs, 1),
+                         "pct_peak": round(100 * gbs / PEAK_GBS, 1),
+                         "path": "fused" if M <= q4.q4_get_crossover_m() else "split"}
+    ach = q4_bytes(1, N, K) / (per_m_us[1] * 1e-6) / 1e9
+    traffic = traffic_from_profile(per_m_us[1])
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic / (per_m_us[1] * 1e-6) / 1e9, 1),
+            "kernel": "fused q4 M=1, K=8192, N=28672",
+            "algorithmic_bytes_per_launch": q4_bytes(1, N, K)}
+    out = {
+        "metric": METRIC,
+        "value": round(total / wall / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "fused 4-bit skinny GEMM, K=8192, N=28672, blocksize 64, "
+                               "M=1,2,4,8 per step",
+                   "M": M_list, "K": K, "N": N, "blocksize": BS, "weight_copies": R},
+        "pct_of_peak": round(100 * total / wall / 1e9 / PEAK_GBS, 1),
+        "per_m": per_m,
+        "roofline": roof,
+    }
+    del sets, w
+    return out, p, M_list
+
+
+def other_configs(d):
+    """Kernel times of the other decode workloads (HIP events, rotated weights)."""
+    import bit_dequant_skinny_amd as q4
+    t = d.t
+    res = {}
+
+    def q4_cfg(name, M_list, N, K, config, shape, paths=("auto",)):
+        p = synth.q4_problem(1, N, K, BS, config=config, shape=shape)
+        sets = d.copies((d.raw(p["Wpacked"]), d.raw(p["absmax"])), q4_bytes(1, N, K))
+        cb = d.raw(p["codebook"])
+        rows = {}
+        for M in M_list:
+            A = d.bf16(synth.activations_bf16(M, K, synth.seed(config, shape, 10 * M + 1)))
+            C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+            fns = []
+            for path in paths:
+                def f(i, path=path):
+                    Wp, am = sets[i % len(sets)]
+                    q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path=path)
+                fns.append(f)
+            us = d.time_launches(fns, reps=max(20, min(200, len(sets) * 2)))
+            for path, u in zip(paths, us):
+                gbs = q4_bytes(M, N, K) / (u * 1e-6) / 1e9
+                rows["M=%d %s" % (M, path)] = {"us": round(u, 2), "GB/s": round(gbs, 1),
+                                               "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+        res[name] = rows
+        return rows
+
+    log("C1 GEMV 4096x4096")
+    q4_cfg("q4 M=1 K=4096 N=4096", [1], 4096, 4096, 0, 0)
+    log("C3 decode layers")
+    cross = {}
+    for shape, (K, N) in enumerate([(5120, 8192), (5120, 5120), (17408, 5120), (8192, 8192)]):
+        rows = q4_cfg("q4 K=%d N=%d" % (K, N), [1, 4, 8, 16], N, K, 2, shape,
+                      paths=("fused", "split"))
+        mstar = None
+        for M in [1, 4, 8, 16]:
+            if rows["M=%d split" % M]["us"] < rows["M=%d fused" % M]["us"]:
+                mstar = M
+                break
+        cross["K=%d N=%d" % (K, N)] = mstar
+    res["crossover (first M of 1,4,8,16 where split beats fused)"] = cross
+    log("C4 bf16 skinny")
+    for shape, N in enumerate([96, 2048, 16384, 31040]):
+        K = 2560
+        W = d.bf16(synth.bf16_weights(N, K, synth.seed(3, shape, 2)))
+        b = d.bf16(synth.bias_bf16(N, synth.seed(3, shape, 3)))
+        sets = d.copies((W,), bf16_bytes(1, N, K, True))
+        rows = {}
+        for M in range(1, 6):
+            A = d.bf16(synth.activations_bf16(M, K, synth.seed(3, shape, 10 * M + 1)))
+            C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+
+            def f(i):
+                q4.bf16_gemm_skinny(A, sets[i % len(sets)][0], b, out=C)
+            u = d.time_launches([f], reps=max(20, min(200, len(sets) * 2)))[0]
+            gbs = bf16_bytes(M, N, K, True) / (u * 1e-6) / 1e9
+            rows["M=%d" % M] = {"us": round(u, 2), "GB/s": round(gbs, 1),
+                                "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+        res["bf16+bias K=2560 N=%d" % N] = rows
+        del sets, W
+    log("C5 large-vocabulary projection")
+    q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0)
+    K, N = 2560, 248320
+    W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
+    rows = {}
+    for M in range(1, 6):
+        A = d.bf16(synth.activations_bf16(M, K, synth.seed(4, 1, 10 * M + 1)))
+        C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+        u = d.time_launches([lambda i: q4.bf16_gemm_skinny(A, W, None, out=C)], reps=20)[0]
+        gbs = bf16_bytes(M, N, K, False) / (u * 1e-6) / 1e9
+        rows["M=%d" % M] = {"us": round(u, 2), "GB/s": round(gbs, 1),
+                            "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+    res["bf16 K=2560 N=248320"] = rows
+    del W
+    # the achievable copy rate with the same 128-bit loads (context for % of peak)
+    src = t.empty(1 << 30, dtype=t.uint8, device=d.dev)
+    dst = t.empty_like(src)
+    u = d.time_launches([lambda i: q4.q4_copy_probe(src, dst)], reps=20)[0]
+    res["copy probe 1 GiB (read+write)"] = {"us": round(u, 1),
+                                            "GB/s": round(2 * (1 << 30) / (u * 1e-6) / 1e9, 1)}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    d = Dev()
+    assert d.t.cuda.is_available(), "bench.py needs an MI355X"
+    out, p, M_list = headline(d, args)
+    log("headline: %.1f GB/s" % out["value"])
+    if not args.quick:
+        out["configs"] = other_configs(d)
+    if not args.no_cpu:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(p, M_list)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,4 +1,6 @@
-// Fused blockwise-4-bit dequantize + skinny GEMM: C[M,N] = A[M,K] * dequant(W)^T.
+// Fused blockwise-4-bit dequantize + skinny GEMM on the vector ALUs:
+// C[M,N] = A[M,K] * dequant(W)^T.  Serves blocksize 32, whose blocks are
+// narrower than the 64-wide scale granule of the matrix-core kernel.
 //
 // The fused path of the bitsandbytes pull request "[ROCm] Optimize
 // kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1"
@@ -120,9 +122,9 @@ hipError_t launch_rows(const uint16_t *A, const uint8_t *Wp, const float *absmax
 
 }  // namespace
 
-hipError_t launch_q4_fused(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                           const float *codebook, int M, int N, int K, int bs_log2,
-                           uint16_t *C, hipStream_t s) {
+hipError_t launch_q4_fused_simt(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                                const float *codebook, int M, int N, int K, int bs_log2,
+                                uint16_t *C, hipStream_t s) {
     if (M <= 1) return launch_rows<1, 8>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
     if (M <= 2) return launch_rows<2, 8>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
     if (M <= 4) return launch_rows<4, 4>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);

@@ -1,0 +1,307 @@
+// Fused 4-bit dequantize + skinny GEMM on the matrix cores (blocksize >= 64).
+//
+// C[M,N] = A[M,K] * dequant(W)^T for M <= 16: the fused path of the
+// bitsandbytes pull request "[ROCm] Optimize kgemm_4bit_inference_naive for
+// ROCm, use it for batch sizes other than 1" (sections "Kernel optimization"
+// and "Fused path support for M > 1"), laid out for CDNA4 rather than after
+// the SIMT kernel of the pages.  Each packed byte is read from HBM once.
+//
+// Decode.  A 256-entry LDS table maps one packed byte (two codes c0, c1) to
+// two dwords: (hi(c0), hi(c1)) and (lo(c0), lo(c1)) in bf16, where
+// hi = bf16(cb) and lo = bf16(cb - hi), so hi + lo equals the fp32 codebook
+// value to within 2^-18 relative.  One SDWA shift and one ds_read_b64 decode
+// two weights; random bytes spread over the table's 2 KiB read at close to
+// the conflict-free ds_read_b64 rate on gfx950.  Two such reads form one B
+// operand of v_mfma_f32_16x16x32_bf16 laid out
+// [hi(c0) hi(c1) lo(c0) lo(c1) hi(c2) hi(c3) lo(c2) lo(c3)] against the A
+// operand [a0 a1 a0 a1 a2 a3 a2 a3], so the matrix core forms a*hi + a*lo
+// exactly and accumulates in fp32, and the loaded registers are the operand
+// registers.  The absmax of each 64-wide block scales the block's partial
+// sum (acc += absmax * D_block).
+//
+// Tiles.  A tile is 16 output features (the B-operand columns, lane % 16)
+// over all of K, walked in 128-wide segments: lane group g = lane / 16 reads
+// 16 bytes (32 codes) of its feature's row at byte 16*g of the segment, so a
+// feature row is read 64 contiguous bytes per segment and one load
+// instruction brings 1 KiB.  Groups 0,1 hold the segment's first 64-wide
+// block and groups 2,3 the second; one v_permlane32_swap exchanges half of
+// each lane's dwords with the lane 32 away so that every MFMA step draws from
+// a single 64-wide block, which keeps the absmax scaling exact per block.
+// Tokens feed the A operand (lane % 16 = token; lanes of tokens >= M are
+// computed and discarded).
+//
+// Schedule.  Workgroups are persistent and take every G-th tile; the KW
+// waves of a workgroup split each tile's segments into contiguous runs, so a
+// wave's scales for four consecutive segments of a row are 32 contiguous
+// bytes, read with one 8-byte load per lane and shared across lane groups
+// with ds_bpermute.  A wave walks its work as
+// (chunk of TB tiles) x (segment slot) x (tile in chunk), so the activation
+// operand of a segment (read from L2 one slot ahead) serves TB tiles.
+// Weight loads run one slot (TB units) ahead in a register ring and use
+// buffer loads, whose hardware range check returns zeros past the end of a
+// buffer, so the loop has no branches.  After each chunk every wave writes its
+// fp32 partials to an LDS slot; after a barrier that leaves global loads in
+// flight, wave 0 sums the KW partials in wave order (deterministic, no
+// atomics) and stores bf16.
+#include "device.h"
+#include "launch.h"
+
+namespace q4 {
+
+namespace {
+
+// Table entry e (a packed byte): x = (hi(cb[e & 15]), hi(cb[e >> 4])),
+// y = (lo(cb[e & 15]), lo(cb[e >> 4])), low nibble = even k = low half.
+__device__ __forceinline__ uint2 pair_table_entry(const float *__restrict__ cb, int e) {
+    const float c0 = cb[e & 15], c1 = cb[e >> 4];
+    const uint32_t h0 = f32_to_bf16_rne(c0), h1 = f32_to_bf16_rne(c1);
+    const uint32_t l0 = f32_to_bf16_rne(c0 - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(c1 - __uint_as_float(h1 << 16));
+    return make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
+}
+
+// Offset (in k) of the 8 codes in dword t of lane group g's 16 bytes after
+// the permlane32 swap.
+__device__ __forceinline__ uint32_t k_offset(int g, int t) {
+    return 32 * (g & 1) + 16 * (g >> 1) + 8 * (t & 1) + 64 * (t >> 1);
+}
+
+// LDS-only barrier: waits for this wave's LDS operations, not for its global
+// loads still in flight, then synchronises the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kPastEnd = 0x80000000u;  // an offset beyond every buffer: reads zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kBufferFlags);
+}
+
+// SR: accumulator rows kept per lane (min(M, 4)); KW: waves per workgroup;
+// TB: tiles per chunk (also the weight loads in flight per wave); NBUF:
+// partial buffers (2 lets the next chunk's partials land while wave 0 reads).
+template <int SR, int KW, int TB, int NBUF>
+__global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
+    const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
+    const float *__restrict__ absmax, const float *__restrict__ codebook, int M, int N, int K,
+    int bs_log2, int tiles, uint16_t *__restrict__ C) {
+    __shared__ uint2 table[256];
+    __shared__ float red[NBUF][KW][TB * SR][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    for (int e = tid; e < 256; e += 64 * KW) table[e] = pair_table_entry(codebook, e);
+    __syncthreads();
+
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int nseg = (K + 127) >> 7;
+    const int spw = (nseg + KW - 1) / KW;  // segment slots per wave per tile
+    const int G = gridDim.x;
+    const int my_tiles = (tiles - (int)blockIdx.x + G - 1) / G;
+    const int nchunks = (my_tiles + TB - 1) / TB;
+    const uint32_t row_bytes = (uint32_t)K >> 1;
+    const uint32_t nb = (uint32_t)K >> bs_log2;
+
+    const __amdgpu_buffer_rsrc_t wres = make_rsrc(Wp, (uint32_t)N * row_bytes);
+    const __amdgpu_buffer_rsrc_t sres = make_rsrc(absmax, (uint32_t)N * nb * 4);
+    const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
+
+    // Wave w owns segments [w*spw, (w+1)*spw) of every tile: slot q is
+    // segment w*spw + q.  Byte offsets advance incrementally in
+    // (chunk, slot, tile) order.
+    const uint32_t seg0 = (uint32_t)wave * spw;
+    const uint32_t w_tile_step = 16u * (uint32_t)G * row_bytes;
+    const uint32_t s_tile_step = 16u * (uint32_t)G * nb * 4;
+    const uint32_t w_lane = seg0 * 64 + 16 * g;
+
+    // issue cursor: chunk ic, slot iq
+    int ic = 0, iq = 0;
+    uint32_t wo_q = 0, n_ic = 0;
+    auto chunk_base = [&](int c) {
+        n_ic = ((uint32_t)blockIdx.x + (uint32_t)(c * TB) * (uint32_t)G) * 16 + j;
+        wo_q = n_ic * row_bytes + w_lane;
+    };
+    chunk_base(0);
+
+    // Scales come in groups of 4 slots: lane group g loads the two 64-wide
+    // block scales of slot (group start + g) for its feature j, and the slot
+    // being computed fetches them from lane j + 16*(slot % 4).
+    uint4 wbuf[TB];
+    float sgrp[TB][2];
+    auto issue_slot = [&]() {  // loads of (chunk ic, slot iq) for its TB tiles
+#pragma unroll
+        for (int tr = 0; tr < TB; ++tr) {
+            const uint32_t wo = wo_q + tr * w_tile_step;
+            wbuf[tr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
+        }
+        if ((iq & 3) == 0) {
+            const uint32_t k0 = (seg0 + iq + g) * 128;
+            const uint32_t b0 = (k0 >> bs_log2) * 4, b1 = ((k0 + 64) >> bs_log2) * 4;
+#pragma unroll
+            for (int tr = 0; tr < TB; ++tr) {
+                const uint32_t so = (n_ic * nb) * 4 + tr * s_tile_step;
+                sgrp[tr][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)(so + b0), 0, 0));
+                sgrp[tr][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)(so + b1), 0, 0));
+            }
+        }
+        if (++iq == spw) {
+            iq = 0;
+            chunk_base(++ic);
+        } else {
+            wo_q += 64;
+        }
+    };
+
+    // Activation operand of slot q: token j's 8 activations for each of the
+    // lane's 4 dwords of codes.  Lanes of tokens >= M read token 0 (their
+    // outputs are discarded); k >= K (a ragged last segment, or a slot past
+    // the last segment) reads zeros, which cancels whatever codes sit there.
+    const uint32_t a_row = (uint32_t)(j < M ? j : 0) * (uint32_t)K * 2;
+    uint4 anext[4];
+    auto load_a = [&](int q) {
+        const uint32_t kk = (seg0 + q) * 128;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t k = kk + k_offset(g, t);
+            const uint32_t off = k < (uint32_t)K ? a_row + k * 2 : kPastEnd;
+            anext[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)off, 0, 0));
+        }
+    };
+
+    issue_slot();
+    load_a(0);
+
+    const floatx4 zerof = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nchunks; ++c) {
+        float acc[TB][SR];
+#pragma unroll
+        for (int tr = 0; tr < TB; ++tr)
+#pragma unroll
+            for (int r = 0; r < SR; ++r) acc[tr][r] = 0.f;
+
+        for (int q = 0; q < spw; ++q) {
+            // activation operand, each pair of activations duplicated
+            uint4 adup[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                adup[2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
+                adup[2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
+            }
+            uint4 w[TB];
+            float am[TB][2];
+            const int src = (j + 16 * (q & 3)) * 4;
+#pragma unroll
+            for (int tr = 0; tr < TB; ++tr) {
+                w[tr] = wbuf[tr];
+                am[tr][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sgrp[tr][0])));
+                am[tr][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sgrp[tr][1])));
+            }
+            issue_slot();                     // the next slot's weights (and scales)
+            load_a(q + 1 < spw ? q + 1 : 0);  // and its activations
+#pragma unroll
+            for (int tr = 0; tr < TB; ++tr) {
+                uint32_t x[4] = {w[tr].x, w[tr].y, w[tr].z, w[tr].w};
+                // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
+                // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
+                const auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+                const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+                x[0] = s02[0]; x[2] = s02[1];
+                x[1] = s13[0]; x[3] = s13[1];
+                floatx4 D = zerof;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const uint32_t d = x[s >> 1] >> (16 * (s & 1));
+                    const uint2 e0 = table[d & 0xff];
+                    const uint2 e1 = table[(d >> 8) & 0xff];
+                    const uint4 b = make_uint4(e0.x, e0.y, e1.x, e1.y);
+                    D = mfma_bf16_16x16x32(as_bf16x8(adup[s]), as_bf16x8(b), (s & 3) ? D : zerof);
+                    if ((s & 3) == 3) {
+                        const float sc = am[tr][s >> 2];
+#pragma unroll
+                        for (int r = 0; r < SR; ++r) acc[tr][r] = fmaf(sc, D[r], acc[tr][r]);
+                    }
+                }
+            }
+        }
+
+        // combine the KW partials of this chunk's tiles
+        const int buf = NBUF == 2 ? (c & 1) : 0;
+#pragma unroll
+        for (int tr = 0; tr < TB; ++tr)
+#pragma unroll
+            for (int r = 0; r < SR; ++r) red[buf][wave][tr * SR + r][lane] = acc[tr][r];
+        lds_barrier();
+        if (wave == 0) {
+#pragma unroll
+            for (int tr = 0; tr < TB; ++tr) {
+                const int n = ((int)blockIdx.x + (c * TB + tr) * G) * 16 + j;
+#pragma unroll
+                for (int r = 0; r < SR; ++r) {
+                    float v = red[buf][0][tr * SR + r][lane];
+                    for (int w2 = 1; w2 < KW; ++w2) v += red[buf][w2][tr * SR + r][lane];
+                    const int tok = 4 * g + r;
+                    if (n < N && tok < M) C[(size_t)tok * N + n] = (uint16_t)f32_to_bf16_rne(v);
+                }
+            }
+        }
+        if constexpr (NBUF == 1) lds_barrier();
+    }
+}
+
+template <int SR, int KW, int TB, int NBUF>
+hipError_t launch_cfg(const uint16_t *A, const uint8_t *Wp, const float *absmax,
+                      const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
+                      int wg_per_cu, hipStream_t s) {
+    const int tiles = (N + 15) / 16;
+    const DeviceInfo info = device_info();
+    int G = info.num_cus * wg_per_cu;
+    if (G > tiles) G = tiles;
+    fused_mfma_kernel<SR, KW, TB, NBUF><<<dim3(G), dim3(64 * KW), 0, s>>>(
+        A, Wp, absmax, codebook, M, N, K, bs_log2, tiles, C);
+    return hipGetLastError();
+}
+
+template <int SR>
+hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
+                     const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
+                     hipStream_t s) {
+    // 16 waves per CU: one 16-wave workgroup when the segments divide by 16,
+    // else several smaller workgroups so no wave idles on a tile.
+    const int nseg = (K + 127) >> 7;
+    if (nseg % 16 == 0) return launch_cfg<SR, 16, 4, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 1, s);
+    if (nseg % 8 == 0) return launch_cfg<SR, 8, 4, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 2, s);
+    return launch_cfg<SR, 4, 4, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 4, s);
+}
+
+}  // namespace
+
+// The kernel's byte offsets are 32-bit.  The weight offsets run up to two
+// chunks of every workgroup past the last tile (at most 2 * 4 * 1024 tiles of
+// 16 rows on a 256-CU part), so the matrix plus that margin must stay below
+// 4 GiB, and so must the activations.
+bool q4_fused_mfma_fits(int M, int N, int K) {
+    const uint64_t margin_rows = 2ull * 4 * 1024 * 16;
+    return ((uint64_t)N + margin_rows) * (uint64_t)K / 2 < (1ull << 32) &&
+           (uint64_t)M * (uint64_t)K * 2 < (1ull << 31);
+}
+
+hipError_t launch_q4_fused_mfma(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                                const float *codebook, int M, int N, int K, int bs_log2,
+                                uint16_t *C, hipStream_t s) {
+    if (M <= 1) return launch_sr<1>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+    if (M <= 2) return launch_sr<2>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+    return launch_sr<4>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+}
+
+hipError_t launch_q4_fused(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                           const float *codebook, int M, int N, int K, int bs_log2,
+                           uint16_t *C, hipStream_t s) {
+    if (bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K))
+        return launch_q4_fused_mfma(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+    return launch_q4_fused_simt(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+}
+
+}  // namespace q4

@@ -18,9 +18,17 @@ DeviceInfo device_info();  // the current device, cached per device
 hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
                           int N, int K, int bs_log2, void *out, bool out_bf16, hipStream_t s);
 
+// Dispatches to the matrix-core kernel (blocksize >= 64) or the vector-ALU
+// kernel (blocksize 32).
 hipError_t launch_q4_fused(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, int M, int N, int K, int bs_log2,
                            uint16_t *C, hipStream_t s);
+hipError_t launch_q4_fused_mfma(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                                const float *codebook, int M, int N, int K, int bs_log2,
+                                uint16_t *C, hipStream_t s);
+hipError_t launch_q4_fused_simt(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
+                                const float *codebook, int M, int N, int K, int bs_log2,
+                                uint16_t *C, hipStream_t s);
 
 hipError_t launch_bf16_gemm(const uint16_t *A, const uint16_t *W, const uint16_t *bias,
                             int M, int N, int K, uint16_t *C, hipStream_t s);
