@@ -9,15 +9,19 @@
 // Decode.  A 256-entry LDS table maps one packed byte (two codes c0, c1) to
 // two dwords: (hi(c0), hi(c1)) and (lo(c0), lo(c1)) in bf16, where
 // hi = bf16(cb) and lo = bf16(cb - hi), so hi + lo equals the fp32 codebook
-// value to within 2^-18 relative.  One SDWA shift and one ds_read_b64 decode
-// two weights; random bytes spread over the table's 2 KiB read at close to
-// the conflict-free ds_read_b64 rate on gfx950.  Two such reads form one B
-// operand of v_mfma_f32_16x16x32_bf16 laid out
+// value to within 2^-18 relative.  One ds_read_b64 decodes two weights.  Two
+// such reads form one B operand of v_mfma_f32_16x16x32_bf16 laid out
 // [hi(c0) hi(c1) lo(c0) lo(c1) hi(c2) hi(c3) lo(c2) lo(c3)] against the A
 // operand [a0 a1 a0 a1 a2 a3 a2 a3], so the matrix core forms a*hi + a*lo
 // exactly and accumulates in fp32, and the loaded registers are the operand
 // registers.  The absmax of each 64-wide block scales the block's partial
 // sum (acc += absmax * D_block).
+//
+// The table is stored 32 times, interleaved so that entry b of lane l sits
+// at byte b*256 + 8*(l % 32): every lane reads its own pair of LDS banks
+// whatever byte it decodes, so the random lookups never conflict (a single
+// copy loses about half its LDS cycles to bank conflicts).  One v_perm_b32
+// builds that address from the packed byte and the lane's offset.
 //
 // Tiles.  A tile is 16 output features (the B-operand columns, lane % 16)
 // over all of K, walked in 128-wide segments: lane group g = lane / 16 reads
@@ -31,10 +35,11 @@
 // computed and discarded).
 //
 // Schedule.  Workgroups are persistent and take every G-th tile; the KW
-// waves of a workgroup split each tile's segments into contiguous runs, so a
-// wave's scales for four consecutive segments of a row are 32 contiguous
-// bytes, read with one 8-byte load per lane and shared across lane groups
-// with ds_bpermute.  A wave walks its work as
+// waves of a workgroup interleave each tile's segments, so together they read
+// 64*KW contiguous bytes of a row at a time.  Per slot a wave fetches the
+// block scales of its TB tiles' 16 rows with one access per lane (no
+// duplicates) and shares them across lane groups with ds_bpermute.  A wave
+// walks its work as
 // (chunk of TB tiles) x (segment slot) x (tile in chunk), so the activation
 // operand of a segment (read from L2 one slot ahead) serves TB tiles.
 // Weight loads run one slot (TB units) ahead in a register ring and use
@@ -87,13 +92,19 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook, int M, int N, int K,
     int bs_log2, int tiles, uint16_t *__restrict__ C) {
-    __shared__ uint2 table[256];
+    __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
     __shared__ float red[NBUF][KW][TB * SR][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    for (int e = tid; e < 256; e += 64 * KW) table[e] = pair_table_entry(codebook, e);
+    for (int e = tid; e < 256; e += 64 * KW) {
+        const uint2 v = pair_table_entry(codebook, e);
+#pragma unroll 8
+        for (int c = 0; c < 32; ++c) table[e * 32 + c] = v;
+    }
     __syncthreads();
+    const char *tab_bytes = reinterpret_cast<const char *>(table);
+    const uint32_t lane_off = (uint32_t)(lane & 31) * 8;
 
     const int j = lane & 15;
     const int g = lane >> 4;
@@ -109,49 +120,50 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const __amdgpu_buffer_rsrc_t sres = make_rsrc(absmax, (uint32_t)N * nb * 4);
     const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
 
-    // Wave w owns segments [w*spw, (w+1)*spw) of every tile: slot q is
-    // segment w*spw + q.  Byte offsets advance incrementally in
-    // (chunk, slot, tile) order.
-    const uint32_t seg0 = (uint32_t)wave * spw;
+    // Slot q of wave w is segment w + q*KW of every tile (the waves of a
+    // workgroup read 64*KW contiguous bytes of each row at a time).  Byte
+    // offsets advance incrementally in (chunk, slot, tile) order.
     const uint32_t w_tile_step = 16u * (uint32_t)G * row_bytes;
+    const uint32_t w_lane = (uint32_t)wave * 64 + 16 * g;
+    // Scales: for each slot, lane (r, g) = (lane % 16, lane / 16) loads the
+    // two 64-wide block scales of segment (w + q*KW) for row r of the chunk's
+    // tiles g, g + 4, ... (one load pair per tile, no duplicates); the lanes
+    // that decode tile t fetch them from lane j + 16*(t % 4).
+    constexpr int SV = (TB + 3) / 4;  // scale load pairs per lane per slot
     const uint32_t s_tile_step = 16u * (uint32_t)G * nb * 4;
-    const uint32_t w_lane = seg0 * 64 + 16 * g;
+    const uint32_t s_half = bs_log2 == 6 ? 4u : 0u;
 
     // issue cursor: chunk ic, slot iq
     int ic = 0, iq = 0;
-    uint32_t wo_q = 0, n_ic = 0;
+    uint32_t wo_q = 0, so_q = 0;
     auto chunk_base = [&](int c) {
-        n_ic = ((uint32_t)blockIdx.x + (uint32_t)(c * TB) * (uint32_t)G) * 16 + j;
-        wo_q = n_ic * row_bytes + w_lane;
+        const uint32_t n0 = ((uint32_t)blockIdx.x + (uint32_t)(c * TB) * (uint32_t)G) * 16 + j;
+        wo_q = n0 * row_bytes + w_lane;
+        so_q = n0 * nb * 4;
     };
     chunk_base(0);
 
-    // Scales come in groups of 4 slots: lane group g loads the two 64-wide
-    // block scales of slot (group start + g) for its feature j, and the slot
-    // being computed fetches them from lane j + 16*(slot % 4).
     uint4 wbuf[TB];
-    float sgrp[TB][2];
+    float sbuf[SV][2];
     auto issue_slot = [&]() {  // loads of (chunk ic, slot iq) for its TB tiles
 #pragma unroll
         for (int tr = 0; tr < TB; ++tr) {
             const uint32_t wo = wo_q + tr * w_tile_step;
             wbuf[tr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
         }
-        if ((iq & 3) == 0) {
-            const uint32_t k0 = (seg0 + iq + g) * 128;
-            const uint32_t b0 = (k0 >> bs_log2) * 4, b1 = ((k0 + 64) >> bs_log2) * 4;
+        const uint32_t k0 = ((uint32_t)wave + (uint32_t)iq * KW) * 128;
 #pragma unroll
-            for (int tr = 0; tr < TB; ++tr) {
-                const uint32_t so = (n_ic * nb) * 4 + tr * s_tile_step;
-                sgrp[tr][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)(so + b0), 0, 0));
-                sgrp[tr][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)(so + b1), 0, 0));
-            }
+        for (int v = 0; v < SV; ++v) {
+            const int tt = g + 4 * v < TB ? g + 4 * v : 0;
+            const uint32_t so = so_q + tt * s_tile_step + (k0 >> bs_log2) * 4;
+            sbuf[v][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)so, 0, 0));
+            sbuf[v][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)(so + s_half), 0, 0));
         }
         if (++iq == spw) {
             iq = 0;
             chunk_base(++ic);
         } else {
-            wo_q += 64;
+            wo_q += 64u * KW;
         }
     };
 
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint32_t a_row = (uint32_t)(j < M ? j : 0) * (uint32_t)K * 2;
     uint4 anext[4];
     auto load_a = [&](int q) {
-        const uint32_t kk = (seg0 + q) * 128;
+        const uint32_t kk = ((uint32_t)wave + (uint32_t)q * KW) * 128;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t k = kk + k_offset(g, t);
@@ -183,26 +195,34 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             for (int r = 0; r < SR; ++r) acc[tr][r] = 0.f;
 
         for (int q = 0; q < spw; ++q) {
-            // activation operand, each pair of activations duplicated
+            // Activation operand, each pair of activations duplicated.  Built
+            // once per slot and pinned in registers: an MFMA whose operand a
+            // VALU instruction has just written stalls for the hazard, so the
+            // compiler must not rebuild these next to every MFMA.
             uint4 adup[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 adup[2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
                 adup[2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
             }
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                __asm__ volatile("" : "+v"(adup[s].x), "+v"(adup[s].y), "+v"(adup[s].z), "+v"(adup[s].w));
             uint4 w[TB];
             float am[TB][2];
-            const int src = (j + 16 * (q & 3)) * 4;
 #pragma unroll
             for (int tr = 0; tr < TB; ++tr) {
+                const int src = (j + 16 * (tr & 3)) * 4;
                 w[tr] = wbuf[tr];
-                am[tr][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sgrp[tr][0])));
-                am[tr][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sgrp[tr][1])));
+                am[tr][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sbuf[tr >> 2][0])));
+                am[tr][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sbuf[tr >> 2][1])));
             }
             issue_slot();                     // the next slot's weights (and scales)
             load_a(q + 1 < spw ? q + 1 : 0);  // and its activations
-#pragma unroll
-            for (int tr = 0; tr < TB; ++tr) {
+            // Decode is software-pipelined one tile ahead: the 16 table reads
+            // of tile tr+1 are in flight while the MFMAs of tile tr run.
+            uint2 e[2][16];
+            auto decode = [&](int tr, uint2 (&ev)[16]) {
                 uint32_t x[4] = {w[tr].x, w[tr].y, w[tr].z, w[tr].w};
                 // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
                 // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
@@ -210,20 +230,39 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
                 x[0] = s02[0]; x[2] = s02[1];
                 x[1] = s13[0]; x[3] = s13[1];
-                floatx4 D = zerof;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const uint32_t d = x[s >> 1] >> (16 * (s & 1));
-                    const uint2 e0 = table[d & 0xff];
-                    const uint2 e1 = table[(d >> 8) & 0xff];
-                    const uint4 b = make_uint4(e0.x, e0.y, e1.x, e1.y);
-                    D = mfma_bf16_16x16x32(as_bf16x8(adup[s]), as_bf16x8(b), (s & 3) ? D : zerof);
-                    if ((s & 3) == 3) {
-                        const float sc = am[tr][s >> 2];
-#pragma unroll
-                        for (int r = 0; r < SR; ++r) acc[tr][r] = fmaf(sc, D[r], acc[tr][r]);
-                    }
+                for (int i = 0; i < 16; ++i) {
+                    // address = byte * 256 + lane_off: byte 1 from the packed
+                    // dword, byte 0 from lane_off, bytes 2-3 zero
+                    const uint32_t addr = __builtin_amdgcn_perm(x[i >> 2], lane_off, 0x0c0c0000u | ((4 + (i & 3)) << 8));
+                    ev[i] = *reinterpret_cast<const uint2 *>(tab_bytes + addr);
                 }
+            };
+            decode(0, e[0]);
+#pragma unroll
+            for (int tr = 0; tr < TB; ++tr) {
+                // Per tile: its MFMAs, then the next tile's decode (VALU and
+                // LDS work that runs under the matrix cores), then the scale
+                // FMAs that consume the MFMA results.  Tiles past the end of
+                // a partial last chunk are computed too (their loads read
+                // zeros past the buffer end and their outputs are never
+                // stored), which keeps this loop one block.
+                const uint2 *ev = e[tr & 1];
+                // two independent chains, one per 64-wide block
+                floatx4 D0 = zerof, D1 = zerof;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
+                    const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
+                    D0 = mfma_bf16_16x16x32(as_bf16x8(adup[s]), as_bf16x8(b0), D0);
+                    D1 = mfma_bf16_16x16x32(as_bf16x8(adup[4 + s]), as_bf16x8(b1), D1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (tr + 1 < TB) decode(tr + 1, e[(tr + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < SR; ++r)
+                    acc[tr][r] = fmaf(am[tr][1], D1[r], fmaf(am[tr][0], D0[r], acc[tr][r]));
             }
         }
 
@@ -268,12 +307,11 @@ template <int SR>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
                      hipStream_t s) {
-    // 16 waves per CU: one 16-wave workgroup when the segments divide by 16,
-    // else several smaller workgroups so no wave idles on a tile.
-    const int nseg = (K + 127) >> 7;
-    if (nseg % 16 == 0) return launch_cfg<SR, 16, 4, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 1, s);
-    if (nseg % 8 == 0) return launch_cfg<SR, 8, 4, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 2, s);
-    return launch_cfg<SR, 4, 4, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 4, s);
+    // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS),
+    // 8 tiles per chunk so each wave keeps 8 KiB of weights in flight; for
+    // more than two tokens the partial tiles share a single buffer.
+    constexpr int NBUF = SR <= 2 ? 2 : 1;
+    return launch_cfg<SR, 8, 8, NBUF>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 1, s);
 }
 
 }  // namespace
