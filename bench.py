@@ -40,7 +40,8 @@ BS = 64
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 1 << 30
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fused_q4_m1_k8192_n28672.traffic.md")
-FUSED_SOURCE = os.path.join(ROOT, "bit_dequant_skinny_amd", "csrc", "fused.hip")
+FUSED_SOURCES = [os.path.join(ROOT, "bit_dequant_skinny_amd", "csrc", f)
+                 for f in ("fused_mfma.hip", "device.h")]
 
 
 def log(*a):
@@ -98,6 +99,13 @@ class Dev:
                 for i in range(len(fns))]  # microseconds
 
 
+def fused_source_hash():
+    h = hashlib.sha256()
+    for f in FUSED_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(achieved_us):
     """HBM bytes per launch of the M=1 kernel from the committed counter
     summary, if it was taken on the current fused-kernel source."""
@@ -110,8 +118,7 @@ def traffic_from_profile(achieved_us):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    src = hashlib.sha256(open(FUSED_SOURCE, "rb").read()).hexdigest()
-    if fields.get("fused.hip sha256") != src:
+    if fields.get("kernel source sha256") != fused_source_hash():
         return None
     try:
         return float(fields["HBM bytes per launch"])
@@ -153,7 +160,8 @@ def headline(d, args):
     import bit_dequant_skinny_amd as q4
     t = d.t
     N, K = 28672, 8192
-    M_list = [1, 2, 4, 8]
+    M_list = args.m
+    assert 1 in M_list, "the roofline is taken on the M=1 kernel"
     log("generating the K=%d N=%d workload" % (K, N))
     p = synth.q4_problem(1, N, K, BS, config=1, shape=0)
     p["A"] = {M: synth.activations_bf16(M, K, synth.seed(1, 0, 10 * M + 1)) for M in M_list}
@@ -214,7 +222,7 @@ def headline(d, args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16 MFMA, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": "fused 4-bit skinny GEMM, K=8192, N=28672, blocksize 64, "
                                "M=1,2,4,8 per step",
@@ -302,13 +310,19 @@ def other_configs(d):
                             "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
     res["bf16 K=2560 N=248320"] = rows
     del W
-    # the achievable copy rate with the same 128-bit loads (context for % of peak)
-    src = t.empty(1 << 30, dtype=t.uint8, device=d.dev)
-    dst = t.empty_like(src)
-    u = d.time_launches([lambda i: q4.q4_copy_probe(src, dst)], reps=20)[0]
-    res["copy probe 1 GiB (read+write)"] = {"us": round(u, 1),
-                                            "GB/s": round(2 * (1 << 30) / (u * 1e-6) / 1e9, 1)}
+    res["copy probe 1 GiB (read+write)"] = copy_probe(d)
     return res
+
+
+def copy_probe(d, nbytes=1 << 30):
+    """The achievable copy rate with the same 128-bit loads (context for % of
+    peak, and the known-size kernel the HBM byte counters are scaled by)."""
+    import bit_dequant_skinny_amd as q4
+    src = d.t.empty(nbytes, dtype=d.t.uint8, device=d.dev)
+    dst = d.t.empty_like(src)
+    u = d.time_launches([lambda i: q4.q4_copy_probe(src, dst)], reps=20)[0]
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": round(u, 1),
+            "GB/s": round(2 * nbytes / (u * 1e-6) / 1e9, 1)}
 
 
 def main():
@@ -318,6 +332,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--m", type=int, nargs="+", default=[1, 2, 4, 8],
+                    help="token rows per step (profiling runs use --m 1)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the 1 GiB copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -325,6 +343,9 @@ def main():
         sys.exit(2)
     d = Dev()
     assert d.t.cuda.is_available(), "bench.py needs an MI355X"
+    if args.copy_probe:
+        print(json.dumps({"copy probe 1 GiB (read+write)": copy_probe(d)}), flush=True)
+        return
     out, p, M_list = headline(d, args)
     log("headline: %.1f GB/s" % out["value"])
     if not args.quick:
