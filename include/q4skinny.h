@@ -71,8 +71,8 @@ enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
  *  (an fp32 product); products with A accumulate in fp32.
  *
  *  Q4_ERR_INVALID_ARGUMENT: NULL A/Wpacked/absmax/codebook/C, M/N/K < 0,
- *    K == 0, blocksize <= 0 or odd, K % blocksize != 0, A, Wpacked, absmax or
- *    C not 16-byte aligned.
+ *    K == 0, blocksize <= 0 or odd, K % blocksize != 0, A, Wpacked or absmax
+ *    not 16-byte aligned, codebook not 4-byte aligned, C not 2-byte aligned.
  *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}; M or N above
  *    2^30/K-sized limits (N * K / 2 must fit in 2^40 bytes).
  *  Which kernel runs: M <= q4_get_crossover_m() and M <= Q4_FUSED_MAX_M take
@@ -108,7 +108,7 @@ q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float
  *  rounding to bf16.
  *
  *  Q4_ERR_INVALID_ARGUMENT: NULL A/W/C, M/N/K < 0, K == 0, K % 8 != 0,
- *    A, W or C not 16-byte aligned, bias not 2-byte aligned.
+ *    A or W not 16-byte aligned, C or bias not 2-byte aligned.
  *  Q4_ERR_UNSUPPORTED: M > 5.
  */
 q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M, int N,
@@ -125,7 +125,8 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
  * Bit-exact: one fp32 multiply per element, denormals kept.
  *
  *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, N/K < 0, K == 0, bad blocksize
- *    (as above), out_dtype unknown, Wpacked/absmax/out not 16-byte aligned.
+ *    (as above), out_dtype unknown, Wpacked/absmax/out not 16-byte aligned,
+ *    codebook not 4-byte aligned.
  *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}.
  */
 q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
