@@ -36,10 +36,10 @@
 //
 // Schedule.  Workgroups are persistent and take every G-th tile; the KW
 // waves of a workgroup interleave each tile's segments, so together they read
-// 64*KW contiguous bytes of a row at a time.  Per slot a wave fetches the
-// block scales of its TB tiles' 16 rows with one access per lane (no
-// duplicates) and shares them across lane groups with ds_bpermute.  A wave
-// walks its work as
+// 64*KW contiguous bytes of a row at a time.  Per tile and slot a wave
+// fetches the two block scales of each of the tile's 16 rows with one 8-byte
+// load per lane, straight into the lanes that apply them.  A wave walks its
+// work as
 // (chunk of TB tiles) x (segment slot) x (tile in chunk), so the activation
 // operand of a segment (read from L2 one slot ahead) serves TB tiles.
 // Weight loads run one slot (TB units) ahead in a register ring and use
@@ -94,6 +94,14 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     int bs_log2, int tiles, uint16_t *__restrict__ C) {
     __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
     __shared__ float red[NBUF][KW][TB * SR][64];
+    // Block scales of the current and the next slot for the chunk's TB*16
+    // rows: 16 entries per row (the 16 64-wide blocks the KW = 8 waves cover
+    // in one slot; a larger block is repeated over the entries it spans).
+    // Rows are 18 floats apart so the 16 rows a wave reads at once fall in
+    // distinct banks.
+    constexpr int kScaleStride = 18;
+    __shared__ float scl[2][TB * 16 * kScaleStride];
+    static_assert(KW == 8 && 64 * KW == TB * 64, "one 16-byte scale load per thread per slot");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -125,40 +133,26 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // offsets advance incrementally in (chunk, slot, tile) order.
     const uint32_t w_tile_step = 16u * (uint32_t)G * row_bytes;
     const uint32_t w_lane = (uint32_t)wave * 64 + 16 * g;
-    // Scales: for each slot, lane (r, g) = (lane % 16, lane / 16) loads the
-    // two 64-wide block scales of segment (w + q*KW) for row r of the chunk's
-    // tiles g, g + 4, ... (one load pair per tile, no duplicates); the lanes
-    // that decode tile t fetch them from lane j + 16*(t % 4).
-    constexpr int SV = (TB + 3) / 4;  // scale load pairs per lane per slot
-    const uint32_t s_tile_step = 16u * (uint32_t)G * nb * 4;
-    const uint32_t s_half = bs_log2 == 6 ? 4u : 0u;
+    // Scales are staged through LDS one slot ahead: per slot the workgroup
+    // needs the KW*128/bs consecutive block scales of each of its TB*16 rows
+    // (64 bytes per row at bs = 64), which thread t fetches as 16-byte piece
+    // t % 4 of chunk row t / 4, whole cache lines with no duplicates.
+    const int s_row = tid >> 2;
+    const uint32_t s_piece = (uint32_t)(tid & 3) * 16;
+    const uint32_t s_win = (uint32_t)(KW * 128 * 4) >> bs_log2;  // bytes per row per slot
 
-    // issue cursor: chunk ic, slot iq
+    // Issue cursor: the (chunk, slot) whose loads are issued next.  Byte
+    // offsets advance incrementally in (chunk, slot) order.
     int ic = 0, iq = 0;
     uint32_t wo_q = 0, so_q = 0;
     auto chunk_base = [&](int c) {
         const uint32_t n0 = ((uint32_t)blockIdx.x + (uint32_t)(c * TB) * (uint32_t)G) * 16 + j;
         wo_q = n0 * row_bytes + w_lane;
-        so_q = n0 * nb * 4;
+        const uint32_t ns = ((uint32_t)blockIdx.x + (uint32_t)(c * TB + (s_row >> 4)) * (uint32_t)G) * 16 +
+                            (uint32_t)(s_row & 15);
+        so_q = ns * nb * 4;
     };
-    chunk_base(0);
-
-    uint4 wbuf[TB];
-    float sbuf[SV][2];
-    auto issue_slot = [&]() {  // loads of (chunk ic, slot iq) for its TB tiles
-#pragma unroll
-        for (int tr = 0; tr < TB; ++tr) {
-            const uint32_t wo = wo_q + tr * w_tile_step;
-            wbuf[tr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
-        }
-        const uint32_t k0 = ((uint32_t)wave + (uint32_t)iq * KW) * 128;
-#pragma unroll
-        for (int v = 0; v < SV; ++v) {
-            const int tt = g + 4 * v < TB ? g + 4 * v : 0;
-            const uint32_t so = so_q + tt * s_tile_step + (k0 >> bs_log2) * 4;
-            sbuf[v][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)so, 0, 0));
-            sbuf[v][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, (int)(so + s_half), 0, 0));
-        }
+    auto advance = [&]() {
         if (++iq == spw) {
             iq = 0;
             chunk_base(++ic);
@@ -166,12 +160,53 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             wo_q += 64u * KW;
         }
     };
+    chunk_base(0);
+
+    // Load ring: one weight register quad per tile.  The load of tile tr of
+    // the next slot is issued as soon as tile tr of the current slot has been
+    // decoded, so every wave keeps TB loads in flight at all times instead of
+    // draining its queue once per slot.
+    uint4 wbuf[TB];
+    auto issue_tile = [&](int tr) {
+        const uint32_t wo = wo_q + tr * w_tile_step;
+        wbuf[tr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
+    };
+    // This thread's piece of the scales of the cursor's slot; pieces past the
+    // slot's window or past the end of the row read zeros.
+    auto load_scales = [&]() -> floatx4 {
+        const uint32_t w0 = ((uint32_t)iq * KW * 128 >> bs_log2) * 4;  // window start in the row
+        const bool live = s_piece < s_win && w0 + s_piece < nb * 4;
+        const uint32_t so = live ? so_q + w0 + s_piece : kPastEnd;
+        return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sres, (int)so, 0, 0));
+    };
+    // Writes a piece into the staging buffer, repeating each scale over the
+    // 64-wide entries its block spans.
+    auto stage_scales = [&](const floatx4 &v, int buf) {
+        float *row = &scl[buf][s_row * kScaleStride];
+        const int e = (int)s_piece >> 2;  // first block of the piece in the window
+        if (bs_log2 == 6) {
+            *reinterpret_cast<floatx2 *>(row + e) = floatx2{v[0], v[1]};
+            *reinterpret_cast<floatx2 *>(row + e + 2) = floatx2{v[2], v[3]};
+        } else if (bs_log2 == 7) {
+            if (e < 8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *reinterpret_cast<floatx2 *>(row + 2 * (e + i)) = floatx2{v[i], v[i]};
+            }
+        } else if (e < 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<floatx2 *>(row + 4 * (e + i)) = floatx2{v[i], v[i]};
+                *reinterpret_cast<floatx2 *>(row + 4 * (e + i) + 2) = floatx2{v[i], v[i]};
+            }
+        }
+    };
 
     // Activation operand of slot q: token j's 8 activations for each of the
-    // lane's 4 dwords of codes.  Lanes of tokens >= M read token 0 (their
-    // outputs are discarded); k >= K (a ragged last segment, or a slot past
-    // the last segment) reads zeros, which cancels whatever codes sit there.
-    const uint32_t a_row = (uint32_t)(j < M ? j : 0) * (uint32_t)K * 2;
+    // lane's 4 dwords of codes.  Rows of tokens >= M lie past the end of A,
+    // and k >= K (a ragged last segment, or a slot past the last segment)
+    // takes an offset past every buffer: both read zeros without touching
+    // memory, which cancels whatever codes sit there.
+    const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;  // past the end of A for j >= M
     uint4 anext[4];
     auto load_a = [&](int q) {
         const uint32_t kk = ((uint32_t)wave + (uint32_t)q * KW) * 128;
@@ -183,8 +218,34 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         }
     };
 
-    issue_slot();
-    load_a(0);
+    {
+        const floatx4 s0 = load_scales();
+        load_a(0);
+#pragma unroll
+        for (int tr = 0; tr < TB; ++tr) issue_tile(tr);
+        advance();
+        stage_scales(s0, 0);
+        lds_barrier();
+    }
+    int qs = 0;  // slots done, for the staging buffer parity
+
+    // Table lookups of one tile: 16 packed bytes -> 32 bf16 hi/lo pairs.
+    auto decode = [&](const uint4 &wv, uint2 (&ev)[16]) {
+        uint32_t x[4] = {wv.x, wv.y, wv.z, wv.w};
+        // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
+        // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
+        const auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+        x[0] = s02[0]; x[2] = s02[1];
+        x[1] = s13[0]; x[3] = s13[1];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            // address = byte * 256 + lane_off: byte 1 from the packed
+            // dword, byte 0 from lane_off, bytes 2-3 zero
+            const uint32_t addr = __builtin_amdgcn_perm(x[i >> 2], lane_off, 0x0c0c0000u | ((4 + (i & 3)) << 8));
+            ev[i] = *reinterpret_cast<const uint2 *>(tab_bytes + addr);
+        }
+    };
 
     const floatx4 zerof = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < nchunks; ++c) {
@@ -208,45 +269,31 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
 #pragma unroll
             for (int s = 0; s < 8; ++s)
                 __asm__ volatile("" : "+v"(adup[s].x), "+v"(adup[s].y), "+v"(adup[s].z), "+v"(adup[s].w));
-            uint4 w[TB];
-            float am[TB][2];
-#pragma unroll
-            for (int tr = 0; tr < TB; ++tr) {
-                const int src = (j + 16 * (tr & 3)) * 4;
-                w[tr] = wbuf[tr];
-                am[tr][0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sbuf[tr >> 2][0])));
-                am[tr][1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(sbuf[tr >> 2][1])));
-            }
-            issue_slot();                     // the next slot's weights (and scales)
-            load_a(q + 1 < spw ? q + 1 : 0);  // and its activations
+            load_a(iq);  // the activations and scales of the slot issued next
+            const floatx4 snext = load_scales();
+            const float *sc = &scl[qs & 1][j * kScaleStride + 2 * wave];
+
             // Decode is software-pipelined one tile ahead: the 16 table reads
-            // of tile tr+1 are in flight while the MFMAs of tile tr run.
+            // of tile tr+1 are in flight while the MFMAs of tile tr run.  Each
+            // tile's ring entry is refilled with the next slot's loads right
+            // after its decode.
             uint2 e[2][16];
-            auto decode = [&](int tr, uint2 (&ev)[16]) {
-                uint32_t x[4] = {w[tr].x, w[tr].y, w[tr].z, w[tr].w};
-                // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
-                // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
-                const auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-                const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-                x[0] = s02[0]; x[2] = s02[1];
-                x[1] = s13[0]; x[3] = s13[1];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    // address = byte * 256 + lane_off: byte 1 from the packed
-                    // dword, byte 0 from lane_off, bytes 2-3 zero
-                    const uint32_t addr = __builtin_amdgcn_perm(x[i >> 2], lane_off, 0x0c0c0000u | ((4 + (i & 3)) << 8));
-                    ev[i] = *reinterpret_cast<const uint2 *>(tab_bytes + addr);
-                }
-            };
-            decode(0, e[0]);
+            float am[2][2];
+            decode(wbuf[0], e[0]);
+            {
+                const floatx2 a2 = *reinterpret_cast<const floatx2 *>(sc);
+                am[0][0] = a2[0];
+                am[0][1] = a2[1];
+            }
+            issue_tile(0);
 #pragma unroll
             for (int tr = 0; tr < TB; ++tr) {
-                // Per tile: its MFMAs, then the next tile's decode (VALU and
-                // LDS work that runs under the matrix cores), then the scale
-                // FMAs that consume the MFMA results.  Tiles past the end of
-                // a partial last chunk are computed too (their loads read
-                // zeros past the buffer end and their outputs are never
-                // stored), which keeps this loop one block.
+                // Per tile: its MFMAs, then the next tile's decode and loads
+                // (VALU, LDS and memory work that runs under the matrix
+                // cores), then the scale FMAs that consume the MFMA results.
+                // Tiles past the end of a partial last chunk are computed too
+                // (their loads read zeros past the buffer end and their
+                // outputs are never stored), which keeps this loop one block.
                 const uint2 *ev = e[tr & 1];
                 // two independent chains, one per 64-wide block
                 floatx4 D0 = zerof, D1 = zerof;
@@ -258,12 +305,25 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                     D1 = mfma_bf16_16x16x32(as_bf16x8(adup[4 + s]), as_bf16x8(b1), D1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (tr + 1 < TB) decode(tr + 1, e[(tr + 1) & 1]);
+                if (tr + 1 < TB) {
+                    decode(wbuf[tr + 1], e[(tr + 1) & 1]);
+                    const floatx2 a2 = *reinterpret_cast<const floatx2 *>(sc + (tr + 1) * 16 * kScaleStride);
+                    am[(tr + 1) & 1][0] = a2[0];
+                    am[(tr + 1) & 1][1] = a2[1];
+                    issue_tile(tr + 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int r = 0; r < SR; ++r)
-                    acc[tr][r] = fmaf(am[tr][1], D1[r], fmaf(am[tr][0], D0[r], acc[tr][r]));
+                    acc[tr][r] = fmaf(am[tr & 1][1], D1[r], fmaf(am[tr & 1][0], D0[r], acc[tr][r]));
             }
+            advance();
+            // Publish the next slot's scales.  The buffer written here was
+            // last read in the previous slot, which every wave finished before
+            // the previous barrier.
+            stage_scales(snext, (qs + 1) & 1);
+            lds_barrier();
+            ++qs;
         }
 
         // combine the KW partials of this chunk's tiles
@@ -319,11 +379,13 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
 // The kernel's byte offsets are 32-bit.  The weight offsets run up to two
 // chunks of every workgroup past the last tile (at most 2 * 4 * 1024 tiles of
 // 16 rows on a 256-CU part), so the matrix plus that margin must stay below
-// 4 GiB, and so must the activations.
+// 4 GiB; activation offsets reach 16 rows of K (the lanes of absent tokens
+// read past the end of A), which must stay below 4 GiB as well.
 bool q4_fused_mfma_fits(int M, int N, int K) {
+    (void)M;
     const uint64_t margin_rows = 2ull * 4 * 1024 * 16;
     return ((uint64_t)N + margin_rows) * (uint64_t)K / 2 < (1ull << 32) &&
-           (uint64_t)M * (uint64_t)K * 2 < (1ull << 31);
+           16ull * (uint64_t)K * 2 < (1ull << 32);
 }
 
 hipError_t launch_q4_fused_mfma(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
