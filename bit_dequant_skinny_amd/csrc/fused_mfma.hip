@@ -57,8 +57,7 @@ namespace {
 
 // Table entry e (a packed byte): x = (hi(cb[e & 15]), hi(cb[e >> 4])),
 // y = (lo(cb[e & 15]), lo(cb[e >> 4])), low nibble = even k = low half.
-__device__ __forceinline__ uint2 pair_table_entry(const float *__restrict__ cb, int e) {
-    const float c0 = cb[e & 15], c1 = cb[e >> 4];
+__device__ __forceinline__ uint2 pair_table_entry(float c0, float c1) {
     const uint32_t h0 = f32_to_bf16_rne(c0), h1 = f32_to_bf16_rne(c1);
     const uint32_t l0 = f32_to_bf16_rne(c0 - __uint_as_float(h0 << 16));
     const uint32_t l1 = f32_to_bf16_rne(c1 - __uint_as_float(h1 << 16));
@@ -105,12 +104,11 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    for (int e = tid; e < 256; e += 64 * KW) {
-        const uint2 v = pair_table_entry(codebook, e);
-#pragma unroll 8
-        for (int c = 0; c < 32; ++c) table[e * 32 + c] = v;
-    }
-    __syncthreads();
+    // The codebook is read first: loads complete in issue order, so the
+    // table can be built while the first weight loads are still in flight.
+    static_assert(64 * KW >= 256, "one table entry per thread");
+    const int e_tab = tid & 255;
+    const float cb0 = codebook[e_tab & 15], cb1 = codebook[e_tab >> 4];
     const char *tab_bytes = reinterpret_cast<const char *>(table);
     const uint32_t lane_off = (uint32_t)(lane & 31) * 8;
 
@@ -224,6 +222,11 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
 #pragma unroll
         for (int tr = 0; tr < TB; ++tr) issue_tile(tr);
         advance();
+        if (tid < 256) {
+            const uint2 v = pair_table_entry(cb0, cb1);
+#pragma unroll 8
+            for (int c = 0; c < 32; ++c) table[e_tab * 32 + c] = v;
+        }
         stage_scales(s0, 0);
         lds_barrier();
     }
