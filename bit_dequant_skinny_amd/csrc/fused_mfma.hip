@@ -34,20 +34,23 @@
 // Tokens feed the A operand (lane % 16 = token; lanes of tokens >= M are
 // computed and discarded).
 //
-// Schedule.  Workgroups are persistent and take every G-th tile; the KW
-// waves of a workgroup interleave each tile's segments, so together they read
-// 64*KW contiguous bytes of a row at a time.  Per tile and slot a wave
-// fetches the two block scales of each of the tile's 16 rows with one 8-byte
-// load per lane, straight into the lanes that apply them.  A wave walks its
-// work as
-// (chunk of TB tiles) x (segment slot) x (tile in chunk), so the activation
-// operand of a segment (read from L2 one slot ahead) serves TB tiles.
-// Weight loads run one slot (TB units) ahead in a register ring and use
-// buffer loads, whose hardware range check returns zeros past the end of a
-// buffer, so the loop has no branches.  After each chunk every wave writes its
-// fp32 partials to an LDS slot; after a barrier that leaves global loads in
-// flight, wave 0 sums the KW partials in wave order (deterministic, no
-// atomics) and stores bf16.
+// Schedule.  One persistent 8-wave workgroup per CU.  Tiles form groups of
+// TB (1..8, the tiles each CU must cover, chosen per shape so that only the
+// last group holds fewer live tiles); workgroup b computes groups b, b+G, ...
+// as chunks.  The waves of a workgroup interleave each chunk's 128-wide
+// segments, so together they read 64*KW contiguous bytes of every row at a
+// time, and walk their work as (slot = segment) x (tile), so the activation
+// operand of a segment (read from L2 one slot ahead) serves TB tiles.  Block
+// scales are staged through LDS one slot ahead by whole-line cooperative
+// loads.  Weight loads run RS slots ahead in a register ring of about 8
+// units per wave that continues across chunks, and use buffer loads, whose
+// hardware range check returns zeros past the end of a buffer: slots past
+// the last segment or past the workgroup's last chunk take an offset beyond
+// every buffer, so the loop has no bounds branches and reads nothing it does
+// not use.  At the end of a chunk every wave writes its fp32 partials to LDS;
+// after a barrier that leaves global loads in flight, each output is summed
+// over the waves in wave order (deterministic, no atomics) and stored as
+// bf16.
 #include "device.h"
 #include "launch.h"
 
@@ -83,30 +86,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kBufferFlags);
 }
 
-// SR: accumulator rows kept per lane (min(M, 4)); KW: waves per workgroup;
-// TB: tiles per chunk (also the weight loads in flight per wave); NBUF:
-// partial buffers (2 lets the next chunk's partials land while wave 0 reads).
-template <int SR, int KW, int TB, int NBUF>
+constexpr int KW = 8;  // waves per workgroup
+
+// SR: accumulator rows kept per lane (min(M, 4)).  TB: tiles per chunk.  RS:
+// segment slots the weight ring runs ahead, so every wave keeps TB*RS weight
+// loads in flight.  UF: slots per loop iteration, a multiple of RS with UF*TB
+// even, which makes the ring entry and the decode double-buffer index of
+// every unit compile-time constants.
+template <int SR, int TB, int RS, int UF>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook, int M, int N, int K,
-    int bs_log2, int tiles, uint16_t *__restrict__ C) {
+    int bs_log2, int groups, uint16_t *__restrict__ C) {
+    static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
+    static_assert(64 * KW >= 256, "one table entry per thread");
     __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
-    __shared__ float red[NBUF][KW][TB * SR][64];
-    // Block scales of the current and the next slot for the chunk's TB*16
-    // rows: 16 entries per row (the 16 64-wide blocks the KW = 8 waves cover
-    // in one slot; a larger block is repeated over the entries it spans).
-    // Rows are 18 floats apart so the 16 rows a wave reads at once fall in
+    __shared__ float red[KW][TB * SR][64];
+    // Raw block scales of the current and the next period of RS slots, one
+    // row per weight row of the chunk: the RS*KW*128/bs blocks the KW = 8
+    // waves cover in RS slots (16*RS at bs = 64).  There are 128/RS rows (one
+    // 16-byte piece per thread), at least TB*16: the threads past the chunk's
+    // rows write to spare rows, so the staging code has no branches.  Rows
+    // are RS*16 + 2 floats apart so the 16 rows a wave reads at once fall in
     // distinct banks.
-    constexpr int kScaleStride = 18;
-    __shared__ float scl[2][TB * 16 * kScaleStride];
-    static_assert(KW == 8 && 64 * KW == TB * 64, "one 16-byte scale load per thread per slot");
+    static_assert(TB * RS <= 8, "the chunk's rows fit the staging rows");
+    constexpr int kScaleStride = RS * 16 + 2;
+    __shared__ float scl[2][(128 / RS) * kScaleStride];
+    const int G = gridDim.x;
+    const int my_chunks = (groups - (int)blockIdx.x + G - 1) / G;
+    if (my_chunks <= 0) return;  // uniform over the workgroup
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     // The codebook is read first: loads complete in issue order, so the
     // table can be built while the first weight loads are still in flight.
-    static_assert(64 * KW >= 256, "one table entry per thread");
     const int e_tab = tid & 255;
     const float cb0 = codebook[e_tab & 15], cb1 = codebook[e_tab >> 4];
     const char *tab_bytes = reinterpret_cast<const char *>(table);
@@ -115,10 +128,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const int j = lane & 15;
     const int g = lane >> 4;
     const int nseg = (K + 127) >> 7;
-    const int spw = (nseg + KW - 1) / KW;  // segment slots per wave per tile
-    const int G = gridDim.x;
-    const int my_tiles = (tiles - (int)blockIdx.x + G - 1) / G;
-    const int nchunks = (my_tiles + TB - 1) / TB;
+    const int spw = (nseg + KW - 1) / KW;  // segment slots per wave per chunk
     const uint32_t row_bytes = (uint32_t)K >> 1;
     const uint32_t nb = (uint32_t)K >> bs_log2;
 
@@ -126,77 +136,79 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const __amdgpu_buffer_rsrc_t sres = make_rsrc(absmax, (uint32_t)N * nb * 4);
     const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
 
-    // Slot q of wave w is segment w + q*KW of every tile (the waves of a
-    // workgroup read 64*KW contiguous bytes of each row at a time).  Byte
-    // offsets advance incrementally in (chunk, slot, tile) order.
-    const uint32_t w_tile_step = 16u * (uint32_t)G * row_bytes;
-    const uint32_t w_lane = (uint32_t)wave * 64 + 16 * g;
-    // Scales are staged through LDS one slot ahead: per slot the workgroup
-    // needs the KW*128/bs consecutive block scales of each of its TB*16 rows
-    // (64 bytes per row at bs = 64), which thread t fetches as 16-byte piece
-    // t % 4 of chunk row t / 4, whole cache lines with no duplicates.
-    const int s_row = tid >> 2;
-    const uint32_t s_piece = (uint32_t)(tid & 3) * 16;
-    const uint32_t s_win = (uint32_t)(KW * 128 * 4) >> bs_log2;  // bytes per row per slot
+    // Chunk c of this workgroup is tile group blockIdx.x + c*G; tile tr of
+    // group q is q + tr*groups, so at any time neighbouring workgroups read
+    // neighbouring 16-row tiles.  Slot q of wave w is segment w + q*KW (the
+    // waves of a workgroup read 64*KW contiguous bytes of each row at a time).
+    auto group_of = [&](int c) { return (uint32_t)blockIdx.x + (uint32_t)c * (uint32_t)G; };
+    const uint32_t w_tile_step = 16u * (uint32_t)groups * row_bytes;
+    const uint32_t w_lane = 16 * g;
 
-    // Issue cursor: the (chunk, slot) whose loads are issued next.  Byte
-    // offsets advance incrementally in (chunk, slot) order.
+    // Weight issue cursor: the (chunk, slot) whose loads are issued next.
+    // Slots past this workgroup's last chunk and segments past the end of a
+    // row take an offset beyond the buffer: they read zeros without touching
+    // memory.
     int ic = 0, iq = 0;
-    uint32_t wo_q = 0, so_q = 0;
-    auto chunk_base = [&](int c) {
-        const uint32_t n0 = ((uint32_t)blockIdx.x + (uint32_t)(c * TB) * (uint32_t)G) * 16 + j;
-        wo_q = n0 * row_bytes + w_lane;
-        const uint32_t ns = ((uint32_t)blockIdx.x + (uint32_t)(c * TB + (s_row >> 4)) * (uint32_t)G) * 16 +
-                            (uint32_t)(s_row & 15);
-        so_q = ns * nb * 4;
+    uint32_t w_row0 = (group_of(0) * 16 + (uint32_t)j) * row_bytes + w_lane;
+    bool w_live = true;
+    auto w_seek = [&]() {
+        const int seg = wave + iq * KW;
+        w_live = ic < my_chunks && seg < nseg;
+        w_row0 = (group_of(ic) * 16 + (uint32_t)j) * row_bytes + (uint32_t)seg * 64 + w_lane;
     };
-    auto advance = [&]() {
+    auto w_advance = [&]() {
         if (++iq == spw) {
             iq = 0;
-            chunk_base(++ic);
-        } else {
-            wo_q += 64u * KW;
+            ++ic;
         }
+        w_seek();
     };
-    chunk_base(0);
+    w_seek();
+    auto issue = [&](uint4 &dst, int tr) {
+        const uint32_t wo = w_live ? w_row0 + (uint32_t)tr * w_tile_step : kPastEnd;
+        dst = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
+    };
 
-    // Load ring: one weight register quad per tile.  The load of tile tr of
-    // the next slot is issued as soon as tile tr of the current slot has been
-    // decoded, so every wave keeps TB loads in flight at all times instead of
-    // draining its queue once per slot.
-    uint4 wbuf[TB];
-    auto issue_tile = [&](int tr) {
-        const uint32_t wo = wo_q + tr * w_tile_step;
-        wbuf[tr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
-    };
-    // This thread's piece of the scales of the cursor's slot; pieces past the
-    // slot's window or past the end of the row read zeros.
+    // Scales are staged through LDS one period (RS slots) ahead: per period
+    // the workgroup needs the RS*KW*128/bs consecutive block scales of each of
+    // its TB*16 rows (64*RS bytes per row at bs = 64), which thread t fetches
+    // as 16-byte piece t % (4*RS) of chunk row t / (4*RS): at most one load
+    // per thread, whole cache lines with no duplicates.
+    const int s_row = tid / (4 * RS);
+    const bool s_thread = s_row < TB * 16;
+    const uint32_t s_piece = (uint32_t)(tid % (4 * RS)) * 16;
+    const uint32_t s_win = (uint32_t)(RS * KW * 128 * 4) >> bs_log2;  // bytes per row per period
+    int sc = 0, sq = 0;  // scale cursor: the first slot of the period loaded next
     auto load_scales = [&]() -> floatx4 {
-        const uint32_t w0 = ((uint32_t)iq * KW * 128 >> bs_log2) * 4;  // window start in the row
-        const bool live = s_piece < s_win && w0 + s_piece < nb * 4;
-        const uint32_t so = live ? so_q + w0 + s_piece : kPastEnd;
+        const uint32_t w0 = ((uint32_t)sq * KW * 128 >> bs_log2) * 4;  // window start in the row
+        const uint32_t ns = (group_of(sc) + (uint32_t)(s_row >> 4) * (uint32_t)groups) * 16 +
+                            (uint32_t)(s_row & 15);
+        const bool live = s_thread && sc < my_chunks && s_piece < s_win && w0 + s_piece < nb * 4;
+        const uint32_t so = live ? ns * nb * 4 + w0 + s_piece : kPastEnd;
+        sq += RS;
+        if (sq >= spw) {
+            sq = 0;
+            ++sc;
+        }
         return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sres, (int)so, 0, 0));
     };
-    // Writes a piece into the staging buffer, repeating each scale over the
-    // 64-wide entries its block spans.
+    // Writes a piece into the staging buffer; every thread writes, so the
+    // compiler has no branch to sink the scale load into and it stays a
+    // period ahead of its use.
     auto stage_scales = [&](const floatx4 &v, int buf) {
-        float *row = &scl[buf][s_row * kScaleStride];
-        const int e = (int)s_piece >> 2;  // first block of the piece in the window
-        if (bs_log2 == 6) {
-            *reinterpret_cast<floatx2 *>(row + e) = floatx2{v[0], v[1]};
-            *reinterpret_cast<floatx2 *>(row + e + 2) = floatx2{v[2], v[3]};
-        } else if (bs_log2 == 7) {
-            if (e < 8) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) *reinterpret_cast<floatx2 *>(row + 2 * (e + i)) = floatx2{v[i], v[i]};
-            }
-        } else if (e < 4) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<floatx2 *>(row + 4 * (e + i)) = floatx2{v[i], v[i]};
-                *reinterpret_cast<floatx2 *>(row + 4 * (e + i) + 2) = floatx2{v[i], v[i]};
-            }
-        }
+        float *row = &scl[buf][s_row * kScaleStride + (s_piece >> 2)];
+        *reinterpret_cast<floatx2 *>(row) = floatx2{v[0], v[1]};
+        *reinterpret_cast<floatx2 *>(row + 2) = floatx2{v[2], v[3]};
+    };
+    // In slot u of a period, wave w applies the scales of the 64-wide blocks
+    // e = 16u + 2w and e + 1 of the period window, which lie in bs-wide blocks
+    // e >> sh and (e + 1) >> sh: one 8-byte read at the even block below, then
+    // a select (both halves for bs = 64, one half twice for bs = 128 and 256).
+    const int sh = bs_log2 - 6;
+    auto read_scales = [&](const float *p, int pick, float (&out)[2]) {
+        const floatx2 a2 = *reinterpret_cast<const floatx2 *>(p);
+        out[0] = pick == 1 ? a2[1] : a2[0];
+        out[1] = pick == 0 ? a2[0] : a2[1];
     };
 
     // Activation operand of slot q: token j's 8 activations for each of the
@@ -216,22 +228,6 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         }
     };
 
-    {
-        const floatx4 s0 = load_scales();
-        load_a(0);
-#pragma unroll
-        for (int tr = 0; tr < TB; ++tr) issue_tile(tr);
-        advance();
-        if (tid < 256) {
-            const uint2 v = pair_table_entry(cb0, cb1);
-#pragma unroll 8
-            for (int c = 0; c < 32; ++c) table[e_tab * 32 + c] = v;
-        }
-        stage_scales(s0, 0);
-        lds_barrier();
-    }
-    int qs = 0;  // slots done, for the staging buffer parity
-
     // Table lookups of one tile: 16 packed bytes -> 32 bf16 hi/lo pairs.
     auto decode = [&](const uint4 &wv, uint2 (&ev)[16]) {
         uint32_t x[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -250,119 +246,168 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         }
     };
 
-    const floatx4 zerof = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nchunks; ++c) {
-        float acc[TB][SR];
+    // Prologue: the scales and activations of slot 0, RS slots of weights,
+    // then the table, then the first decode.
+    uint4 wbuf[RS][TB];
+    {
+        const floatx4 s0 = load_scales();
+        load_a(0);
 #pragma unroll
-        for (int tr = 0; tr < TB; ++tr)
+        for (int r = 0; r < RS; ++r) {
 #pragma unroll
-            for (int r = 0; r < SR; ++r) acc[tr][r] = 0.f;
-
-        for (int q = 0; q < spw; ++q) {
-            // Activation operand, each pair of activations duplicated.  Built
-            // once per slot and pinned in registers: an MFMA whose operand a
-            // VALU instruction has just written stalls for the hazard, so the
-            // compiler must not rebuild these next to every MFMA.
-            uint4 adup[8];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                adup[2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
-                adup[2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
-            }
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                __asm__ volatile("" : "+v"(adup[s].x), "+v"(adup[s].y), "+v"(adup[s].z), "+v"(adup[s].w));
-            load_a(iq);  // the activations and scales of the slot issued next
-            const floatx4 snext = load_scales();
-            const float *sc = &scl[qs & 1][j * kScaleStride + 2 * wave];
-
-            // Decode is software-pipelined one tile ahead: the 16 table reads
-            // of tile tr+1 are in flight while the MFMAs of tile tr run.  Each
-            // tile's ring entry is refilled with the next slot's loads right
-            // after its decode.
-            uint2 e[2][16];
-            float am[2][2];
-            decode(wbuf[0], e[0]);
-            {
-                const floatx2 a2 = *reinterpret_cast<const floatx2 *>(sc);
-                am[0][0] = a2[0];
-                am[0][1] = a2[1];
-            }
-            issue_tile(0);
-#pragma unroll
-            for (int tr = 0; tr < TB; ++tr) {
-                // Per tile: its MFMAs, then the next tile's decode and loads
-                // (VALU, LDS and memory work that runs under the matrix
-                // cores), then the scale FMAs that consume the MFMA results.
-                // Tiles past the end of a partial last chunk are computed too
-                // (their loads read zeros past the buffer end and their
-                // outputs are never stored), which keeps this loop one block.
-                const uint2 *ev = e[tr & 1];
-                // two independent chains, one per 64-wide block
-                floatx4 D0 = zerof, D1 = zerof;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
-                    const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
-                    D0 = mfma_bf16_16x16x32(as_bf16x8(adup[s]), as_bf16x8(b0), D0);
-                    D1 = mfma_bf16_16x16x32(as_bf16x8(adup[4 + s]), as_bf16x8(b1), D1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (tr + 1 < TB) {
-                    decode(wbuf[tr + 1], e[(tr + 1) & 1]);
-                    const floatx2 a2 = *reinterpret_cast<const floatx2 *>(sc + (tr + 1) * 16 * kScaleStride);
-                    am[(tr + 1) & 1][0] = a2[0];
-                    am[(tr + 1) & 1][1] = a2[1];
-                    issue_tile(tr + 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int r = 0; r < SR; ++r)
-                    acc[tr][r] = fmaf(am[tr & 1][1], D1[r], fmaf(am[tr & 1][0], D0[r], acc[tr][r]));
-            }
-            advance();
-            // Publish the next slot's scales.  The buffer written here was
-            // last read in the previous slot, which every wave finished before
-            // the previous barrier.
-            stage_scales(snext, (qs + 1) & 1);
-            lds_barrier();
-            ++qs;
+            for (int tr = 0; tr < TB; ++tr) issue(wbuf[r][tr], tr);
+            w_advance();
         }
-
-        // combine the KW partials of this chunk's tiles
-        const int buf = NBUF == 2 ? (c & 1) : 0;
-#pragma unroll
-        for (int tr = 0; tr < TB; ++tr)
-#pragma unroll
-            for (int r = 0; r < SR; ++r) red[buf][wave][tr * SR + r][lane] = acc[tr][r];
+        if (tid < 256) {
+            const uint2 v = pair_table_entry(cb0, cb1);
+#pragma unroll 8
+            for (int c = 0; c < 32; ++c) table[e_tab * 32 + c] = v;
+        }
+        stage_scales(s0, 0);
         lds_barrier();
-        if (wave == 0) {
+    }
+    uint2 e[2][16];
+    float am[2][2];
+    decode(wbuf[0][0], e[0]);
+    issue(wbuf[0][0], 0);
+
+    const floatx4 zerof = floatx4{0.f, 0.f, 0.f, 0.f};
+    float acc[TB][SR];
 #pragma unroll
-            for (int tr = 0; tr < TB; ++tr) {
-                const int n = ((int)blockIdx.x + (c * TB + tr) * G) * 16 + j;
+    for (int tr = 0; tr < TB; ++tr)
 #pragma unroll
-                for (int r = 0; r < SR; ++r) {
-                    float v = red[buf][0][tr * SR + r][lane];
-                    for (int w2 = 1; w2 < KW; ++w2) v += red[buf][w2][tr * SR + r][lane];
-                    const int tok = 4 * g + r;
-                    if (n < N && tok < M) C[(size_t)tok * N + n] = (uint16_t)f32_to_bf16_rne(v);
-                }
+        for (int r = 0; r < SR; ++r) acc[tr][r] = 0.f;
+    int pq = 0;   // the slot being computed
+    int qp = 0;   // periods done, for the staging buffer parity
+    floatx4 snext;  // the next period's scale piece
+
+    // One slot: TB units (tiles) of 16 rows x 128 k, software-pipelined one
+    // unit ahead: the table reads of unit u+1 (the next tile, or tile 0 of
+    // the next slot) are in flight while the MFMAs of unit u run, and each
+    // ring entry is refilled RS slots ahead right after its decode.  The slot
+    // loop starts every chunk at ring entry 0 and decode buffer 0, which holds
+    // when a workgroup has one chunk, or RS = 1 and TB is even.
+    auto slot = [&](auto us_c) {
+        constexpr int us = decltype(us_c)::value;
+        constexpr int r_cur = us % RS, r_next = (us + 1) % RS;
+        // Activation operand, each pair of activations duplicated.  Built
+        // once per slot and pinned in registers: an MFMA whose operand a VALU
+        // instruction has just written stalls for the hazard, so the compiler
+        // must not rebuild these next to every MFMA.
+        uint4 adup[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            adup[2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
+            adup[2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            __asm__ volatile("" : "+v"(adup[s].x), "+v"(adup[s].y), "+v"(adup[s].z), "+v"(adup[s].w));
+        load_a(pq + 1 == spw ? 0 : pq + 1);  // the activations of the next slot
+        if constexpr (us % RS == 0) snext = load_scales();  // and the next period's scales
+        const int s_blk = (16 * (us % RS) + 2 * wave) >> sh;
+        const int s_pick = sh == 0 ? -1 : (s_blk & 1);
+        const float *scs = &scl[qp & 1][j * kScaleStride + (s_blk & ~1)];
+        read_scales(scs, s_pick, am[(us * TB) & 1]);
+#pragma unroll
+        for (int tr = 0; tr < TB; ++tr) {
+            const int cur = (us * TB + tr) & 1;
+            const uint2 *ev = e[cur];
+            // two independent chains, one per 64-wide block
+            floatx4 D0 = zerof, D1 = zerof;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
+                const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
+                D0 = mfma_bf16_16x16x32(as_bf16x8(adup[s]), as_bf16x8(b0), D0);
+                D1 = mfma_bf16_16x16x32(as_bf16x8(adup[4 + s]), as_bf16x8(b1), D1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (tr + 1 < TB) {
+                decode(wbuf[r_cur][tr + 1], e[cur ^ 1]);
+                read_scales(scs + (tr + 1) * 16 * kScaleStride, s_pick, am[cur ^ 1]);
+                issue(wbuf[r_cur][tr + 1], tr + 1);
+            } else {
+                // tile 0 of the next slot: its weights are in the ring; its
+                // scales are read at the start of that slot
+                w_advance();
+                decode(wbuf[r_next][0], e[cur ^ 1]);
+                issue(wbuf[r_next][0], 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < SR; ++r)
+                acc[tr][r] = fmaf(am[cur][1], D1[r], fmaf(am[cur][0], D0[r], acc[tr][r]));
+        }
+        // At the end of a period, publish the next period's scales.  The
+        // buffer written here was last read in the previous period, which
+        // every wave finished before the previous barrier.
+        if constexpr (us % RS == RS - 1) {
+            stage_scales(snext, (qp + 1) & 1);
+            lds_barrier();
+            ++qp;
+        }
+        if (++pq == spw) pq = 0;
+    };
+
+    // Chunk end: combine the KW partials of the chunk's tiles.  Output (tile,
+    // token row) pair p is summed by wave p % KW in wave order (no atomics:
+    // the result is deterministic).  The buffer is rewritten at the next
+    // chunk end, after at least one more period barrier (a workgroup with
+    // several chunks has RS = 1: a barrier every slot).  The stores of C sit
+    // outside the unrolled slot loop: a store makes the compiler wait for
+    // every outstanding load before the next use of a loaded register, which
+    // here happens once per chunk instead of once per slot.
+    for (int pc = 0;;) {
+        for (int q0 = 0; q0 < spw; q0 += UF) {
+            slot(std::integral_constant<int, 0>{});
+            if constexpr (UF > 1) { if (q0 + 1 < spw) slot(std::integral_constant<int, 1 % UF>{}); }
+            if constexpr (UF > 2) { if (q0 + 2 < spw) slot(std::integral_constant<int, 2 % UF>{}); }
+            if constexpr (UF > 3) { if (q0 + 3 < spw) slot(std::integral_constant<int, 3 % UF>{}); }
+            if constexpr (UF > 4) { if (q0 + 4 < spw) slot(std::integral_constant<int, 4 % UF>{}); }
+            if constexpr (UF > 5) { if (q0 + 5 < spw) slot(std::integral_constant<int, 5 % UF>{}); }
+            if constexpr (UF > 6) { if (q0 + 6 < spw) slot(std::integral_constant<int, 6 % UF>{}); }
+            if constexpr (UF > 7) { if (q0 + 7 < spw) slot(std::integral_constant<int, 7 % UF>{}); }
+        }
+#pragma unroll
+        for (int tr = 0; tr < TB; ++tr)
+#pragma unroll
+            for (int r = 0; r < SR; ++r) {
+                red[wave][tr * SR + r][lane] = acc[tr][r];
+                acc[tr][r] = 0.f;
+            }
+        lds_barrier();
+        const uint32_t grp = group_of(pc);
+#pragma unroll
+        for (int p0 = 0; p0 < TB * SR; p0 += KW) {
+            const int p = p0 + wave;
+            if (p < TB * SR) {
+                const int tr = p / SR, r = p % SR;
+                float v = red[0][p][lane];
+#pragma unroll
+                for (int w2 = 1; w2 < KW; ++w2) v += red[w2][p][lane];
+                const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
+                const int tok = 4 * g + r;
+                if (n < N && tok < M) C[(size_t)tok * N + n] = (uint16_t)f32_to_bf16_rne(v);
             }
         }
-        if constexpr (NBUF == 1) lds_barrier();
+        if (++pc == my_chunks) break;
     }
 }
 
-template <int SR, int KW, int TB, int NBUF>
-hipError_t launch_cfg(const uint16_t *A, const uint8_t *Wp, const float *absmax,
-                      const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
-                      int wg_per_cu, hipStream_t s) {
-    const int tiles = (N + 15) / 16;
-    const DeviceInfo info = device_info();
-    int G = info.num_cus * wg_per_cu;
-    if (G > tiles) G = tiles;
-    fused_mfma_kernel<SR, KW, TB, NBUF><<<dim3(G), dim3(64 * KW), 0, s>>>(
-        A, Wp, absmax, codebook, M, N, K, bs_log2, tiles, C);
+template <int SR, int TB>
+hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
+                     const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
+                     int groups, int G, hipStream_t s) {
+    // Ring depth TB*RS of about 8 units (8 KiB of weights in flight per wave).
+    constexpr int RS = TB == 1 ? 8 : TB == 2 ? 4 : TB <= 4 ? 2 : 1;
+    constexpr int UF = (RS * TB) % 2 == 0 ? RS : 2 * RS;
+    // With RS > 1 or an odd TB every workgroup must compute a single chunk (the
+    // ring entry and decode buffer of a chunk's first unit are fixed at compile
+    // time); TB < 8 gives that, since then groups <= CUs.
+    if ((RS > 1 || TB % 2) && groups > G) return hipErrorInvalidValue;
+    fused_mfma_kernel<SR, TB, RS, UF><<<dim3(G), dim3(64 * KW), 0, s>>>(
+        A, Wp, absmax, codebook, M, N, K, bs_log2, groups, C);
     return hipGetLastError();
 }
 
@@ -370,24 +415,38 @@ template <int SR>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
                      hipStream_t s) {
-    // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS),
-    // 8 tiles per chunk so each wave keeps 8 KiB of weights in flight; for
-    // more than two tokens the partial tiles share a single buffer.
-    constexpr int NBUF = SR <= 2 ? 2 : 1;
-    return launch_cfg<SR, 8, 8, NBUF>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, 1, s);
+    // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS).
+    // TB = the tiles each CU must cover, up to 8, so that every chunk but the
+    // last holds TB live tiles; a workgroup loops over ceil(groups / CUs)
+    // chunks.
+    const int tiles = (N + 15) / 16;
+    const int cus = device_info().num_cus;
+    int tb = (tiles + cus - 1) / cus;
+    if (tb > 8) tb = 8;
+    const int groups = (tiles + tb - 1) / tb;
+    const int G = groups < cus ? groups : cus;
+    switch (tb) {
+    case 1: return launch_tb<SR, 1>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 2: return launch_tb<SR, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 3: return launch_tb<SR, 3>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 4: return launch_tb<SR, 4>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 5: return launch_tb<SR, 5>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 6: return launch_tb<SR, 6>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 7: return launch_tb<SR, 7>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    default: return launch_tb<SR, 8>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    }
 }
 
 }  // namespace
 
-// The kernel's byte offsets are 32-bit.  The weight offsets run up to two
-// chunks of every workgroup past the last tile (at most 2 * 4 * 1024 tiles of
-// 16 rows on a 256-CU part), so the matrix plus that margin must stay below
-// 4 GiB; activation offsets reach 16 rows of K (the lanes of absent tokens
-// read past the end of A), which must stay below 4 GiB as well.
+// The kernel's byte offsets are 32-bit.  Weight and scale offsets reach the
+// rows of the last tile group, at most 8 tiles (128 rows) past the last row,
+// so the matrix plus 256 rows must stay below 4 GiB; activation offsets reach
+// 16 rows of K (the lanes of absent tokens read past the end of A), which must
+// stay below 4 GiB as well.
 bool q4_fused_mfma_fits(int M, int N, int K) {
     (void)M;
-    const uint64_t margin_rows = 2ull * 4 * 1024 * 16;
-    return ((uint64_t)N + margin_rows) * (uint64_t)K / 2 < (1ull << 32) &&
+    return ((uint64_t)N + 256) * (uint64_t)K / 2 < (1ull << 32) &&
            16ull * (uint64_t)K * 2 < (1ull << 32);
 }
 
