@@ -10,8 +10,8 @@ different copy of the packed weights: the copies total >= 1 GiB, four times
 the 256 MB Infinity Cache, so every timed launch streams its weights from HBM.
 
 Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time
-of the K timed steps), per-M kernel times from HIP events on the launch
-stream, the roofline of the M=1 kernel, a CPU-oracle baseline on a bounded
+of the K timed steps), per-M kernel times from back-to-back launches between
+HIP events on the launch stream, the roofline of the M=1 kernel, a CPU-oracle baseline on a bounded
 sample, and (unless --quick) the other decode workloads: the 4096x4096 GEMV,
 the decode layer set with its fused-vs-split crossover, the bf16 skinny GEMM
 and the large-vocabulary projection.
@@ -79,24 +79,25 @@ class Dev:
         return out
 
     def time_launches(self, fns, reps, warmup=3):
-        """Average HIP-event duration of each launch in fns over `reps` rounds,
-        each round calling the functions in order (on torch's current stream,
-        which the library launches on)."""
+        """Average duration of each launch in fns: `reps` launches of one
+        function back to back (f(i) for i = 0..reps-1, so rotating weight
+        copies change every launch) between one pair of HIP events on torch's
+        current stream, which the library launches on.  Back-to-back launches
+        keep the per-launch event overhead out of the average."""
         t = self.t
-        for _ in range(warmup):
-            for f in fns:
-                f(0)
-        t.cuda.synchronize()
-        evs = [[(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
-                for _ in fns] for _ in range(reps)]
-        for r in range(reps):
-            for i, f in enumerate(fns):
-                evs[r][i][0].record()
-                f(r)
-                evs[r][i][1].record()
-        t.cuda.synchronize()
-        return [float(np.mean([evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(reps)])) * 1e3
-                for i in range(len(fns))]  # microseconds
+        out = []
+        for f in fns:
+            for i in range(warmup):
+                f(i)
+            t.cuda.synchronize()
+            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                f(i)
+            e1.record()
+            t.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / reps)  # microseconds
+        return out
 
 
 def fused_source_hash():
@@ -190,21 +191,17 @@ def headline(d, args):
             launch(M, n)
             n += 1
     t.cuda.synchronize()
-    evs = []
-    t.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         for M in M_list:
-            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-            e0.record()
             launch(M, n)
-            e1.record()
-            evs.append((M, e0, e1))
             n += 1
     t.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_m_us = {M: float(np.mean([a.elapsed_time(b) for (m, a, b) in evs if m == M])) * 1e3
-                for M in M_list}
+    # Per-M kernel times: back-to-back launches of one M over the rotating
+    # weight copies between one event pair.
+    per_m_us = dict(zip(M_list, d.time_launches(
+        [lambda i, M=M: launch(M, i) for M in M_list], reps=4 * R)))
     total = args.steps * sum(q4_bytes(M, N, K) for M in M_list)
     per_m = {}
     for M in M_list:
@@ -212,18 +209,8 @@ def headline(d, args):
         per_m[str(M)] = {"us": round(per_m_us[M], 2), "GB/s": round(gbs, 1),
                          "pct_peak": round(100 * gbs / PEAK_GBS, 1),
                          "path": "fused" if M <= q4.q4_get_crossover_m() else "split"}
-    # The roofline kernel (M=1) on its own: R*4 launches back to back on the
-    # launch stream, one event pair around them, so the average excludes the
-    # per-launch event overhead the step timing above carries.
-    reps = 4 * R
-    e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-    t.cuda.synchronize()
-    e0.record()
-    for i in range(reps):
-        launch(1, i)
-    e1.record()
-    t.cuda.synchronize()
-    m1_us = e0.elapsed_time(e1) * 1e3 / reps
+    # The roofline kernel is the M=1 launch, timed as above.
+    m1_us = per_m_us[1]
     ach = q4_bytes(1, N, K) / (m1_us * 1e-6) / 1e9
     traffic = traffic_from_profile()
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
