@@ -16,6 +16,13 @@ Function map (steps as numbered in the C file):
   bf16_gemm       O6  fp64-accumulated A * W^T (+ bias), plus S
   q4_gemm_w16     O7  O5 on bf16-rounded weights (split-path diagnostic)
   gemm_f32w       O8  plain fp64 GEMM on an already dequantized fp32 W
+  f16_to_double   O9  IEEE binary16 widened exactly
+  f32_to_f16      O9  fp32 -> binary16, nearest-even
+  dequant_f16     O9  O3 rounded to binary16
+  q4_gemm_ex      O10 O5 with bf16 / fp16 / fp32 activations and a bias
+
+Element types are named "bf16", "fp16", "fp32" (uint16 bit patterns for the
+two 16-bit types, float32 arrays for fp32).
 """
 from __future__ import annotations
 
@@ -77,6 +84,14 @@ class Oracle:
         lib.oracle_q4_gemm_w16.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
         lib.oracle_bf16_gemm.argtypes = [P, P, P, I, I, I, P, I, P, P]
         lib.oracle_gemm_f32w.argtypes = [P, P, I, I, I, P]
+        lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_double.restype = ctypes.c_double
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_f32_to_f16_array.argtypes = [P, I, P]
+        lib.oracle_dequant_f16.argtypes = [P, P, P, I, I, I, P]
+        lib.oracle_q4_gemm_ex.argtypes = [P, ctypes.c_int, P, P, P, P, ctypes.c_int, I, I, I, I,
+                                          P, I, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -160,6 +175,43 @@ class Oracle:
         S = np.empty((M, nc), dtype=np.float64)
         self.lib.oracle_bf16_gemm(_ptr(A), _ptr(W), _ptr(b), M, N, K, _ptr(c), nc,
                                   _ptr(C), _ptr(S))
+        return C, S
+
+    DTYPES = {"bf16": (0, np.uint16), "fp32": (1, np.float32), "fp16": (2, np.uint16)}
+
+    def f16_to_double(self, bits) -> np.ndarray:
+        """fp64 values of binary16 bit patterns (uint16 array, any shape)."""
+        b = _c(bits, np.uint16)
+        return np.array([self.lib.oracle_f16_to_double(int(v)) for v in b.ravel()],
+                        dtype=np.float64).reshape(b.shape)
+
+    def f32_to_f16(self, x) -> np.ndarray:
+        """binary16 bit patterns of an fp32 array (any shape), nearest-even."""
+        xs = _c(x, np.float32)
+        out = np.empty(xs.shape, dtype=np.uint16)
+        self.lib.oracle_f32_to_f16_array(_ptr(xs), xs.size, _ptr(out))
+        return out
+
+    def dequant_f16(self, Wpacked, absmax, codebook, N, K, bs) -> np.ndarray:
+        """binary16 bit patterns (uint16) of the dequantized weights."""
+        Wp, am, cb = _c(Wpacked, np.uint8), _c(absmax, np.float32), _c(codebook, np.float32)
+        out = np.empty((N, K), dtype=np.uint16)
+        self.lib.oracle_dequant_f16(_ptr(Wp), _ptr(am), _ptr(cb), N, K, bs, _ptr(out))
+        return out
+
+    def q4_gemm_ex(self, A, a_dtype, Wpacked, absmax, codebook, M, N, K, bs, bias=None,
+                   bias_dtype="bf16", cols=None):
+        """(C, S) in fp64 for activations of a_dtype and an optional bias."""
+        acode, anp = self.DTYPES[a_dtype]
+        bcode, bnp = self.DTYPES[bias_dtype]
+        Aa = _c(A, anp)
+        b = None if bias is None else _c(bias, bnp)
+        Wp, am, cb = _c(Wpacked, np.uint8), _c(absmax, np.float32), _c(codebook, np.float32)
+        c, nc = self._cols(cols, N)
+        C = np.empty((M, nc), dtype=np.float64)
+        S = np.empty((M, nc), dtype=np.float64)
+        self.lib.oracle_q4_gemm_ex(_ptr(Aa), acode, _ptr(Wp), _ptr(am), _ptr(cb), _ptr(b), bcode,
+                                   M, N, K, bs, _ptr(c), nc, _ptr(C), _ptr(S))
         return C, S
 
     def gemm_f32w(self, A_bf16, W_f32, M, N, K):

@@ -32,7 +32,9 @@
  *  - a dequantized weight is one IEEE binary32 product codebook[code]*absmax;
  *    the bf16 dequantized weight is that product rounded to bf16 with
  *    round-to-nearest-even;
- *  - activations, weights and bias in bf16 are widened exactly to fp32/fp64.
+ *  - activations, weights and bias in bf16, fp16 or fp32 are widened exactly
+ *    to fp64; a bias is added to the sum of products;
+ *  - fp16 is IEEE binary16, rounded to from fp32 to nearest even.
  *
  * Compiled with -O2 -ffp-contract=off (no fused multiply-add anywhere) and
  * without -ffast-math, so fp32 denormals are kept.
@@ -230,6 +232,125 @@ void oracle_gemm_f32w(const uint16_t *A, const float *W, int64_t M, int64_t N, i
                 sum += bf16_to_double(A[m * K + k]) * (double)W[n * K + k];
             C[m * N + n] = sum;
         }
+}
+
+/* ---- O9: IEEE binary16 <-> binary32 -------------------------------------- */
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.  A
+ * normal value is (1 + f/1024) * 2^(e - 15), a subnormal (e = 0) is
+ * f * 2^-24, e = 31 is infinity (f = 0) or NaN. */
+double oracle_f16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + f / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
+/* Nearest binary16 to a binary32 value, ties to the even fraction.  The
+ * 24-bit significand is shifted right to the binary16 precision at the
+ * value's exponent (11 bits for normals, fewer for subnormals); the bits
+ * shifted out decide the rounding exactly as in the bf16 case.  A carry out
+ * of the fraction moves to the next binade; past 65504 the result is
+ * infinity. */
+uint16_t oracle_f32_to_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000);
+    int E = (int)((u >> 23) & 0xFF);
+    uint32_t m = u & 0x7FFFFF;
+    if (E == 0xFF)
+        return (uint16_t)(sign | (m ? 0x7E00 : 0x7C00));
+    if (E == 0)
+        return sign; /* binary32 subnormals are below half the smallest binary16 subnormal */
+    uint32_t sig = (1u << 23) | m; /* value = sig * 2^(E - 150) */
+    int e16 = E - 127 + 15;       /* biased binary16 exponent for a normal result */
+    int shift = e16 >= 1 ? 13 : 13 + (1 - e16);
+    if (shift > 24)
+        return sign;
+    uint32_t q = sig >> shift;
+    uint32_t rem = sig & ((1u << shift) - 1);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1)))
+        q += 1;
+    if (e16 >= 1) {
+        if (q == 2048) { /* carried into the next binade */
+            q = 1024;
+            e16 += 1;
+        }
+        if (e16 >= 31)
+            return (uint16_t)(sign | 0x7C00);
+        return (uint16_t)(sign | (e16 << 10) | (q & 0x3FF));
+    }
+    /* subnormal result: q counts units of 2^-24; q == 1024 is the smallest normal */
+    return (uint16_t)(sign | q);
+}
+
+void oracle_f32_to_f16_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f32_to_f16(x[i]);
+}
+
+void oracle_dequant_f16(const uint8_t *Wpacked, const float *absmax, const float *codebook,
+                        int64_t N, int64_t K, int64_t bs, uint16_t *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            out[n * K + k] = oracle_f32_to_f16(oracle_w32(Wpacked, absmax, codebook, K, bs, n, k));
+}
+
+/* ---- O10: the fused 4-bit GEMM with any activation type and a bias ------- */
+/* Element types: 0 bf16, 1 binary32, 2 binary16 (the library's codes).
+ * Each element is widened exactly to fp64. */
+static double elem(const void *p, int64_t i, int dtype)
+{
+    if (dtype == 1)
+        return (double)((const float *)p)[i];
+    uint16_t b = ((const uint16_t *)p)[i];
+    return dtype == 2 ? oracle_f16_to_double(b) : bf16_to_double(b);
+}
+
+/* C[m, j] = sum over k of a[m,k] * w32(cols[j], k) + bias[cols[j]], fp64 in
+ * increasing k, bias added last; every product is exact in fp64 (at most 24
+ * by 24 significant bits).  S adds |bias| to the sum of |a*w|.  bias may be
+ * NULL. */
+void oracle_q4_gemm_ex(const void *A, int a_dtype, const uint8_t *Wpacked, const float *absmax,
+                       const float *codebook, const void *bias, int bias_dtype, int64_t M,
+                       int64_t N, int64_t K, int64_t bs, const int64_t *cols, int64_t ncols,
+                       double *C, double *S)
+{
+    if (cols == NULL)
+        ncols = N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < ncols; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0, sum_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double a = elem(A, m * K + k, a_dtype);
+                double w = (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k);
+                double p = a * w;
+                sum += p;
+                sum_abs += fabs(p);
+            }
+            if (bias) {
+                double b = elem(bias, n, bias_dtype);
+                sum += b;
+                sum_abs += fabs(b);
+            }
+            C[m * ncols + j] = sum;
+            if (S)
+                S[m * ncols + j] = sum_abs;
+        }
+    }
 }
 
 int oracle_max_threads(void)

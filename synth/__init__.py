@@ -18,6 +18,8 @@ weights, which these seeded draws stand in for):
             the 0.0 entry.  Codes are packed two per byte, low nibble = even k.
   * bf16 W: N(0, 0.02) in fp32 rounded to bf16.
   * bias  : N(0, 1) in fp32 rounded to bf16, shape [N].
+  * other element types: the same N(0, 1) draws kept in fp32, or rounded to
+    IEEE binary16 by numpy's cast (round-to-nearest-even).
 Seeds: ``seed(config, shape, tensor)`` = 1000*config + 100*shape + tensor, with
 tensor 2 for W, 3 for the bias and 10*M + 1 for A, so an M sweep reuses one W.
 """
@@ -32,7 +34,7 @@ import numpy as np
 __all__ = [
     "seed", "rng", "nf4_style_codebook", "random_codebook", "activations_bf16",
     "weights_f32", "quantize_blockwise", "pack_nibbles", "bf16_from_f32",
-    "bf16_weights", "bias_bf16", "q4_problem", "bf16_problem",
+    "bf16_weights", "bias_bf16", "q4_problem", "bf16_problem", "activations", "bias",
 ]
 
 
@@ -177,3 +179,24 @@ def bf16_problem(M: int, N: int, K: int, with_bias: bool, config: int = 0, shape
         "bias": bias_bf16(N, seed(config, shape, 3)) if with_bias else None,
         "M": M, "N": N, "K": K,
     }
+
+
+def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 draws as bf16 / fp16 bit patterns (uint16) or fp32 values."""
+    if dtype == "fp32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "fp16":
+        return np.ascontiguousarray(x.astype(np.float16).view(np.uint16))
+    if dtype == "bf16":
+        return bf16_from_f32(x)
+    raise ValueError("dtype must be bf16, fp16 or fp32")
+
+
+def activations(M: int, K: int, s: int, dtype: str = "bf16") -> np.ndarray:
+    """[M, K] N(0, 1) draws in dtype ("bf16" and "fp16" as uint16 bit patterns)."""
+    return _cast(rng(s).standard_normal((M, K), dtype=np.float32), dtype)
+
+
+def bias(N: int, s: int, dtype: str = "bf16") -> np.ndarray:
+    """[N] N(0, 1) draws in dtype."""
+    return _cast(rng(s).standard_normal(N, dtype=np.float32), dtype)

@@ -5,7 +5,8 @@ AssertionError when the oracle disagrees with:
   * hand-worked fixtures under tests/golden (nibble order, a dequantize + GEMM
     example, bf16 rounding cases),
   * the definition of correct rounding checked with exact rationals,
-  * torch's bf16 cast (a library routine) on random bit patterns,
+  * torch's bf16 cast and numpy's fp16 cast and widening (library routines)
+    on random and structured bit patterns,
   * exact rational brute force on tiny GEMMs (error within the fp64
     recursive-summation bound),
   * invariants: one-hot rows return a dequantized weight exactly, scaling A by
@@ -333,6 +334,114 @@ def pin_split_diagnostic(orc):
     W16 = orc.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
     C6, S6 = orc.bf16_gemm(p["A"], W16, None, M, N, K)
     assert np.array_equal(C7, C6) and np.array_equal(S7, S6)
+
+
+# --------------------------------------------------------------------------- O9
+def _f16_val(bits) -> float:
+    return float(np.array([int(bits)], dtype=np.uint16).view(np.float16)[0])
+
+
+def pin_f16_decode_exhaustive(orc):
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = orc.f16_to_double(bits)
+    ref = bits.view(np.float16).astype(np.float64)  # numpy's exact widening
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_f16_rounding_golden(orc):
+    for line in golden_lines("f16_rounding.txt"):
+        src, dst = line.split()[:2]
+        x = np.array([int(src, 16)], dtype=np.uint32).view(np.float32)
+        got = int(orc.f32_to_f16(x)[0])
+        assert got == int(dst, 16), (line, hex(got))
+
+
+def pin_f16_rounding_vs_numpy(orc):
+    g = synth.rng(32)
+    bits = g.integers(0, 2 ** 32, size=1 << 19, dtype=np.uint64).astype(np.uint32)
+    # every fp32 exponent that lands in or near the fp16 range, with the tie,
+    # near-tie and carry-out low bits of the 13 dropped bits
+    exps = np.arange(95, 145, dtype=np.uint32) << 23
+    mants = np.array([0, 0x1000, 0xFFF, 0x1001, 0x3000, 0x7FF000, 0x7FFFFF, 0x7FE000, 0x2000],
+                     dtype=np.uint32)
+    edge = (exps[:, None] | mants[None, :]).ravel()
+    bits = np.concatenate([bits, edge, edge | 0x80000000])
+    x = bits.view(np.float32)
+    x = x[~np.isnan(x)]
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.f32_to_f16(x), ref)
+
+
+def pin_dequant_f16_is_rounded_product(orc):
+    N, K, bs = 4, 128, 64
+    p = synth.q4_problem(1, N, K, bs, config=97, codebook=synth.random_codebook(5))
+    w = orc.dequant_f32(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
+    h = orc.dequant_f16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
+    assert np.array_equal(h, w.astype(np.float16).view(np.uint16))
+
+
+# -------------------------------------------------------------------------- O10
+def _act_val(x, dtype) -> float:
+    if dtype == "fp32":
+        return float(x)
+    return _f16_val(x) if dtype == "fp16" else _bf16_val(x)
+
+
+def pin_q4_gemm_ex_bruteforce(orc):
+    g = synth.rng(43)
+    cases = [(1, 3, 64, 64, "fp16", "fp16"), (2, 2, 128, 64, "fp32", "fp32"),
+             (3, 2, 64, 32, "fp16", "bf16"), (2, 3, 128, 128, "fp32", None)]
+    for M, N, K, bs, adt, bdt in cases:
+        cb = synth.random_codebook(int(g.integers(100)))
+        codes = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+        absmax = g.uniform(0.01, 0.1, size=(N, K // bs)).astype(np.float32)
+        A = synth.activations(M, K, int(g.integers(1 << 30)), adt)
+        b = None if bdt is None else synth.bias(N, int(g.integers(1 << 30)), bdt)
+        C, S = orc.q4_gemm_ex(A, adt, synth.pack_nibbles(codes), absmax, cb, M, N, K, bs,
+                              bias=b, bias_dtype=bdt or "bf16")
+        bound = Fraction(_fp64_sum_bound(K + 1))
+        for m in range(M):
+            for n in range(N):
+                terms = []
+                for k in range(K):
+                    w = _frac(np.float32(float(_frac(cb[codes[n, k]]) * _frac(absmax[n, k // bs]))))
+                    terms.append(_frac(_act_val(A[m, k], adt)) * w)
+                if b is not None:
+                    terms.append(_frac(_act_val(b[n], bdt)))
+                ce = sum(terms, Fraction(0))
+                se = sum((abs(t) for t in terms), Fraction(0))
+                assert abs(_frac(C[m, n]) - ce) <= bound * se, (adt, m, n)
+                assert abs(_frac(S[m, n]) - se) <= bound * se
+
+
+def pin_q4_gemm_ex_reduces_to_bf16(orc):
+    M, N, K, bs = 3, 5, 192, 64
+    p = synth.q4_problem(M, N, K, bs, config=98)
+    args = (p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    C5, S5 = orc.q4_gemm(p["A"], *args)
+    C, S = orc.q4_gemm_ex(p["A"], "bf16", *args)
+    assert np.array_equal(C, C5) and np.array_equal(S, S5)
+    # the same values held as fp32 give the same sums
+    A32 = (p["A"].astype(np.uint32) << 16).view(np.float32)
+    C, S = orc.q4_gemm_ex(A32, "fp32", *args)
+    assert np.array_equal(C, C5) and np.array_equal(S, S5)
+
+
+def pin_q4_gemm_ex_bias_alone(orc):
+    M, N, K, bs = 2, 6, 128, 64
+    p = synth.q4_problem(M, N, K, bs, config=99)
+    for dt in ("bf16", "fp16", "fp32"):
+        b = synth.bias(N, 7, dt)
+        A = np.zeros((M, K), dtype=np.float32 if dt == "fp32" else np.uint16)
+        C, S = orc.q4_gemm_ex(A, dt, p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs,
+                              bias=b, bias_dtype=dt)
+        for n in range(N):
+            assert np.all(C[:, n] == _act_val(b[n], dt)), (dt, n)
+            assert np.all(S[:, n] == abs(_act_val(b[n], dt)))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -37,6 +37,19 @@ MUTANTS = {
                         "double w = (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k);\n                double p = (k == K - 1) ? 0.0 : a * w;"),
     "bias_dropped": ("sum += b;", "sum += 0.0 * b;"),
     "bf16_w_transposed": ("bf16_to_double(W[n * K + k])", "bf16_to_double(W[k * N + n])"),
+    "f16_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "f16_exponent_bias": ("v = ldexp(1.0 + f / 1024.0, e - 15);", "v = ldexp(1.0 + f / 1024.0, e - 16);"),
+    "f16_truncates": ("if (rem > half || (rem == half && (q & 1)))\n        q += 1;", "if (0)\n        q += 1;"),
+    "f16_ties_away": ("if (rem > half || (rem == half && (q & 1)))\n        q += 1;",
+                      "if (rem >= half)\n        q += 1;"),
+    "f16_no_binade_carry": ("if (q == 2048) { /* carried into the next binade */",
+                            "if (q == 4096) { /* carried into the next binade */"),
+    "f16_no_overflow": ("if (e16 >= 31)\n            return (uint16_t)(sign | 0x7C00);", "if (0)\n            return 0;"),
+    "ex_fp16_read_as_bf16": ("return dtype == 2 ? oracle_f16_to_double(b) : bf16_to_double(b);",
+                             "return bf16_to_double(b);"),
+    "ex_bias_dropped": ("double b = elem(bias, n, bias_dtype);\n                sum += b;",
+                        "double b = elem(bias, n, bias_dtype);\n                sum += 0.0 * b;"),
+    "ex_a_transposed": ("double a = elem(A, m * K + k, a_dtype);", "double a = elem(A, k * M + m, a_dtype);"),
     "w16_not_rounded": ("double p = a * bf16_to_double(w16);",
                         "double p = a * (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k) + 0.0 * w16;"),
 }
