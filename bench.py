@@ -305,6 +305,29 @@ def other_configs(d):
                                 "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
         res["bf16+bias K=2560 N=%d" % N] = rows
         del sets, W
+    log("4-bit path: bias epilogue and other element types, K=8192 N=28672")
+    N, K = 28672, 8192
+    p = synth.q4_problem(1, N, K, BS, config=1, shape=0)
+    sets = d.copies((d.raw(p["Wpacked"]), d.raw(p["absmax"])), q4_bytes(1, N, K))
+    cb = d.raw(p["codebook"])
+    bias32 = d.raw(synth.bias(N, synth.seed(1, 0, 3), "fp32"))
+    rows = {}
+    for adt, tdt in (("fp16", t.float16), ("fp32", t.float32)):
+        for M in (1, 8):
+            a_h = synth.activations(M, K, synth.seed(1, 0, 10 * M + 1), adt)
+            A = (d.raw(a_h).view(t.float16) if adt == "fp16" else d.raw(a_h))
+            C = t.empty((M, N), dtype=t.float32, device=d.dev)
+
+            def f(i, A=A, C=C):
+                Wp, am = sets[i % len(sets)]
+                q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, bias=bias32, out_dtype=t.float32)
+            u = d.time_launches([f], reps=4 * len(sets))[0]
+            nbytes = q4_bytes(M, N, K) + (2 if adt == "fp16" else 6) * M * K + 2 * M * N + 4 * N
+            gbs = nbytes / (u * 1e-6) / 1e9
+            rows["%s A, fp32 C + bias, M=%d" % (adt, M)] = {
+                "us": round(u, 2), "GB/s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+    res["q4 K=8192 N=28672 dtypes+bias"] = rows
+    del sets
     log("C5 large-vocabulary projection")
     q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0)
     K, N = 2560, 248320

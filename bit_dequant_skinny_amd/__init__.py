@@ -6,7 +6,8 @@ stream.  There is no CPU fallback: if the library is missing, importing the
 functions below raises.
 
 Entry points (same names as the C ABI in include/q4skinny.h):
-  q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize=64, out=None, path="auto")
+  q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize=64, out=None, path="auto",
+                 bias=None, out_dtype=None)   (q4_gemm_skinny_path / q4_gemm_skinny_ex)
   bf16_gemm_skinny(A, W, bias=None, out=None)
   q4_dequant(Wpacked, absmax, codebook, blocksize=64, out_dtype=torch.bfloat16, out=None)
   q4_get_crossover_m() / q4_set_crossover_m(m) / q4_release_workspace()
@@ -21,13 +22,13 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4skinny.so")
 
 Q4_OK, Q4_ERR_INVALID_ARGUMENT, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = 0, 1, 2, 3
-Q4_DTYPE_BF16, Q4_DTYPE_FP32 = 0, 1
+Q4_DTYPE_BF16, Q4_DTYPE_FP32, Q4_DTYPE_FP16 = 0, 1, 2
 PATHS = {"auto": 0, "fused": 1, "split": 2}
 FUSED_MAX_M = 16
 
 # Every symbol include/q4skinny.h declares.
 EXPORTS = (
-    "q4_gemm_skinny", "q4_gemm_skinny_path", "bf16_gemm_skinny", "q4_dequant",
+    "q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex", "bf16_gemm_skinny", "q4_dequant",
     "q4_get_crossover_m", "q4_set_crossover_m", "q4_release_workspace", "q4_last_error",
     "q4_copy_probe", "q4_version",
 )
@@ -52,11 +53,13 @@ def lib():
         P, I = ctypes.c_void_p, ctypes.c_int
         L.q4_gemm_skinny.argtypes = [P, P, P, P, I, I, I, I, P, P]
         L.q4_gemm_skinny_path.argtypes = [P, P, P, P, I, I, I, I, P, P, I]
+        L.q4_gemm_skinny_ex.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
         L.bf16_gemm_skinny.argtypes = [P, P, P, I, I, I, P, P]
         L.q4_dequant.argtypes = [P, P, P, I, I, I, P, I, P]
         L.q4_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
         L.q4_set_crossover_m.argtypes = [I]
-        for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "bf16_gemm_skinny", "q4_dequant",
+        for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
+                     "bf16_gemm_skinny", "q4_dequant",
                      "q4_copy_probe", "q4_set_crossover_m", "q4_release_workspace"):
             getattr(L, name).restype = ctypes.c_int
         L.q4_get_crossover_m.restype = ctypes.c_int
@@ -81,6 +84,16 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _dtype_code(dtype):
+    torch = _torch()
+    codes = {torch.bfloat16: Q4_DTYPE_BF16, torch.float16: Q4_DTYPE_FP16,
+             torch.float32: Q4_DTYPE_FP32}
+    if dtype not in codes:
+        raise TypeError("dtype must be torch.bfloat16, torch.float16 or torch.float32, got %s"
+                        % dtype)
+    return codes[dtype]
+
+
 def _dev(t, name, dtype):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
@@ -94,8 +107,13 @@ def _dev(t, name, dtype):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, path: str = "auto"):
-    """C[M,N] = A[M,K] * dequant(W)[N,K]^T in bf16 (fp32 accumulation)."""
+def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, path: str = "auto",
+                   bias=None, out_dtype=None):
+    """C[M,N] = A[M,K] * dequant(W)[N,K]^T (+ bias), fp32 accumulation.
+
+    A may be bf16, fp16 or fp32; C (and bias) have out_dtype, by default A's
+    dtype.  bf16 in and out without a bias calls q4_gemm_skinny_path, anything
+    else q4_gemm_skinny_ex."""
     torch = _torch()
     if A.dim() != 2 or Wpacked.dim() != 2:
         raise ValueError("A must be [M, K] and Wpacked [N, K/2]")
@@ -107,14 +125,25 @@ def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, 
         raise ValueError("absmax must be [N, K/blocksize]")
     if codebook.numel() != 16:
         raise ValueError("codebook must hold 16 entries")
+    out_dtype = A.dtype if out_dtype is None else out_dtype
+    a_code, c_code = _dtype_code(A.dtype), _dtype_code(out_dtype)
+    if bias is not None and tuple(bias.shape) != (N,):
+        raise ValueError("bias must be [N]")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
     elif tuple(out.shape) != (M, N):
         raise ValueError("out must be [M, N]")
-    _check(lib().q4_gemm_skinny_path(
-        _dev(A, "A", torch.bfloat16), _dev(Wpacked, "Wpacked", torch.uint8),
-        _dev(absmax, "absmax", torch.float32), _dev(codebook, "codebook", torch.float32),
-        M, N, K, blocksize, _dev(out, "out", torch.bfloat16), _stream(A), PATHS[path]))
+    if a_code == Q4_DTYPE_BF16 and c_code == Q4_DTYPE_BF16 and bias is None:
+        _check(lib().q4_gemm_skinny_path(
+            _dev(A, "A", torch.bfloat16), _dev(Wpacked, "Wpacked", torch.uint8),
+            _dev(absmax, "absmax", torch.float32), _dev(codebook, "codebook", torch.float32),
+            M, N, K, blocksize, _dev(out, "out", torch.bfloat16), _stream(A), PATHS[path]))
+        return out
+    bptr = None if bias is None else _dev(bias, "bias", out_dtype)
+    _check(lib().q4_gemm_skinny_ex(
+        _dev(A, "A", A.dtype), a_code, _dev(Wpacked, "Wpacked", torch.uint8),
+        _dev(absmax, "absmax", torch.float32), _dev(codebook, "codebook", torch.float32), bptr,
+        M, N, K, blocksize, _dev(out, "out", out_dtype), c_code, _stream(A), PATHS[path]))
     return out
 
 
@@ -139,17 +168,15 @@ def bf16_gemm_skinny(A, W, bias=None, out=None):
 
 
 def q4_dequant(Wpacked, absmax, codebook, blocksize: int = 64, out_dtype=None, out=None):
-    """W[N,K] = codebook[code] * absmax, as bf16 (default) or fp32."""
+    """W[N,K] = codebook[code] * absmax, as bf16 (default), fp16 or fp32."""
     torch = _torch()
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
-    if out_dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
     N, K = Wpacked.shape[0], Wpacked.shape[1] * 2
     if out is None:
         out = torch.empty((N, K), dtype=out_dtype, device=Wpacked.device)
     elif tuple(out.shape) != (N, K) or out.dtype != out_dtype:
         raise ValueError("out must be [N, K] of out_dtype")
-    code = Q4_DTYPE_BF16 if out_dtype == torch.bfloat16 else Q4_DTYPE_FP32
+    code = _dtype_code(out_dtype)
     _check(lib().q4_dequant(
         _dev(Wpacked, "Wpacked", torch.uint8), _dev(absmax, "absmax", torch.float32),
         _dev(codebook, "codebook", torch.float32), N, K, blocksize, _dev(out, "out", out_dtype),

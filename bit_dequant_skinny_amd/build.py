@@ -4,7 +4,7 @@
 
 Produces ``bit_dequant_skinny_amd/libq4skinny.so`` with hipcc.  All device code
 is built with packed-fp32 instructions disabled (the compiler still emits
-ordinary v_fma_f32 / v_mul_f32).
+ordinary v_fma_f32 / v_mul_f32) and without floating-point contraction.
 """
 from __future__ import annotations
 
@@ -22,6 +22,11 @@ ARCH = "gfx950"
 
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    # every multiply and add rounds as written: the kernels spell out their
+    # fused multiply-adds with fmaf, and the dequantize must round the fp32
+    # product before narrowing it (contraction would fold both into one
+    # mixed-precision fma with a single rounding and lose the sign of zero)
+    "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

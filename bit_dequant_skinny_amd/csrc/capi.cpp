@@ -167,15 +167,19 @@ q4_status drain_prior_error() {
     return Q4_OK;
 }
 
-q4_status run_fused(const void *A, const uint8_t *Wp, const float *am, const float *cb, int M,
-                    int N, int K, int bs_log2, void *C, hipStream_t s) {
-    hipError_t e = q4::launch_q4_fused(static_cast<const uint16_t *>(A), Wp, am, cb, M, N, K,
-                                       bs_log2, static_cast<uint16_t *>(C), s);
+bool known_dtype(int dt) { return dt == Q4_DTYPE_BF16 || dt == Q4_DTYPE_FP16 || dt == Q4_DTYPE_FP32; }
+size_t dtype_size(int dt) { return dt == Q4_DTYPE_FP32 ? 4 : 2; }
+
+q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
+                    const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
+                    hipStream_t s) {
+    hipError_t e = q4::launch_q4_fused(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, C, c_dt, s);
     return check_launch(e, "fused");
 }
 
-q4_status run_split(const void *A, const uint8_t *Wp, const float *am, const float *cb, int M,
-                    int N, int K, int bs_log2, void *C, hipStream_t s) {
+q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
+                    const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
+                    hipStream_t s) {
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) {
@@ -186,11 +190,10 @@ q4_status run_split(const void *A, const uint8_t *Wp, const float *am, const flo
     const size_t bytes = (size_t)N * (size_t)K * 2;
     q4_status st = workspace(device, s, bytes, &ws);
     if (st != Q4_OK) return st;
-    e = q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, true, s);
+    e = q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, Q4_DTYPE_BF16, s);
     st = check_launch(e, "dequant");
     if (st != Q4_OK) return st;
-    e = q4::launch_bf16_gemm(static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(ws),
-                             nullptr, M, N, K, static_cast<uint16_t *>(C), s);
+    e = q4::launch_bf16_gemm(A, a_dt, static_cast<const uint16_t *>(ws), bias, M, N, K, C, c_dt, s);
     return check_launch(e, "gemm");
 }
 
@@ -221,11 +224,15 @@ DeviceInfo device_info() {
 
 extern "C" {
 
-q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
-                              const float *codebook, int M, int N, int K, int blocksize,
-                              void *C, void *stream, int path) {
+q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
+                            const float *absmax, const float *codebook, const void *bias, int M,
+                            int N, int K, int blocksize, void *C, int c_dtype, void *stream,
+                            int path) {
     if (path != Q4_PATH_AUTO && path != Q4_PATH_FUSED && path != Q4_PATH_SPLIT)
         return fail(Q4_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+    if (!known_dtype(a_dtype) || !known_dtype(c_dtype))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown dtype (a_dtype=%d, c_dtype=%d)", a_dtype,
+                    c_dtype);
     if (M < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d)", M);
     int bs_log2 = 0;
     q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
@@ -234,22 +241,36 @@ q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float
         return fail(Q4_ERR_UNSUPPORTED, "fused path supports M <= %d (M=%d)", Q4_FUSED_MAX_M, M);
     if ((int64_t)M * K > (int64_t(1) << 40))
         return fail(Q4_ERR_UNSUPPORTED, "M*K too large");
-    if (M == 0 || N == 0) return ok();
-    if (!A || !Wpacked || !absmax || !codebook || !C)
-        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-    if (!aligned(A, 16) || !aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) ||
-        !aligned(C, 2))
-        return fail(Q4_ERR_INVALID_ARGUMENT,
-                    "A, Wpacked and absmax must be 16-byte aligned, C 2-byte aligned");
-    drain_prior_error();
-    hipStream_t s = static_cast<hipStream_t>(stream);
     bool fused;
     if (path == Q4_PATH_FUSED) fused = true;
     else if (path == Q4_PATH_SPLIT) fused = false;
     else fused = M <= crossover() && M <= Q4_FUSED_MAX_M;
-    st = fused ? run_fused(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s)
-               : run_split(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+    if (!fused && a_dtype == Q4_DTYPE_FP32)
+        return fail(Q4_ERR_UNSUPPORTED,
+                    "fp32 activations take the fused path only (M <= %d, M=%d)", Q4_FUSED_MAX_M, M);
+    if (M == 0 || N == 0) return ok();
+    if (!A || !Wpacked || !absmax || !codebook || !C)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    const size_t cs = dtype_size(c_dtype);
+    if (!aligned(A, 16) || !aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) ||
+        !aligned(C, cs) || (bias && !aligned(bias, cs)))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "A, Wpacked and absmax must be 16-byte aligned, C and bias aligned to "
+                    "their element size");
+    drain_prior_error();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = fused ? run_fused(A, a_dtype, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C,
+                           c_dtype, s)
+               : run_split(A, a_dtype, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C,
+                           c_dtype, s);
     return st == Q4_OK ? ok() : st;
+}
+
+q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
+                              const float *codebook, int M, int N, int K, int blocksize,
+                              void *C, void *stream, int path) {
+    return q4_gemm_skinny_ex(A, Q4_DTYPE_BF16, Wpacked, absmax, codebook, nullptr, M, N, K,
+                             blocksize, C, Q4_DTYPE_BF16, stream, path);
 }
 
 q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *absmax,
@@ -274,17 +295,16 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
         return fail(Q4_ERR_INVALID_ARGUMENT,
                     "A and W must be 16-byte aligned, C and bias 2-byte aligned");
     drain_prior_error();
-    hipError_t e = q4::launch_bf16_gemm(
-        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W),
-        static_cast<const uint16_t *>(bias), M, N, K, static_cast<uint16_t *>(C),
-        static_cast<hipStream_t>(stream));
+    hipError_t e = q4::launch_bf16_gemm(A, Q4_DTYPE_BF16, static_cast<const uint16_t *>(W), bias,
+                                        M, N, K, C, Q4_DTYPE_BF16,
+                                        static_cast<hipStream_t>(stream));
     q4_status st = check_launch(e, "gemm");
     return st == Q4_OK ? ok() : st;
 }
 
 q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook, int N,
                      int K, int blocksize, void *out, int out_dtype, void *stream) {
-    if (out_dtype != Q4_DTYPE_BF16 && out_dtype != Q4_DTYPE_FP32)
+    if (!known_dtype(out_dtype))
         return fail(Q4_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
     int bs_log2 = 0;
     q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
@@ -295,8 +315,8 @@ q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *c
     if (!aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) || !aligned(out, 16))
         return fail(Q4_ERR_INVALID_ARGUMENT, "Wpacked, absmax and out must be 16-byte aligned");
     drain_prior_error();
-    hipError_t e = q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, out,
-                                      out_dtype == Q4_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    hipError_t e = q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, out, out_dtype,
+                                      static_cast<hipStream_t>(stream));
     st = check_launch(e, "dequant");
     return st == Q4_OK ? ok() : st;
 }

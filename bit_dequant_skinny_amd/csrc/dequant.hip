@@ -4,7 +4,9 @@
 // "[ROCm] Optimize kgemm_4bit_inference_naive for ROCm, use it for batch sizes
 // other than 1" (section "Fused path support for M > 1").
 //
-// HBM-bound: 0.5625 B read + 2 (bf16) or 4 (fp32) B written per weight.  One
+// HBM-bound: 0.5625 B read + 2 (bf16, fp16) or 4 (fp32) B written per weight.
+// The fp32 product is written as is, or rounded once to bf16 or fp16
+// (nearest even).  One
 // lane handles one 32-bit word of packed codes (8 weights) per step, so a wave
 // reads 256 contiguous bytes and writes 1 KiB (bf16) in one store; each lane
 // has four such words in flight.  Because K % bs == 0, blocking the flattened
@@ -20,7 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
-template <bool BF16>
+template <int OT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__restrict__ packed,
                                                            const float *__restrict__ absmax,
                                                            const float *__restrict__ codebook,
@@ -49,12 +51,26 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
 #pragma unroll
             for (int j = 0; j < 8; ++j) w[j] = cb_lookup(table, d[u] >> (4 * j)) * am[u];
             if (i < words) {
-                if constexpr (BF16) {
+                if constexpr (OT == kBf16) {
                     uint4 o;
                     o.x = f32_to_bf16_rne(w[0]) | (f32_to_bf16_rne(w[1]) << 16);
                     o.y = f32_to_bf16_rne(w[2]) | (f32_to_bf16_rne(w[3]) << 16);
                     o.z = f32_to_bf16_rne(w[4]) | (f32_to_bf16_rne(w[5]) << 16);
                     o.w = f32_to_bf16_rne(w[6]) | (f32_to_bf16_rne(w[7]) << 16);
+                    reinterpret_cast<uint4 *>(out)[i] = o;
+                } else if constexpr (OT == kF16) {
+                    // The fp32 product is pinned in a register first: the
+                    // compiler would otherwise fold multiply and narrowing into
+                    // one mixed-precision fma, a single rounding that differs
+                    // from rounding the fp32 product (and drops the sign of a
+                    // zero product).
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) __asm__ volatile("" : "+v"(w[j]));
+                    uint4 o;
+                    o.x = f32_to_f16_rne(w[0]) | (f32_to_f16_rne(w[1]) << 16);
+                    o.y = f32_to_f16_rne(w[2]) | (f32_to_f16_rne(w[3]) << 16);
+                    o.z = f32_to_f16_rne(w[4]) | (f32_to_f16_rne(w[5]) << 16);
+                    o.w = f32_to_f16_rne(w[6]) | (f32_to_f16_rne(w[7]) << 16);
                     reinterpret_cast<uint4 *>(out)[i] = o;
                 } else {
                     float4 *o = reinterpret_cast<float4 *>(out) + 2 * i;
@@ -69,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
 }  // namespace
 
 hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
-                          int N, int K, int bs_log2, void *out, bool out_bf16, hipStream_t s) {
+                          int N, int K, int bs_log2, void *out, int out_dt, hipStream_t s) {
     const uint64_t words = (uint64_t)N * (uint64_t)K / 8;
     const DeviceInfo info = device_info();
     const uint64_t per_block = (uint64_t)kThreads * kUnroll;
@@ -78,11 +94,14 @@ hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const flo
     if (blocks > cap) blocks = cap;
     if (blocks == 0) blocks = 1;
     const uint32_t *packed = reinterpret_cast<const uint32_t *>(Wpacked);
-    if (out_bf16)
-        dequant_kernel<true><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+    if (out_dt == kBf16)
+        dequant_kernel<kBf16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+            packed, absmax, codebook, words, bs_log2, out);
+    else if (out_dt == kF16)
+        dequant_kernel<kF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
             packed, absmax, codebook, words, bs_log2, out);
     else
-        dequant_kernel<false><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+        dequant_kernel<kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
             packed, absmax, codebook, words, bs_log2, out);
     return hipGetLastError();
 }

@@ -35,6 +35,43 @@ __device__ __forceinline__ float cb_lookup(int table, uint32_t code) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Element types of the C ABI (the Q4_DTYPE_* codes).
+enum : int { kBf16 = 0, kF32 = 1, kF16 = 2 };
+
+// IEEE binary16 <-> fp32.  Widening is exact; narrowing rounds to nearest
+// even (v_cvt_f16_f32 in the default rounding mode, fp16 denormals kept).
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// A pair of fp16 values as two pairs of bf16 values, hi and lo, with
+// hi + lo equal to each fp16 value exactly: hi is the nearest bf16 and the
+// remainder has at most 3 significant bits, well inside bf16's precision and
+// range.
+__device__ __forceinline__ uint2 f16x2_to_bf16_hilo(uint32_t d) {
+    const float f0 = f16_to_f32(d & 0xffffu), f1 = f16_to_f32(d >> 16);
+    const uint32_t h0 = f32_to_bf16_rne(f0), h1 = f32_to_bf16_rne(f1);
+    const uint32_t l0 = f32_to_bf16_rne(f0 - bf16_lo(h0)), l1 = f32_to_bf16_rne(f1 - bf16_lo(h1));
+    return make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
+}
+
+// Element i of a vector of type dt (bf16, fp16 or fp32), widened to fp32.
+__device__ __forceinline__ float load_elem(const void *p, size_t i, int dt) {
+    if (dt == kF32) return reinterpret_cast<const float *>(p)[i];
+    const uint32_t b = reinterpret_cast<const uint16_t *>(p)[i];
+    return dt == kF16 ? f16_to_f32(b) : bf16_lo(b);
+}
+
+// Rounds v to type dt (nearest even) and stores it as element i.
+__device__ __forceinline__ void store_elem(void *p, size_t i, float v, int dt) {
+    if (dt == kF32) reinterpret_cast<float *>(p)[i] = v;
+    else if (dt == kF16) reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_f16_rne(v);
+    else reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16_rne(v);
+}
+
 __device__ __forceinline__ floatx4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -1,6 +1,8 @@
 // Fused blockwise-4-bit dequantize + skinny GEMM on the vector ALUs:
-// C[M,N] = A[M,K] * dequant(W)^T.  Serves blocksize 32, whose blocks are
-// narrower than the 64-wide scale granule of the matrix-core kernel.
+// C[M,N] = A[M,K] * dequant(W)^T (+ bias).  Serves blocksize 32, whose blocks
+// are narrower than the 64-wide scale granule of the matrix-core kernel, fp32
+// activations (widened exactly, multiplied in fp32), and shapes beyond the
+// matrix-core kernel's 32-bit offsets.
 //
 // The fused path of the bitsandbytes pull request "[ROCm] Optimize
 // kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1"
@@ -25,11 +27,37 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int MT, int ROWS>
+// Eight consecutive activations of type AT (bf16, fp16 or fp32), widened to
+// fp32 exactly.
+template <int AT>
+__device__ __forceinline__ void load8(const void *A, size_t i, float (&a)[8]) {
+    if constexpr (AT == kF32) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(A) + i);
+        const float4 u = p[0], v = p[1];
+        a[0] = u.x; a[1] = u.y; a[2] = u.z; a[3] = u.w;
+        a[4] = v.x; a[5] = v.y; a[6] = v.z; a[7] = v.w;
+    } else {
+        const uint4 av = ld128(static_cast<const uint16_t *>(A) + i);
+        const uint32_t d[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (AT == kF16) {
+                a[2 * t] = f16_to_f32(d[t] & 0xffffu);
+                a[2 * t + 1] = f16_to_f32(d[t] >> 16);
+            } else {
+                a[2 * t] = bf16_lo(d[t]);
+                a[2 * t + 1] = bf16_hi(d[t]);
+            }
+        }
+    }
+}
+
+template <int AT, int MT, int ROWS>
 __global__ __launch_bounds__(kThreads) void fused_rows_kernel(
-    const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ absmax, const float *__restrict__ codebook, int M, int N, int K,
-    int bs_log2, uint16_t *__restrict__ C) {
+    const void *__restrict__ A, const uint8_t *__restrict__ Wp,
+    const float *__restrict__ absmax, const float *__restrict__ codebook,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, void *__restrict__ C,
+    int c_dt) {
     const int lane = threadIdx.x & 63;
     const int wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
     const int n0 = wave * ROWS;
@@ -65,27 +93,30 @@ __global__ __launch_bounds__(kThreads) void fused_rows_kernel(
         for (int r = 0; r < ROWS; ++r)
 #pragma unroll
             for (int m = 0; m < MT; ++m) part[r][m] = 0.f;
-#pragma unroll
+#pragma unroll 1
         for (int q = 0; q < 4; ++q) {
-            float a[MT][8];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                uint4 av = make_uint4(0, 0, 0, 0);
-                if (m < M && valid) av = ld128(A + (size_t)m * K + (size_t)cc * 32 + q * 8);
-                a[m][0] = bf16_lo(av.x); a[m][1] = bf16_hi(av.x);
-                a[m][2] = bf16_lo(av.y); a[m][3] = bf16_hi(av.y);
-                a[m][4] = bf16_lo(av.z); a[m][5] = bf16_hi(av.z);
-                a[m][6] = bf16_lo(av.w); a[m][7] = bf16_hi(av.w);
-            }
+            // Decode this dword of every row once, then stream the token rows
+            // past it one at a time (8 activations live, whatever MT is).
+            float v[ROWS][8];
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) {
                 const uint32_t d = (q == 0) ? w[r].x : (q == 1) ? w[r].y : (q == 2) ? w[r].z : w[r].w;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float v = cb_lookup(table, d >> (4 * j));
+                for (int j = 0; j < 8; ++j) v[r][j] = cb_lookup(table, d >> (4 * j));
+            }
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) part[r][m] = fmaf(a[m][j], v, part[r][m]);
+            for (int m = 0; m < MT; ++m) {
+                float a[8];
+                if (m < M && valid) {
+                    load8<AT>(A, (size_t)m * K + (size_t)cc * 32 + q * 8, a);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a[e] = 0.f;
                 }
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) part[r][m] = fmaf(a[j], v[r][j], part[r][m]);
             }
         }
 #pragma unroll
@@ -104,32 +135,47 @@ __global__ __launch_bounds__(kThreads) void fused_rows_kernel(
         for (int r = 0; r < ROWS; ++r)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
-                if (n0 + r < N && m < M)
-                    C[(size_t)m * N + n0 + r] = (uint16_t)f32_to_bf16_rne(acc[r][m]);
+                if (n0 + r < N && m < M) {
+                    float v = acc[r][m];
+                    if (bias) v += load_elem(bias, n0 + r, c_dt);  // before the single rounding
+                    store_elem(C, (size_t)m * N + n0 + r, v, c_dt);
+                }
     }
 }
 
-template <int MT, int ROWS>
-hipError_t launch_rows(const uint16_t *A, const uint8_t *Wp, const float *absmax,
-                       const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
-                       hipStream_t s) {
+template <int AT, int MT, int ROWS>
+hipError_t launch_rows(const void *A, const uint8_t *Wp, const float *absmax,
+                       const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
+                       void *C, int c_dt, hipStream_t s) {
     const int waves = (N + ROWS - 1) / ROWS;
     const int blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
-    fused_rows_kernel<MT, ROWS><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, Wp, absmax, codebook,
-                                                                         M, N, K, bs_log2, C);
+    fused_rows_kernel<AT, MT, ROWS><<<dim3(blocks), dim3(kThreads), 0, s>>>(
+        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt);
     return hipGetLastError();
+}
+
+template <int AT>
+hipError_t launch_at(const void *A, const uint8_t *Wp, const float *absmax, const float *codebook,
+                     const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
+                     hipStream_t s) {
+    if (M <= 1) return launch_rows<AT, 1, 8>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (M <= 2) return launch_rows<AT, 2, 8>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (M <= 4) return launch_rows<AT, 4, 4>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (M <= 8) return launch_rows<AT, 8, 2>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    return launch_rows<AT, 16, 1>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
 }
 
 }  // namespace
 
-hipError_t launch_q4_fused_simt(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                                const float *codebook, int M, int N, int K, int bs_log2,
-                                uint16_t *C, hipStream_t s) {
-    if (M <= 1) return launch_rows<1, 8>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    if (M <= 2) return launch_rows<2, 8>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    if (M <= 4) return launch_rows<4, 4>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    if (M <= 8) return launch_rows<8, 2>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    return launch_rows<16, 2>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
+                                const float *absmax, const float *codebook, const void *bias,
+                                int M, int N, int K, int bs_log2, void *C, int c_dt,
+                                hipStream_t s) {
+    if (a_dt == kF32)
+        return launch_at<kF32>(A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (a_dt == kF16)
+        return launch_at<kF16>(A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    return launch_at<kBf16>(A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
 }
 
 }  // namespace q4

@@ -88,16 +88,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 
 constexpr int KW = 8;  // waves per workgroup
 
-// SR: accumulator rows kept per lane (min(M, 4)).  TB: tiles per chunk.  RS:
+// AT: activation type, bf16 (one MFMA per operand pair) or fp16 (split
+// exactly into bf16 hi + lo, two MFMAs).  SR: accumulator rows kept per lane
+// (min(M, 4)).  TB: tiles per chunk.  RS:
 // segment slots the weight ring runs ahead, so every wave keeps TB*RS weight
 // loads in flight.  UF: slots per loop iteration, a multiple of RS with UF*TB
 // even, which makes the ring entry and the decode double-buffer index of
 // every unit compile-time constants.
-template <int SR, int TB, int RS, int UF>
+template <int AT, int SR, int TB, int RS, int UF>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
-    const float *__restrict__ absmax, const float *__restrict__ codebook, int M, int N, int K,
-    int bs_log2, int groups, uint16_t *__restrict__ C) {
+    const float *__restrict__ absmax, const float *__restrict__ codebook,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups,
+    void *__restrict__ C, int c_dt) {
+    static_assert(AT == kBf16 || AT == kF16, "bf16 or fp16 activations");
+    constexpr int NA = AT == kF16 ? 2 : 1;  // bf16 terms per activation
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
     static_assert(64 * KW >= 256, "one table entry per thread");
     __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
@@ -290,19 +295,32 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     auto slot = [&](auto us_c) {
         constexpr int us = decltype(us_c)::value;
         constexpr int r_cur = us % RS, r_next = (us + 1) % RS;
-        // Activation operand, each pair of activations duplicated.  Built
-        // once per slot and pinned in registers: an MFMA whose operand a VALU
-        // instruction has just written stalls for the hazard, so the compiler
-        // must not rebuild these next to every MFMA.
-        uint4 adup[8];
+        // Activation operand, each pair of activations duplicated (fp16
+        // activations as two bf16 operands, hi and lo).  Built once per slot
+        // and pinned in registers: an MFMA whose operand a VALU instruction has
+        // just written stalls for the hazard, so the compiler must not rebuild
+        // these next to every MFMA.
+        uint4 adup[NA][8];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            adup[2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
-            adup[2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
+            if constexpr (AT == kBf16) {
+                adup[0][2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
+                adup[0][2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
+            } else {
+                const uint2 x = f16x2_to_bf16_hilo(anext[t].x), y = f16x2_to_bf16_hilo(anext[t].y);
+                const uint2 z = f16x2_to_bf16_hilo(anext[t].z), w = f16x2_to_bf16_hilo(anext[t].w);
+                adup[0][2 * t] = make_uint4(x.x, x.x, y.x, y.x);
+                adup[0][2 * t + 1] = make_uint4(z.x, z.x, w.x, w.x);
+                adup[NA - 1][2 * t] = make_uint4(x.y, x.y, y.y, y.y);
+                adup[NA - 1][2 * t + 1] = make_uint4(z.y, z.y, w.y, w.y);
+            }
         }
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            __asm__ volatile("" : "+v"(adup[s].x), "+v"(adup[s].y), "+v"(adup[s].z), "+v"(adup[s].w));
+        for (int h = 0; h < NA; ++h)
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                __asm__ volatile("" : "+v"(adup[h][s].x), "+v"(adup[h][s].y), "+v"(adup[h][s].z),
+                                 "+v"(adup[h][s].w));
         load_a(pq + 1 == spw ? 0 : pq + 1);  // the activations of the next slot
         if constexpr (us % RS == 0) snext = load_scales();  // and the next period's scales
         const int s_blk = (16 * (us % RS) + 2 * wave) >> sh;
@@ -319,8 +337,11 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             for (int s = 0; s < 4; ++s) {
                 const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
                 const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
-                D0 = mfma_bf16_16x16x32(as_bf16x8(adup[s]), as_bf16x8(b0), D0);
-                D1 = mfma_bf16_16x16x32(as_bf16x8(adup[4 + s]), as_bf16x8(b1), D1);
+#pragma unroll
+                for (int h = 0; h < NA; ++h) {
+                    D0 = mfma_bf16_16x16x32(as_bf16x8(adup[h][s]), as_bf16x8(b0), D0);
+                    D1 = mfma_bf16_16x16x32(as_bf16x8(adup[h][4 + s]), as_bf16x8(b1), D1);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (tr + 1 < TB) {
@@ -388,17 +409,20 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 for (int w2 = 1; w2 < KW; ++w2) v += red[w2][p][lane];
                 const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
                 const int tok = 4 * g + r;
-                if (n < N && tok < M) C[(size_t)tok * N + n] = (uint16_t)f32_to_bf16_rne(v);
+                if (n < N && tok < M) {
+                    if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
+                    store_elem(C, (size_t)tok * N + n, v, c_dt);
+                }
             }
         }
         if (++pc == my_chunks) break;
     }
 }
 
-template <int SR, int TB>
+template <int AT, int SR, int TB>
 hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
-                     const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
-                     int groups, int G, hipStream_t s) {
+                     const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
+                     void *C, int c_dt, int groups, int G, hipStream_t s) {
     // Ring depth TB*RS of about 8 units (8 KiB of weights in flight per wave).
     constexpr int RS = TB == 1 ? 8 : TB == 2 ? 4 : TB <= 4 ? 2 : 1;
     constexpr int UF = (RS * TB) % 2 == 0 ? RS : 2 * RS;
@@ -406,15 +430,15 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // ring entry and decode buffer of a chunk's first unit are fixed at compile
     // time); TB < 8 gives that, since then groups <= CUs.
     if ((RS > 1 || TB % 2) && groups > G) return hipErrorInvalidValue;
-    fused_mfma_kernel<SR, TB, RS, UF><<<dim3(G), dim3(64 * KW), 0, s>>>(
-        A, Wp, absmax, codebook, M, N, K, bs_log2, groups, C);
+    fused_mfma_kernel<AT, SR, TB, RS, UF><<<dim3(G), dim3(64 * KW), 0, s>>>(
+        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt);
     return hipGetLastError();
 }
 
-template <int SR>
+template <int AT, int SR>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
-                     const float *codebook, int M, int N, int K, int bs_log2, uint16_t *C,
-                     hipStream_t s) {
+                     const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
+                     void *C, int c_dt, hipStream_t s) {
     // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS).
     // TB = the tiles each CU must cover, up to 8, so that every chunk but the
     // last holds TB live tiles; a workgroup loops over ceil(groups / CUs)
@@ -426,14 +450,14 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     const int groups = (tiles + tb - 1) / tb;
     const int G = groups < cus ? groups : cus;
     switch (tb) {
-    case 1: return launch_tb<SR, 1>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    case 2: return launch_tb<SR, 2>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    case 3: return launch_tb<SR, 3>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    case 4: return launch_tb<SR, 4>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    case 5: return launch_tb<SR, 5>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    case 6: return launch_tb<SR, 6>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    case 7: return launch_tb<SR, 7>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
-    default: return launch_tb<SR, 8>(A, Wp, absmax, codebook, M, N, K, bs_log2, C, groups, G, s);
+    case 1: return launch_tb<AT, SR, 1>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 2: return launch_tb<AT, SR, 2>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 3: return launch_tb<AT, SR, 3>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 4: return launch_tb<AT, SR, 4>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 5: return launch_tb<AT, SR, 5>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 6: return launch_tb<AT, SR, 6>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 7: return launch_tb<AT, SR, 7>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    default: return launch_tb<AT, SR, 8>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
     }
 }
 
@@ -450,20 +474,29 @@ bool q4_fused_mfma_fits(int M, int N, int K) {
            16ull * (uint64_t)K * 2 < (1ull << 32);
 }
 
-hipError_t launch_q4_fused_mfma(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                                const float *codebook, int M, int N, int K, int bs_log2,
-                                uint16_t *C, hipStream_t s) {
-    if (M <= 1) return launch_sr<1>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    if (M <= 2) return launch_sr<2>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    return launch_sr<4>(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
+                                const float *absmax, const float *codebook, const void *bias,
+                                int M, int N, int K, int bs_log2, void *C, int c_dt,
+                                hipStream_t s) {
+    const uint16_t *A16 = static_cast<const uint16_t *>(A);
+    if (a_dt == kF16) {
+        if (M <= 1) return launch_sr<kF16, 1>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+        if (M <= 2) return launch_sr<kF16, 2>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+        return launch_sr<kF16, 4>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    }
+    if (M <= 1) return launch_sr<kBf16, 1>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (M <= 2) return launch_sr<kBf16, 2>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    return launch_sr<kBf16, 4>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
 }
 
-hipError_t launch_q4_fused(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                           const float *codebook, int M, int N, int K, int bs_log2,
-                           uint16_t *C, hipStream_t s) {
-    if (bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K))
-        return launch_q4_fused_mfma(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
-    return launch_q4_fused_simt(A, Wpacked, absmax, codebook, M, N, K, bs_log2, C, s);
+hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
+                           const float *codebook, const void *bias, int M, int N, int K,
+                           int bs_log2, void *C, int c_dt, hipStream_t s) {
+    if (a_dt != kF32 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K))
+        return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
+                                    C, c_dt, s);
+    return launch_q4_fused_simt(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C,
+                                c_dt, s);
 }
 
 }  // namespace q4

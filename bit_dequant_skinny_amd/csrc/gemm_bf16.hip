@@ -21,6 +21,11 @@
 //
 // When N is small the waves of a workgroup split K and combine their fp32
 // tiles through LDS in a fixed order (deterministic, no atomics).
+//
+// fp16 activations (split path of the 4-bit GEMM) are split exactly into
+// bf16 hi + lo and take two MFMAs per step.  The bias (optional) has the
+// output's type; the output is bf16, fp16 or fp32, rounded once from the fp32
+// sum plus bias.
 #include "device.h"
 #include "launch.h"
 
@@ -31,11 +36,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-template <int MT>
+template <int AT, int MT>
 __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
-    const uint16_t *__restrict__ bias, int M, int N, int K, int ksplit,
-    uint16_t *__restrict__ C) {
+    const void *__restrict__ bias, int M, int N, int K, int ksplit,
+    void *__restrict__ C, int c_dt) {
     __shared__ floatx4 red[kWaves][MT][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -66,7 +71,14 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(
         for (int t = 0; t < MT; ++t) {
             const int tok = t * 16 + j;
             const uint4 av = (kin && tok < M) ? ld128(A + (size_t)tok * K + k) : zero;
-            acc[t] = mfma_bf16_16x16x32(as_bf16x8(av), as_bf16x8(wv), acc[t]);
+            if constexpr (AT == kF16) {
+                const uint2 x = f16x2_to_bf16_hilo(av.x), y = f16x2_to_bf16_hilo(av.y);
+                const uint2 z = f16x2_to_bf16_hilo(av.z), w = f16x2_to_bf16_hilo(av.w);
+                acc[t] = mfma_bf16_16x16x32(as_bf16x8(make_uint4(x.x, y.x, z.x, w.x)), as_bf16x8(wv), acc[t]);
+                acc[t] = mfma_bf16_16x16x32(as_bf16x8(make_uint4(x.y, y.y, z.y, w.y)), as_bf16x8(wv), acc[t]);
+            } else {
+                acc[t] = mfma_bf16_16x16x32(as_bf16x8(av), as_bf16x8(wv), acc[t]);
+            }
         }
     }
 
@@ -84,20 +96,20 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(
     }
 
     if (n0 + j >= N) return;
-    const float b = bias ? bf16_lo(bias[n0 + j]) : 0.f;
+    const float b = bias ? load_elem(bias, n0 + j, c_dt) : 0.f;
     // D layout: lane holds feature j and tokens 4*g + r of each 16-token tile.
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = t * 16 + g * 4 + r;
-            if (tok < M) C[(size_t)tok * N + n0 + j] = (uint16_t)f32_to_bf16_rne(acc[t][r] + b);
+            if (tok < M) store_elem(C, (size_t)tok * N + n0 + j, acc[t][r] + b, c_dt);
         }
 }
 
-template <int MT>
-hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const uint16_t *bias, int M, int N,
-                     int K, uint16_t *C, hipStream_t s) {
+template <int AT, int MT>
+hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const void *bias, int M, int N,
+                     int K, void *C, int c_dt, hipStream_t s) {
     const int tiles = (N + 15) / 16;
     const DeviceInfo info = device_info();
     // Split K across the waves of a workgroup when there are too few feature
@@ -107,27 +119,37 @@ hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const uint16_t *bias,
     if (tiles < info.num_cus * 2) ksplit = 4;
     const int tiles_per_block = kWaves / ksplit;
     const int blocks = (tiles + tiles_per_block - 1) / tiles_per_block;
-    bf16_gemm_kernel<MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K, ksplit, C);
+    bf16_gemm_kernel<AT, MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K, ksplit,
+                                                                     C, c_dt);
     return hipGetLastError();
+}
+
+template <int AT>
+hipError_t launch_slabs(const uint16_t *A, const uint16_t *W, const void *bias, int M, int N,
+                        int K, void *C, int c_dt, hipStream_t s) {
+    // Token tiles of 16; above 64 tokens the weight is streamed once per
+    // 64-token slab.
+    const size_t c_size = c_dt == kF32 ? 4 : 2;
+    for (int m0 = 0; m0 < M; m0 += 64) {
+        const int mm = (M - m0) < 64 ? (M - m0) : 64;
+        const uint16_t *Am = A + (size_t)m0 * K;
+        void *Cm = static_cast<char *>(C) + (size_t)m0 * N * c_size;
+        hipError_t e;
+        if (mm <= 16) e = launch_mt<AT, 1>(Am, W, bias, mm, N, K, Cm, c_dt, s);
+        else if (mm <= 32) e = launch_mt<AT, 2>(Am, W, bias, mm, N, K, Cm, c_dt, s);
+        else e = launch_mt<AT, 4>(Am, W, bias, mm, N, K, Cm, c_dt, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bf16_gemm(const uint16_t *A, const uint16_t *W, const uint16_t *bias, int M,
-                            int N, int K, uint16_t *C, hipStream_t s) {
-    // Token tiles of 16; above 64 tokens the weight is streamed once per
-    // 64-token slab.
-    for (int m0 = 0; m0 < M; m0 += 64) {
-        const int mm = (M - m0) < 64 ? (M - m0) : 64;
-        const uint16_t *Am = A + (size_t)m0 * K;
-        uint16_t *Cm = C + (size_t)m0 * N;
-        hipError_t e;
-        if (mm <= 16) e = launch_mt<1>(Am, W, bias, mm, N, K, Cm, s);
-        else if (mm <= 32) e = launch_mt<2>(Am, W, bias, mm, N, K, Cm, s);
-        else e = launch_mt<4>(Am, W, bias, mm, N, K, Cm, s);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,
+                            int N, int K, void *C, int c_dt, hipStream_t s) {
+    const uint16_t *A16 = static_cast<const uint16_t *>(A);
+    if (a_dt == kF16) return launch_slabs<kF16>(A16, W, bias, M, N, K, C, c_dt, s);
+    return launch_slabs<kBf16>(A16, W, bias, M, N, K, C, c_dt, s);
 }
 
 }  // namespace q4

@@ -15,23 +15,29 @@ struct DeviceInfo {
 };
 DeviceInfo device_info();  // the current device, cached per device
 
+// Element types are the Q4_DTYPE_* codes (kBf16, kF32, kF16 in device.h).
 hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
-                          int N, int K, int bs_log2, void *out, bool out_bf16, hipStream_t s);
+                          int N, int K, int bs_log2, void *out, int out_dt, hipStream_t s);
 
-// Dispatches to the matrix-core kernel (blocksize >= 64) or the vector-ALU
-// kernel (blocksize 32).
-hipError_t launch_q4_fused(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                           const float *codebook, int M, int N, int K, int bs_log2,
-                           uint16_t *C, hipStream_t s);
-hipError_t launch_q4_fused_mfma(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                                const float *codebook, int M, int N, int K, int bs_log2,
-                                uint16_t *C, hipStream_t s);
-hipError_t launch_q4_fused_simt(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
-                                const float *codebook, int M, int N, int K, int bs_log2,
-                                uint16_t *C, hipStream_t s);
+// Fused 4-bit GEMM, C = A * dequant(W)^T (+ bias), A of type a_dt, bias and C
+// of type c_dt.  Dispatches to the matrix-core kernel (bf16 or fp16
+// activations, blocksize >= 64) or the vector-ALU kernel (blocksize 32, fp32
+// activations, offsets beyond 32 bits).
+hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
+                           const float *codebook, const void *bias, int M, int N, int K,
+                           int bs_log2, void *C, int c_dt, hipStream_t s);
+hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
+                                const float *absmax, const float *codebook, const void *bias,
+                                int M, int N, int K, int bs_log2, void *C, int c_dt,
+                                hipStream_t s);
+hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
+                                const float *absmax, const float *codebook, const void *bias,
+                                int M, int N, int K, int bs_log2, void *C, int c_dt,
+                                hipStream_t s);
 
-hipError_t launch_bf16_gemm(const uint16_t *A, const uint16_t *W, const uint16_t *bias,
-                            int M, int N, int K, uint16_t *C, hipStream_t s);
+// bf16-weight GEMM on the matrix cores, C = A * W^T (+ bias); A bf16 or fp16.
+hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,
+                            int N, int K, void *C, int c_dt, hipStream_t s);
 
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
 

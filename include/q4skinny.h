@@ -44,7 +44,8 @@ typedef enum q4_status {
     Q4_ERR_HIP = 3               /* the HIP runtime reported an error (see q4_last_error) */
 } q4_status;
 
-enum { Q4_DTYPE_BF16 = 0, Q4_DTYPE_FP32 = 1 };
+/* Element types: bfloat16, IEEE binary32, IEEE binary16. */
+enum { Q4_DTYPE_BF16 = 0, Q4_DTYPE_FP32 = 1, Q4_DTYPE_FP16 = 2 };
 enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
 
 /* Largest M the fused 4-bit kernels handle; larger M always takes the split path. */
@@ -94,6 +95,38 @@ q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float
                               void *C, void *stream, int path);
 
 /*
+ * q4_gemm_skinny_ex: q4_gemm_skinny with a bias and other element types.
+ *
+ * Defined by the maintainer's comment on the bitsandbytes pull request
+ * "[ROCm] Optimize kgemm_4bit_inference_naive for ROCm, use it for batch
+ * sizes other than 1", which lists a fused bias epilogue (C += bias) and
+ * fp32 / fp16 / bf16 variants that all accumulate in fp32.
+ *
+ *  A        [M, K] of a_dtype (Q4_DTYPE_BF16, Q4_DTYPE_FP16 or Q4_DTYPE_FP32).
+ *  Wpacked, absmax, codebook: as in q4_gemm_skinny.
+ *  bias     [N] of c_dtype, or NULL.
+ *  C        [M, N] of c_dtype (Q4_DTYPE_BF16, Q4_DTYPE_FP16 or Q4_DTYPE_FP32).
+ *  path     Q4_PATH_AUTO, Q4_PATH_FUSED or Q4_PATH_SPLIT, as in
+ *           q4_gemm_skinny_path.
+ *
+ *  C[m, n] = round_c(sum_k a[m, k] * w(n, k) + bias[n]): the products are
+ *  exact, the sum is fp32, the bias is added to the fp32 sum and the result
+ *  is rounded once to c_dtype (nearest even).  fp16 and fp32 activations are
+ *  exact in the kernels (fp16 as an exact bf16 hi + lo pair on the matrix
+ *  cores, fp32 on the vector ALUs).  The split path rounds the weights to
+ *  bf16 first, as q4_gemm_skinny does.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: as q4_gemm_skinny, plus an unknown dtype or
+ *    path, C or bias not aligned to their element size.
+ *  Q4_ERR_UNSUPPORTED: as q4_gemm_skinny; fp32 activations on the split
+ *    path (M > Q4_FUSED_MAX_M, or above the crossover, or forced).
+ */
+q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
+                            const float *absmax, const float *codebook, const void *bias, int M,
+                            int N, int K, int blocksize, void *C, int c_dtype, void *stream,
+                            int path);
+
+/*
  * bf16_gemm_skinny: C = A * W^T (+ bias) for unquantized bf16 weights.
  *
  * Defined by the report on vLLM pull request 40687 "Support N=5 in wvSplitK
@@ -121,7 +154,8 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
  * "[ROCm] Optimize kgemm_4bit_inference_naive ..." (section "Fused path
  * support for M > 1": "split dequantize + GEMM").  Same packed layout as
  * q4_gemm_skinny.  out_dtype Q4_DTYPE_FP32 writes the fp32 product,
- * Q4_DTYPE_BF16 writes it rounded to bf16 (nearest-even; NaN stays NaN).
+ * Q4_DTYPE_BF16 and Q4_DTYPE_FP16 write it rounded once to bf16 or fp16
+ * (nearest-even; NaN stays NaN; fp16 overflows to infinity).
  * Bit-exact: one fp32 multiply per element, denormals kept.
  *
  *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, N/K < 0, K == 0, bad blocksize

@@ -54,10 +54,35 @@ def as_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def assert_within_tolerance(C_gpu_bits, C_ref, S, what=""):
-    got = as_f64(C_gpu_bits)
+# Twice the unit roundoff of each output type (2^-7 for bf16 as above); an
+# fp16 output also carries an absolute half-quantum below 2^-14.
+REL_OUT = {"bf16": 2.0 ** -7, "fp16": 2.0 ** -10, "fp32": 2.0 ** -23}
+ABS_OUT = {"bf16": 0.0, "fp16": 2.0 ** -25, "fp32": 0.0}
+
+
+def host_f64(x) -> np.ndarray:
+    """Device tensor of bf16 / fp16 / fp32 -> fp64 values on the host."""
+    t = torch()
+    if x.dtype == t.bfloat16:
+        return as_f64(bf16_host(x))
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def to_dev_dtype(arr: np.ndarray, dtype: str):
+    """Seeded input in dtype ("bf16"/"fp16" bit patterns or fp32 values) -> device."""
+    t = torch()
+    if dtype == "fp32":
+        return to_dev(arr, "f32")
+    x = t.from_numpy(np.ascontiguousarray(arr, np.uint16).view(np.int16))
+    return x.view(t.bfloat16 if dtype == "bf16" else t.float16).to(dev())
+
+
+def assert_within_tolerance(C_gpu_bits, C_ref, S, what="", out="bf16", values=None):
+    """Elementwise |C_gpu - C_ref| <= 2 u_out |C_ref| + 1e-3 S (+ the fp16
+    subnormal half-quantum).  C_gpu is bf16 bit patterns, or fp64 values."""
+    got = as_f64(C_gpu_bits) if values is None else values
     assert got.shape == C_ref.shape, (got.shape, C_ref.shape)
-    bound = REL * np.abs(C_ref) + ABS_S * S
+    bound = REL_OUT[out] * np.abs(C_ref) + ABS_S * S + ABS_OUT[out]
     err = np.abs(got - C_ref)
     bad = ~(err <= bound)
     if bad.any():
