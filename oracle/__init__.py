@@ -20,6 +20,7 @@ Function map (steps as numbered in the C file):
   f32_to_f16      O9  fp32 -> binary16, nearest-even
   dequant_f16     O9  O3 rounded to binary16
   q4_gemm_ex      O10 O5 with bf16 / fp16 / fp32 activations and a bias
+  quantize        O11 blockwise absmax + nearest-entry codes (inverse of O3)
 
 Element types are named "bf16", "fp16", "fp32" (uint16 bit patterns for the
 two 16-bit types, float32 arrays for fp32).
@@ -92,6 +93,7 @@ class Oracle:
         lib.oracle_dequant_f16.argtypes = [P, P, P, I, I, I, P]
         lib.oracle_q4_gemm_ex.argtypes = [P, ctypes.c_int, P, P, P, P, ctypes.c_int, I, I, I, I,
                                           P, I, P, P]
+        lib.oracle_quantize.argtypes = [P, ctypes.c_int, P, I, I, I, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -213,6 +215,15 @@ class Oracle:
         self.lib.oracle_q4_gemm_ex(_ptr(Aa), acode, _ptr(Wp), _ptr(am), _ptr(cb), _ptr(b), bcode,
                                    M, N, K, bs, _ptr(c), nc, _ptr(C), _ptr(S))
         return C, S
+
+    def quantize(self, W, w_dtype, codebook, N, K, bs):
+        """(codes uint8 [N, K], absmax float32 [N, K/bs]) of W in w_dtype."""
+        code, npt = self.DTYPES[w_dtype]
+        Wa, cb = _c(W, npt), _c(codebook, np.float32)
+        codes = np.empty((N, K), dtype=np.uint8)
+        absmax = np.empty((N, K // bs), dtype=np.float32)
+        self.lib.oracle_quantize(_ptr(Wa), code, _ptr(cb), N, K, bs, _ptr(codes), _ptr(absmax))
+        return codes, absmax
 
     def gemm_f32w(self, A_bf16, W_f32, M, N, K):
         A, W = _c(A_bf16, np.uint16), _c(W_f32, np.float32)

@@ -353,6 +353,44 @@ void oracle_q4_gemm_ex(const void *A, int a_dtype, const uint8_t *Wpacked, const
     }
 }
 
+/* ---- O11: blockwise 4-bit quantization (the inverse of O3) ---------------- */
+/* For a strictly increasing codebook c[0] < ... < c[15] and each block of bs
+ * consecutive k of a row: absmax = max |w| over the block (exact), and each
+ * weight takes the code of the entry nearest to the exact ratio w / absmax,
+ * a tie between two entries going to the lower one.  Entries i and i+1 are
+ * separated by their midpoint m_i = (c[i] + c[i+1]) / 2 (exact in fp64), so
+ * the nearest entry is the number of midpoints strictly below the ratio; with
+ * absmax > 0, m_i < w / absmax is the same as m_i * absmax < w, and that
+ * product of two 24-bit significands is exact in fp64, so every comparison is
+ * exact.  A block of zeros (absmax = 0) takes the ratio 0.  Weights are
+ * bf16, fp16 or fp32 (element types as in O10), widened exactly. */
+void oracle_quantize(const void *W, int w_dtype, const float *codebook, int64_t N, int64_t K,
+                     int64_t bs, uint8_t *codes, float *absmax)
+{
+    double mid[15];
+    for (int i = 0; i < 15; i++)
+        mid[i] = ((double)codebook[i] + (double)codebook[i + 1]) / 2.0;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t b = 0; b < K / bs; b++) {
+            double a = 0.0;
+            for (int64_t k = b * bs; k < (b + 1) * bs; k++) {
+                double w = fabs(elem(W, n * K + k, w_dtype));
+                if (w > a)
+                    a = w;
+            }
+            absmax[n * (K / bs) + b] = (float)a; /* a is one of the inputs: exact */
+            for (int64_t k = b * bs; k < (b + 1) * bs; k++) {
+                double w = a > 0.0 ? elem(W, n * K + k, w_dtype) : 0.0;
+                double scale = a > 0.0 ? a : 1.0;
+                int code = 0;
+                for (int i = 0; i < 15; i++)
+                    if (mid[i] * scale < w)
+                        code++;
+                codes[n * K + k] = (uint8_t)code;
+            }
+        }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -444,4 +444,91 @@ def pin_q4_gemm_ex_bias_alone(orc):
             assert np.all(S[:, n] == abs(_act_val(b[n], dt)))
 
 
+# -------------------------------------------------------------------------- O11
+def _int4_codebook():
+    # (i - 8) / 8: every midpoint (2i - 15) / 16 is an fp32 number, so exact
+    # ties can be written down
+    return np.array([(i - 8) / 8.0 for i in range(16)], dtype=np.float32)
+
+
+def _exact_quantize(W_vals, cb, bs):
+    """Exact rationals: block absmax, then the nearest entry to w / absmax with
+    ties to the lower index (brute force over all 16 entries)."""
+    N, K = W_vals.shape
+    codes = np.zeros((N, K), dtype=np.uint8)
+    absmax = np.zeros((N, K // bs), dtype=np.float64)
+    cbf = [_frac(c) for c in cb]
+    for n in range(N):
+        for b in range(K // bs):
+            blk = [_frac(W_vals[n, k]) for k in range(b * bs, (b + 1) * bs)]
+            a = max(abs(v) for v in blk)
+            absmax[n, b] = float(a)
+            for i, v in enumerate(blk):
+                x = v / a if a != 0 else Fraction(0)
+                d = [abs(x - c) for c in cbf]
+                codes[n, b * bs + i] = d.index(min(d))
+    return codes, absmax
+
+
+def pin_quantize_bruteforce(orc):
+    g = synth.rng(71)
+    for N, K, bs, dt, cb in [(3, 128, 64, "fp32", synth.random_codebook(3)),
+                             (2, 128, 32, "bf16", synth.nf4_style_codebook()),
+                             (2, 256, 128, "fp16", synth.random_codebook(4)),
+                             (1, 256, 256, "fp32", _int4_codebook())]:
+        W = synth.activations(N, K, int(g.integers(1 << 30)), dt)
+        vals = np.array([[_act_val(W[n, k], dt) for k in range(K)] for n in range(N)])
+        codes, absmax = orc.quantize(W, dt, cb, N, K, bs)
+        ce, ae = _exact_quantize(vals, cb, bs)
+        assert np.array_equal(absmax.astype(np.float64), ae), dt
+        assert np.array_equal(codes, ce), dt
+
+
+def pin_quantize_exact_ties(orc):
+    cb = _int4_codebook()
+    K, bs = 64, 64
+    mids = [(float(cb[i]) + float(cb[i + 1])) / 2 for i in range(15)]
+    w = [1.0]  # the block's absmax is 1, so the ratio is the weight itself
+    expect = [15]
+    for i, m in enumerate(mids):
+        m32 = np.float32(m)
+        assert float(m32) == m
+        w += [m, float(np.nextafter(m32, np.float32(2))), float(np.nextafter(m32, np.float32(-2)))]
+        expect += [i, i + 1, i]
+    w += [0.0] * (K - len(w))
+    expect += [8] * (K - len(expect))
+    W = np.array([w], dtype=np.float32)
+    codes, absmax = orc.quantize(W, "fp32", cb, 1, K, bs)
+    assert absmax[0, 0] == 1.0
+    assert list(codes[0]) == expect
+
+
+def pin_quantize_roundtrip_and_zero_block(orc):
+    g = synth.rng(72)
+    cb = synth.random_codebook(6)
+    N, K, bs = 4, 256, 64
+    codes = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    one = int(np.nonzero(cb == 1.0)[0][0])
+    codes[:, ::bs] = one  # every block holds the entry 1, so absmax is the block scale
+    am = g.uniform(0.01, 0.1, size=(N, K // bs)).astype(np.float32)
+    am[1, 2] = 0.0  # a block of zeros
+    W = orc.dequant_f32(synth.pack_nibbles(codes), am, cb, N, K, bs)
+    c2, a2 = orc.quantize(W, "fp32", cb, N, K, bs)
+    assert np.array_equal(a2, am)
+    zero = int(np.nonzero(cb == 0.0)[0][0])
+    mask = np.ones_like(codes, dtype=bool)
+    mask[1, 2 * bs:3 * bs] = False
+    assert np.array_equal(c2[mask], codes[mask])
+    assert np.all(c2[1, 2 * bs:3 * bs] == zero)
+
+
+def pin_quantize_matches_numpy_searchsorted(orc):
+    # synth's quantizer: numpy searchsorted on fp64 midpoints of w / absmax in fp64
+    W = synth.weights_f32(64, 512, 17)
+    for bs, cb in [(64, synth.nf4_style_codebook()), (32, synth.random_codebook(12))]:
+        c1, a1 = orc.quantize(W, "fp32", cb, 64, 512, bs)
+        c2, a2 = synth.quantize_blockwise(W, cb, bs)
+        assert np.array_equal(a1, a2) and np.array_equal(c1, c2)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

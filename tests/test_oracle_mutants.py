@@ -50,6 +50,12 @@ MUTANTS = {
     "ex_bias_dropped": ("double b = elem(bias, n, bias_dtype);\n                sum += b;",
                         "double b = elem(bias, n, bias_dtype);\n                sum += 0.0 * b;"),
     "ex_a_transposed": ("double a = elem(A, m * K + k, a_dtype);", "double a = elem(A, k * M + m, a_dtype);"),
+    "quantize_ties_up": ("if (mid[i] * scale < w)", "if (mid[i] * scale <= w)"),
+    "quantize_signed_max": ("double w = fabs(elem(W, n * K + k, w_dtype));", "double w = elem(W, n * K + k, w_dtype);"),
+    "quantize_mid_is_entry": ("mid[i] = ((double)codebook[i] + (double)codebook[i + 1]) / 2.0;",
+                              "mid[i] = (double)codebook[i];"),
+    "quantize_block_shift": ("for (int64_t k = b * bs; k < (b + 1) * bs; k++) {\n                double w = fabs",
+                             "for (int64_t k = b * bs + 1; k < (b + 1) * bs && k < K; k++) {\n                double w = fabs"),
     "w16_not_rounded": ("double p = a * bf16_to_double(w16);",
                         "double p = a * (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k) + 0.0 * w16;"),
 }
