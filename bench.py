@@ -328,6 +328,20 @@ def other_configs(d):
                 "us": round(u, 2), "GB/s": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
     res["q4 K=8192 N=28672 dtypes+bias"] = rows
     del sets
+    log("blockwise quantizer, 28672 x 8192")
+    rows = {}
+    cbq = q4.q4_codebook_preset("nf4_style")
+    for dtn, tdt in (("fp32", t.float32), ("bf16", t.bfloat16)):
+        Wq = t.from_numpy(synth.weights_f32(N, K, 85)).to(d.dev).to(tdt)
+        outs = (t.empty((N, K // 2), dtype=t.uint8, device=d.dev),
+                t.empty((N, K // BS), dtype=t.float32, device=d.dev))
+        u = d.time_launches([lambda i: q4.q4_quantize(Wq, cbq, BS, out=outs)], reps=20)[0]
+        nbytes = N * K * Wq.element_size() + N * K // 2 + 4 * N * K // BS
+        gbs = nbytes / (u * 1e-6) / 1e9
+        rows["%s W" % dtn] = {"us": round(u, 2), "GB/s": round(gbs, 1),
+                              "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+        del Wq, outs
+    res["q4_quantize N=28672 K=8192 bs=64"] = rows
     log("C5 large-vocabulary projection")
     q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0)
     K, N = 2560, 248320

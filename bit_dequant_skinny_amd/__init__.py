@@ -10,6 +10,8 @@ Entry points (same names as the C ABI in include/q4skinny.h):
                  bias=None, out_dtype=None)   (q4_gemm_skinny_path / q4_gemm_skinny_ex)
   bf16_gemm_skinny(A, W, bias=None, out=None)
   q4_dequant(Wpacked, absmax, codebook, blocksize=64, out_dtype=torch.bfloat16, out=None)
+  q4_quantize(W, codebook, blocksize=64, out=None)   codebook: host sequence of 16 floats
+  q4_codebook_preset(name)   "nf4_style" or "int4" -> numpy float32 [16]
   q4_get_crossover_m() / q4_set_crossover_m(m) / q4_release_workspace()
   q4_copy_probe(src, dst) / q4_version()
 ``lib()`` returns the raw ctypes handle for callers that pass pointers.
@@ -30,8 +32,9 @@ FUSED_MAX_M = 16
 EXPORTS = (
     "q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex", "bf16_gemm_skinny", "q4_dequant",
     "q4_get_crossover_m", "q4_set_crossover_m", "q4_release_workspace", "q4_last_error",
-    "q4_copy_probe", "q4_version",
+    "q4_copy_probe", "q4_version", "q4_quantize", "q4_codebook_preset",
 )
+PRESETS = {"nf4_style": 0, "int4": 1}
 
 
 class Q4Error(RuntimeError):
@@ -49,6 +52,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError("libq4skinny.so is not built; run python -m bit_dequant_skinny_amd.build")
+        # torch first: its HIP runtime is then the one the library binds to
+        # (same soname), so the process has a single runtime.  Loading the
+        # library first pulls in a second copy that sees no device once
+        # torch's has claimed it.
+        _torch()
         L = ctypes.CDLL(LIB_PATH)
         P, I = ctypes.c_void_p, ctypes.c_int
         L.q4_gemm_skinny.argtypes = [P, P, P, P, I, I, I, I, P, P]
@@ -58,9 +66,12 @@ def lib():
         L.q4_dequant.argtypes = [P, P, P, I, I, I, P, I, P]
         L.q4_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
         L.q4_set_crossover_m.argtypes = [I]
+        L.q4_quantize.argtypes = [P, I, P, I, I, I, P, P, P]
+        L.q4_codebook_preset.argtypes = [I, P]
         for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
                      "bf16_gemm_skinny", "q4_dequant",
-                     "q4_copy_probe", "q4_set_crossover_m", "q4_release_workspace"):
+                     "q4_copy_probe", "q4_set_crossover_m", "q4_release_workspace",
+                     "q4_quantize", "q4_codebook_preset"):
             getattr(L, name).restype = ctypes.c_int
         L.q4_get_crossover_m.restype = ctypes.c_int
         L.q4_last_error.restype = ctypes.c_char_p
@@ -209,3 +220,34 @@ def q4_release_workspace() -> None:
 
 def q4_version() -> str:
     return lib().q4_version().decode()
+
+
+def q4_quantize(W, codebook, blocksize: int = 64, out=None):
+    """(Wpacked uint8 [N, K/2], absmax fp32 [N, K/blocksize]) of W (bf16, fp16
+    or fp32 on the GPU); codebook: 16 strictly increasing floats (host)."""
+    import numpy as np
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    N, K = W.shape
+    cb = np.ascontiguousarray(np.asarray(codebook, dtype=np.float32).reshape(-1))
+    if cb.size != 16:
+        raise ValueError("codebook must hold 16 entries")
+    if out is None:
+        nb = K // blocksize if blocksize > 0 and K % blocksize == 0 else 0
+        out = (torch.empty((N, K // 2), dtype=torch.uint8, device=W.device),
+               torch.empty((N, nb), dtype=torch.float32, device=W.device))
+    Wp, am = out
+    _check(lib().q4_quantize(
+        _dev(W, "W", W.dtype), _dtype_code(W.dtype), cb.ctypes.data_as(ctypes.c_void_p), N, K,
+        blocksize, _dev(Wp, "Wpacked", torch.uint8), _dev(am, "absmax", torch.float32),
+        _stream(W)))
+    return Wp, am
+
+
+def q4_codebook_preset(name: str = "nf4_style"):
+    """A 16-entry fp32 table (numpy): "nf4_style" or "int4"."""
+    import numpy as np
+    out = np.empty(16, dtype=np.float32)
+    _check(lib().q4_codebook_preset(PRESETS[name], out.ctypes.data_as(ctypes.c_void_p)))
+    return out

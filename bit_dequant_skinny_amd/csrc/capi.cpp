@@ -10,7 +10,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -319,6 +321,78 @@ q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *c
                                       static_cast<hipStream_t>(stream));
     st = check_launch(e, "dequant");
     return st == Q4_OK ? ok() : st;
+}
+
+q4_status q4_quantize(const void *W, int w_dtype, const float *codebook, int N, int K,
+                      int blocksize, uint8_t *Wpacked, float *absmax, void *stream) {
+    if (!known_dtype(w_dtype)) return fail(Q4_ERR_INVALID_ARGUMENT, "unknown w_dtype %d", w_dtype);
+    int bs_log2 = 0;
+    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
+    if (st != Q4_OK) return st;
+    if (blocksize < 32)
+        return fail(Q4_ERR_UNSUPPORTED, "blocksize %d: the quantizer needs >= 32", blocksize);
+    if (!codebook) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL codebook");
+    q4::QuantizeTable tab{};
+    for (int i = 0; i < 16; ++i)
+        if (!std::isfinite(codebook[i]))
+            return fail(Q4_ERR_INVALID_ARGUMENT, "codebook entry %d is not finite", i);
+    for (int i = 0; i < 15; ++i) {
+        if (!(codebook[i] < codebook[i + 1]))
+            return fail(Q4_ERR_INVALID_ARGUMENT,
+                        "the quantizer needs a strictly increasing codebook (entries %d, %d)", i,
+                        i + 1);
+        tab.mid[i] = ((double)codebook[i] + (double)codebook[i + 1]) / 2.0;  // exact
+    }
+    // the entry nearest to 0, ties to the lower one: midpoints below 0
+    tab.zero_code = 0;
+    for (int i = 0; i < 15; ++i) tab.zero_code += tab.mid[i] < 0.0 ? 1u : 0u;
+    if (N == 0) return ok();
+    if (!W || !Wpacked || !absmax) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(W, 16) || !aligned(Wpacked, 16) || !aligned(absmax, 4))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "W and Wpacked must be 16-byte aligned, absmax 4-byte aligned");
+    drain_prior_error();
+    hipError_t e = q4::launch_quantize(W, w_dtype, N, K, bs_log2, tab, Wpacked, absmax,
+                                       static_cast<hipStream_t>(stream));
+    st = check_launch(e, "quantize");
+    return st == Q4_OK ? ok() : st;
+}
+
+namespace {
+// Standard normal quantile by bisection on 0.5 * erfc(-x / sqrt 2): the
+// function is increasing, so 200 halvings of [-40, 40] pin the root to the
+// last bit of a double.
+double normal_quantile(double p) {
+    double lo = -40.0, hi = 40.0;
+    for (int it = 0; it < 200; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p) lo = mid;
+        else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+}  // namespace
+
+q4_status q4_codebook_preset(int which, float *codebook) {
+    if (!codebook) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL codebook");
+    if (which == Q4_CODEBOOK_INT4) {
+        for (int i = 0; i < 16; ++i) codebook[i] = (float)(i - 8) / 8.0f;
+        return ok();
+    }
+    if (which != Q4_CODEBOOK_NF4_STYLE)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown codebook preset %d", which);
+    const double p_max = 0.97;
+    double pos[8], neg[7];
+    for (int i = 1; i <= 8; ++i) pos[i - 1] = normal_quantile(0.5 + (i / 8.0) * (p_max - 0.5));
+    for (int i = 1; i <= 7; ++i) neg[i - 1] = normal_quantile(0.5 - (i / 7.0) * (p_max - 0.5));
+    double v[16];
+    int n = 0;
+    for (int i = 0; i < 7; ++i) v[n++] = neg[i] / -neg[6];
+    v[n++] = 0.0;
+    for (int i = 0; i < 8; ++i) v[n++] = pos[i] / pos[7];
+    std::sort(v, v + 16);
+    for (int i = 0; i < 16; ++i) codebook[i] = (float)v[i];
+    return ok();
 }
 
 int q4_get_crossover_m(void) { return crossover(); }

@@ -39,6 +39,17 @@ hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
 hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,
                             int N, int K, void *C, int c_dt, hipStream_t s);
 
+// Quantizer thresholds derived on the host from a strictly increasing table:
+// mid[i] = (c[i] + c[i+1]) / 2 in fp64 (exact), zero_code = the entry nearest
+// to 0 (ties to the lower one).
+struct QuantizeTable {
+    double mid[15];
+    uint32_t zero_code;
+};
+hipError_t launch_quantize(const void *W, int w_dt, int N, int K, int bs_log2,
+                           const QuantizeTable &tab, uint8_t *Wpacked, float *absmax,
+                           hipStream_t s);
+
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
 
 }  // namespace q4

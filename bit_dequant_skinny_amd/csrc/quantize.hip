@@ -1,0 +1,140 @@
+// Blockwise 4-bit quantization: W[N,K] -> Wpacked[N,K/2] + absmax[N,K/bs].
+//
+// The step before the path: it produces the packed weights and block scales
+// the fused kernels read (blockwise absmax quantization to a 16-entry table,
+// blocksize 64 by default, in the bitsandbytes pull request "[ROCm] Optimize
+// kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1",
+// maintainer's comment).  For a strictly increasing table c[0..15]:
+//   absmax = max |w| over the block (exact);
+//   code   = the entry nearest to the exact ratio w / absmax, a tie going to
+//            the lower entry; a block of zeros takes the ratio 0.
+//
+// No division: with m_i = (c[i] + c[i+1]) / 2 (computed exactly on the host
+// in fp64), the code is the number of i with m_i * absmax < w.  That product
+// is exact in fp64; the kernel rounds it up to U_i, the smallest fp32 above
+// it, once per block, after which "m_i * absmax < w" is exactly "w >= U_i" for
+// every fp32 w: fifteen fp32 compares per weight.
+//
+// Layout: one lane takes 8 consecutive weights (one packed 32-bit word of
+// codes); bs/8 neighbouring lanes hold one block (K % bs == 0, so blocks of
+// the flattened matrix are blocks of its rows) and combine their maxima with
+// a butterfly of lane swaps.  HBM-bound for fp32 input (4.5 bytes per
+// weight); for 16-bit inputs the compares bound it.
+#include "device.h"
+#include "launch.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Smallest fp32 strictly above the fp64 value t (t finite, |t| below the
+// fp32 range or the result is +-inf as rounding gives).
+__device__ __forceinline__ float next_fp32_above(double t) {
+    float f = (float)t;  // nearest
+    if ((double)f <= t) {
+        const uint32_t u = __float_as_uint(f);
+        if ((u & 0x7fffffffu) == 0) f = __uint_as_float(1u);       // +-0 -> smallest subnormal
+        else if ((u >> 31) == 0) f = __uint_as_float(u + 1u);      // positive: one ulp up
+        else f = __uint_as_float(u - 1u);                          // negative: one ulp toward 0
+    }
+    return f;
+}
+
+template <int WT>
+__device__ __forceinline__ void load8w(const void *W, uint64_t word, float (&w)[8]) {
+    if constexpr (WT == kF32) {
+        const float4 *p = reinterpret_cast<const float4 *>(W) + 2 * word;
+        const float4 a = p[0], b = p[1];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+        const uint4 v = reinterpret_cast<const uint4 *>(W)[word];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (WT == kF16) {
+                w[2 * t] = f16_to_f32(d[t] & 0xffffu);
+                w[2 * t + 1] = f16_to_f32(d[t] >> 16);
+            } else {
+                w[2 * t] = bf16_lo(d[t]);
+                w[2 * t + 1] = bf16_hi(d[t]);
+            }
+        }
+    }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const void *__restrict__ W, uint64_t words, int bs_log2, QuantizeTable tab,
+    uint32_t *__restrict__ packed, float *__restrict__ absmax) {
+    const int lane = threadIdx.x & 63;
+    const int lpb = 1 << (bs_log2 - 3);  // lanes per block (4..32)
+    const uint64_t wave = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
+    // The loop bound is uniform across the wave (64 words = 512 weights, a
+    // multiple of every blocksize), so the lane swaps run with all lanes on.
+    for (uint64_t base = wave * 64; base < words; base += nwaves * 64) {
+        const uint64_t word = base + lane;
+        const bool live = word < words;
+        float w[8];
+        if (live) {
+            load8w<WT>(W, word, w);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = 0.f;
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(w[j]));
+        for (int off = 1; off < lpb; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+        uint32_t out;
+        if (a > 0.f) {
+            float U[15];
+#pragma unroll
+            for (int i = 0; i < 15; ++i) U[i] = next_fp32_above(tab.mid[i] * (double)a);
+            out = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int i = 0; i < 15; ++i) c += w[j] >= U[i] ? 1u : 0u;
+                out |= c << (4 * j);
+            }
+        } else {
+            out = tab.zero_code * 0x11111111u;
+        }
+        if (live) {
+            packed[word] = out;
+            if ((lane & (lpb - 1)) == 0) absmax[(word * 8) >> bs_log2] = a;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *W, int w_dt, int N, int K, int bs_log2,
+                           const QuantizeTable &tab, uint8_t *Wpacked, float *absmax,
+                           hipStream_t s) {
+    const uint64_t words = (uint64_t)N * (uint64_t)K / 8;
+    const DeviceInfo info = device_info();
+    const uint64_t per_block = (uint64_t)kThreads;  // one word per thread per pass
+    uint64_t blocks = (words + per_block - 1) / per_block;
+    const uint64_t cap = (uint64_t)info.num_cus * 16;
+    if (blocks > cap) blocks = cap;
+    if (blocks == 0) blocks = 1;
+    uint32_t *packed = reinterpret_cast<uint32_t *>(Wpacked);
+    if (w_dt == kF32)
+        quantize_kernel<kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+            W, words, bs_log2, tab, packed, absmax);
+    else if (w_dt == kF16)
+        quantize_kernel<kF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+            W, words, bs_log2, tab, packed, absmax);
+    else
+        quantize_kernel<kBf16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+            W, words, bs_log2, tab, packed, absmax);
+    return hipGetLastError();
+}
+
+}  // namespace q4

@@ -167,6 +167,50 @@ q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *c
                      int N, int K, int blocksize, void *out, int out_dtype, void *stream);
 
 /*
+ * q4_quantize: blockwise 4-bit quantization, the inverse of q4_dequant.
+ *
+ * Produces the packed weights and block scales of the fused kernels: the
+ * blockwise absmax quantization to a 16-entry NF4/FP4 table, blocksize 64 by
+ * default, that the maintainer's comment on the bitsandbytes pull request
+ * "[ROCm] Optimize kgemm_4bit_inference_naive ..." describes.  The pages do
+ * not spell out the rounding; this library's reading:
+ *   absmax[n, b] = max |W[n, k]| over the block (exact);
+ *   code(n, k)   = the index of the codebook entry nearest to the exact ratio
+ *                  W[n, k] / absmax[n, b], a tie going to the lower entry;
+ *                  a block of zeros stores absmax 0 and the entry nearest 0.
+ *
+ *  W        [N, K] of w_dtype (Q4_DTYPE_BF16, Q4_DTYPE_FP16 or Q4_DTYPE_FP32),
+ *           device memory, finite values.
+ *  codebook fp32 [16] in HOST memory, strictly increasing (the thresholds
+ *           between entries are derived on the host).
+ *  Wpacked  uint8 [N, K/2] output, layout as in q4_gemm_skinny.
+ *  absmax   fp32 [N, K/blocksize] output.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, unknown w_dtype, N/K < 0, K == 0,
+ *    K % blocksize != 0, blocksize <= 0 or odd, a codebook that is not finite
+ *    and strictly increasing, W or Wpacked not 16-byte aligned, absmax not
+ *    4-byte aligned.
+ *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}.
+ */
+q4_status q4_quantize(const void *W, int w_dtype, const float *codebook, int N, int K,
+                      int blocksize, uint8_t *Wpacked, float *absmax, void *stream);
+
+/*
+ * q4_codebook_preset: writes a 16-entry table to host memory.  The pages name
+ * NF4 and FP4 tables but print no values, so the presets follow rules of this
+ * library:
+ *  Q4_CODEBOOK_NF4_STYLE  8 positive entries at the standard-normal quantiles
+ *    of 0.5 + (i/8)(0.97 - 0.5), i = 1..8, 7 negative entries at
+ *    0.5 - (i/7)(0.97 - 0.5), i = 1..7, each side divided by its largest
+ *    magnitude (so the extremes are exactly -1 and 1), plus 0; sorted.
+ *  Q4_CODEBOOK_INT4       the uniform grid (i - 8) / 8, i = 0..15.
+ * Both are strictly increasing and hold -1 and 0, so they suit q4_quantize.
+ * Q4_ERR_INVALID_ARGUMENT for an unknown preset or a NULL pointer.
+ */
+enum { Q4_CODEBOOK_NF4_STYLE = 0, Q4_CODEBOOK_INT4 = 1 };
+q4_status q4_codebook_preset(int which, float *codebook);
+
+/*
  * Crossover control.  The fused-versus-split threshold (fused when
  * M <= crossover) starts at the value measured on MI355X and compiled in,
  * unless the environment variable Q4_CROSSOVER_M holds an integer at the

@@ -148,3 +148,66 @@ def test_binding_refuses_cpu_tensors():
     cb = torch.zeros(16)
     with pytest.raises(ValueError):
         q4.q4_gemm_skinny(A, W, am, cb, out=torch.empty(1, 4, dtype=torch.bfloat16))
+
+
+def _ex(M=1, N=16, K=128, bs=64, adt=0, cdt=0, A=FAKE, W=FAKE, am=FAKE, cb=FAKE, bias=None,
+        C=FAKE, path=0):
+    return q4.lib().q4_gemm_skinny_ex(A, adt, W, am, cb, bias, M, N, K, bs, C, cdt, None, path)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(adt=3), INV), (dict(cdt=-1), INV), (dict(path=9), INV), (dict(M=-2), INV),
+    (dict(K=96), INV), (dict(bs=16, K=128), UNS), (dict(A=None), INV), (dict(C=None), INV),
+    (dict(cdt=1, C=FAKE + 2), INV), (dict(cdt=1, bias=FAKE + 2), INV), (dict(bias=FAKE + 1), INV),
+    (dict(A=FAKE + 8), INV), (dict(adt=1, path=2), UNS), (dict(adt=1, M=17), UNS),
+    (dict(path=1, M=17), UNS), (dict(M=0), OK), (dict(N=0, cdt=2), OK),
+    (dict(adt=1, M=0, path=1), OK),
+])
+def test_q4_gemm_ex_validation(kw, expect):
+    assert _ex(**kw) == expect
+    assert (q4.lib().q4_last_error().decode() == "") == (expect == OK)
+
+
+def _quant(cb, N=4, K=128, bs=64, wdt=0, W=FAKE, Wp=FAKE, am=FAKE):
+    import numpy as np
+    c = None if cb is None else np.ascontiguousarray(cb, dtype=np.float32)
+    ptr = None if c is None else c.ctypes.data_as(ctypes.c_void_p)
+    return q4.lib().q4_quantize(W, wdt, ptr, N, K, bs, Wp, am, None)
+
+
+def test_q4_quantize_validation():
+    import numpy as np
+    good = q4.q4_codebook_preset("nf4_style")
+    assert _quant(good, N=0) == OK
+    assert _quant(None) == INV
+    assert _quant(good, wdt=7) == INV
+    assert _quant(good, K=100) == INV
+    assert _quant(good, bs=16, K=128) == UNS
+    assert _quant(good, W=None) == INV
+    assert _quant(good, Wp=FAKE + 4) == INV
+    assert _quant(good, am=FAKE + 2) == INV
+    bad = good.copy()
+    bad[3], bad[4] = bad[4], bad[3]   # not increasing
+    assert _quant(bad, N=0) == INV
+    dup = good.copy()
+    dup[5] = dup[6]                    # not strictly increasing
+    assert _quant(dup, N=0) == INV
+    nan = good.copy()
+    nan[2] = np.nan
+    assert _quant(nan, N=0) == INV
+
+
+def test_codebook_presets():
+    import numpy as np
+    import synth
+    nf4 = q4.q4_codebook_preset("nf4_style")
+    # the same rule as the test generator's table, which uses Python's own
+    # normal quantile (a different algorithm from the library's bisection)
+    assert np.array_equal(nf4.view(np.uint32), synth.nf4_style_codebook().view(np.uint32))
+    int4 = q4.q4_codebook_preset("int4")
+    assert list(int4) == [(i - 8) / 8 for i in range(16)]
+    for cb in (nf4, int4):
+        assert np.all(np.diff(cb) > 0) and cb[0] == -1.0 and 0.0 in cb
+    out = np.empty(16, dtype=np.float32)
+    assert q4.lib().q4_codebook_preset(5, out.ctypes.data_as(ctypes.c_void_p)) == INV
+    assert q4.lib().q4_codebook_preset(0, None) == INV
