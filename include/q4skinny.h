@@ -48,8 +48,12 @@ typedef enum q4_status {
 enum { Q4_DTYPE_BF16 = 0, Q4_DTYPE_FP32 = 1, Q4_DTYPE_FP16 = 2 };
 enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
 
-/* Largest M the fused 4-bit kernels handle; larger M always takes the split path. */
-#define Q4_FUSED_MAX_M 16
+/* Token rows one fused 4-bit pass handles; the fused path runs larger M in
+ * passes over slabs of this many rows, each pass streaming the packed weights
+ * again. */
+#define Q4_FUSED_PASS_M 16
+/* Largest crossover value q4_set_crossover_m accepts. */
+#define Q4_CROSSOVER_MAX 65536
 
 /*
  * q4_gemm_skinny: C = A * dequant(W)^T with W blockwise 4-bit quantized.
@@ -76,9 +80,9 @@ enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
  *    not 16-byte aligned, codebook not 4-byte aligned, C not 2-byte aligned.
  *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}; M or N above
  *    2^30/K-sized limits (N * K / 2 must fit in 2^40 bytes).
- *  Which kernel runs: M <= q4_get_crossover_m() and M <= Q4_FUSED_MAX_M take
- *  the fused kernel; other M take the split path (dequantize to bf16 into a
- *  library-owned workspace of N*K*2 bytes, then an MFMA bf16 GEMM).
+ *  Which kernel runs: M <= the crossover take the fused kernel (in passes of
+ *  Q4_FUSED_PASS_M rows); other M take the split path (dequantize to bf16 into
+ *  a library-owned workspace of N*K*2 bytes, then an MFMA bf16 GEMM).
  */
 q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *absmax,
                          const float *codebook, int M, int N, int K, int blocksize,
@@ -87,8 +91,7 @@ q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *abs
 /*
  * q4_gemm_skinny_path: q4_gemm_skinny with the path forced (Q4_PATH_AUTO,
  * Q4_PATH_FUSED or Q4_PATH_SPLIT).  Used by the crossover measurement and
- * the tests.  Q4_PATH_FUSED with M > Q4_FUSED_MAX_M is Q4_ERR_UNSUPPORTED;
- * an unknown path value is Q4_ERR_INVALID_ARGUMENT.
+ * the tests.  An unknown path value is Q4_ERR_INVALID_ARGUMENT.
  */
 q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
                               const float *codebook, int M, int N, int K, int blocksize,
@@ -119,7 +122,7 @@ q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float
  *  Q4_ERR_INVALID_ARGUMENT: as q4_gemm_skinny, plus an unknown dtype or
  *    path, C or bias not aligned to their element size.
  *  Q4_ERR_UNSUPPORTED: as q4_gemm_skinny; fp32 activations on the split
- *    path (M > Q4_FUSED_MAX_M, or above the crossover, or forced).
+ *    path (above the crossover, or forced).
  */
 q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
                             const float *absmax, const float *codebook, const void *bias, int M,
@@ -214,7 +217,7 @@ q4_status q4_codebook_preset(int which, float *codebook);
  * Crossover control.  The fused-versus-split threshold (fused when
  * M <= crossover) starts at the value measured on MI355X and compiled in,
  * unless the environment variable Q4_CROSSOVER_M holds an integer at the
- * first call.  q4_set_crossover_m accepts 0..Q4_FUSED_MAX_M (0 = always split).
+ * first call.  q4_set_crossover_m accepts 0..Q4_CROSSOVER_MAX (0 = always split).
  */
 int q4_get_crossover_m(void);
 q4_status q4_set_crossover_m(int m);

@@ -45,7 +45,7 @@ def test_exports_seen_by_nm():
 
 def test_version_and_crossover_defaults():
     assert "gfx950" in q4.q4_version()
-    assert 0 <= q4.q4_get_crossover_m() <= q4.FUSED_MAX_M
+    assert 0 <= q4.q4_get_crossover_m() <= q4.CROSSOVER_MAX
 
 
 def _q4(M=1, N=16, K=128, bs=64, A=FAKE, W=FAKE, am=FAKE, cb=FAKE, C=FAKE, path=0):
@@ -60,7 +60,7 @@ def _q4(M=1, N=16, K=128, bs=64, A=FAKE, W=FAKE, am=FAKE, cb=FAKE, C=FAKE, path=
     (dict(A=None), INV), (dict(W=None), INV), (dict(am=None), INV), (dict(cb=None), INV),
     (dict(C=None), INV), (dict(A=FAKE + 8), INV), (dict(W=FAKE + 4), INV),
     (dict(am=FAKE + 4), INV), (dict(cb=FAKE + 2), INV), (dict(C=FAKE + 1), INV),
-    (dict(path=7), INV), (dict(path=1, M=17), UNS),
+    (dict(path=7), INV), (dict(path=1, M=17, K=100), INV),
     (dict(M=0), OK), (dict(N=0), OK), (dict(M=0, A=None, C=None), OK),
 ])
 def test_q4_gemm_validation(kw, expect):
@@ -118,7 +118,7 @@ def test_crossover_setter_range():
     L = q4.lib()
     old = L.q4_get_crossover_m()
     assert L.q4_set_crossover_m(-1) == INV
-    assert L.q4_set_crossover_m(17) == INV
+    assert L.q4_set_crossover_m(q4.CROSSOVER_MAX + 1) == INV
     assert L.q4_set_crossover_m(4) == OK and L.q4_get_crossover_m() == 4
     assert L.q4_set_crossover_m(old) == OK
 
@@ -159,8 +159,8 @@ def _ex(M=1, N=16, K=128, bs=64, adt=0, cdt=0, A=FAKE, W=FAKE, am=FAKE, cb=FAKE,
     (dict(adt=3), INV), (dict(cdt=-1), INV), (dict(path=9), INV), (dict(M=-2), INV),
     (dict(K=96), INV), (dict(bs=16, K=128), UNS), (dict(A=None), INV), (dict(C=None), INV),
     (dict(cdt=1, C=FAKE + 2), INV), (dict(cdt=1, bias=FAKE + 2), INV), (dict(bias=FAKE + 1), INV),
-    (dict(A=FAKE + 8), INV), (dict(adt=1, path=2), UNS), (dict(adt=1, M=17), UNS),
-    (dict(path=1, M=17), UNS), (dict(M=0), OK), (dict(N=0, cdt=2), OK),
+    (dict(A=FAKE + 8), INV), (dict(adt=1, path=2), UNS), (dict(adt=1, M=40, path=2), UNS),
+    (dict(path=1, M=17, bs=48, K=96), UNS), (dict(M=0), OK), (dict(N=0, cdt=2), OK),
     (dict(adt=1, M=0, path=1), OK),
 ])
 def test_q4_gemm_ex_validation(kw, expect):

@@ -87,10 +87,17 @@ def test_fp32_activations_reject_split():
         q4.q4_gemm_skinny(A, Wp, am, cb, 64, path="split")
     assert e.value.status == q4.Q4_ERR_UNSUPPORTED
     A20 = to_dev(synth.activations(20, 128, 6, "fp32"), "f32")
-    with pytest.raises(q4.Q4Error) as e:
-        q4.q4_gemm_skinny(A20, Wp, am, cb, 64)
+    old = q4.q4_get_crossover_m()
+    try:
+        q4.q4_set_crossover_m(16)   # M = 20 now routes to split, which fp32 cannot take
+        with pytest.raises(q4.Q4Error) as e:
+            q4.q4_gemm_skinny(A20, Wp, am, cb, 64)
+    finally:
+        q4.q4_set_crossover_m(old)
     assert e.value.status == q4.Q4_ERR_UNSUPPORTED
-    del t
+    C = q4.q4_gemm_skinny(A20, Wp, am, cb, 64, path="fused")   # in two passes
+    t.cuda.synchronize()
+    assert C.shape == (20, 16)
 
 
 def test_fused_bias_alone_and_determinism():

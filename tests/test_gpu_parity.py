@@ -146,11 +146,28 @@ def test_split_parity(M, N, K, bs):
     assert_within_tolerance(got, Cr, S, "split vs fused oracle")
 
 
-def test_auto_path_routes_large_m_to_split():
+@pytest.mark.parametrize("M", [17, 33, 64, 70])
+@pytest.mark.parametrize("N,K,bs", [(37, 640, 64), (130, 2048, 32), (16, 4096, 128)])
+def test_fused_parity_in_slabs(M, N, K, bs):
+    """M above one pass runs in 16-row slabs; every slab meets the tolerance."""
+    p = synth.q4_problem(M, N, K, bs, config=55, shape=N % 5)
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused")
+    _sync()
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(bf16_host(C), Cr, S, "fused slabs M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_auto_path_routes_above_crossover_to_split():
     M, N, K, bs = 24, 64, 512, 64
     p = synth.q4_problem(M, N, K, bs, config=57)
     A, Wp, am, cb = q4_to_dev(p)
-    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs)
+    old = q4.q4_get_crossover_m()
+    try:
+        q4.q4_set_crossover_m(16)
+        C = q4.q4_gemm_skinny(A, Wp, am, cb, bs)
+    finally:
+        q4.q4_set_crossover_m(old)
     Cs = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="split")
     _sync()
     assert np.array_equal(bf16_host(C), bf16_host(Cs))
