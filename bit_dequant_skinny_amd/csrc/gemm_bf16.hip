@@ -22,6 +22,13 @@
 // When N is small the waves of a workgroup split K and combine their fp32
 // tiles through LDS in a fixed order (deterministic, no atomics).
 //
+// Up to 16 token rows (the skinny case and the split path's slabs of 16) take
+// the streaming kernel: each wave keeps kRing steps of weights (1 KiB per step)
+// and their activations in flight in a register ring, with buffer loads whose
+// hardware range check returns zeros past the end of a buffer, so absent token
+// rows, weight rows past N and steps past the wave's share of K cost no memory
+// traffic and need no branches.  Wider slabs take the plain kernel below.
+//
 // fp16 activations (split path of the 4-bit GEMM) are split exactly into
 // bf16 hi + lo and take two MFMAs per step.  The bias (optional) has the
 // output's type; the output is bf16, fp16 or fp32, rounded once from the fp32
@@ -35,6 +42,96 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+
+constexpr int kRing = 8;                     // steps of 32 k in flight per wave
+constexpr uint32_t kPastEnd = 0x80000000u;   // an offset beyond every buffer: reads zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int AT>
+__device__ __forceinline__ floatx4 mfma_step(uint4 av, uint4 wv, floatx4 acc) {
+    if constexpr (AT == kF16) {
+        const uint2 x = f16x2_to_bf16_hilo(av.x), y = f16x2_to_bf16_hilo(av.y);
+        const uint2 z = f16x2_to_bf16_hilo(av.z), w = f16x2_to_bf16_hilo(av.w);
+        acc = mfma_bf16_16x16x32(as_bf16x8(make_uint4(x.x, y.x, z.x, w.x)), as_bf16x8(wv), acc);
+        return mfma_bf16_16x16x32(as_bf16x8(make_uint4(x.y, y.y, z.y, w.y)), as_bf16x8(wv), acc);
+    } else {
+        return mfma_bf16_16x16x32(as_bf16x8(av), as_bf16x8(wv), acc);
+    }
+}
+
+// Streaming kernel for M <= 16: wave (tile, k part) as in bf16_gemm_kernel,
+// every step one 16-byte weight load and one 16-byte activation load per
+// lane, kRing steps ahead of the MFMA that consumes them.
+template <int AT>
+__global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
+    const void *__restrict__ bias, int M, int N, int K, int ksplit,
+    void *__restrict__ C, int c_dt) {
+    __shared__ floatx4 red[kWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tiles_per_block = kWaves / ksplit;
+    const int tile = blockIdx.x * tiles_per_block + wave / ksplit;
+    const int kpart = wave % ksplit;
+    const int n0 = tile * 16;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    const int steps = (K + 31) >> 5;
+    const int s_begin = (kpart * steps) / ksplit;
+    const int s_end = ((kpart + 1) * steps) / ksplit;
+
+    const __amdgpu_buffer_rsrc_t wres = make_rsrc(W, (uint32_t)N * (uint32_t)K * 2);
+    const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
+    // rows past N and tokens past M lie beyond their buffers
+    const uint32_t w_row = (uint32_t)(n0 + j) * (uint32_t)K * 2;
+    const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;
+    auto offs = [&](int st, uint32_t row) -> uint32_t {
+        const uint32_t k = (uint32_t)(st << 5) + (uint32_t)(g << 3);
+        return (st < s_end && k < (uint32_t)K) ? row + 2 * k : kPastEnd;
+    };
+    uint4 wv[kRing], av[kRing];
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+        wv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)offs(s_begin + r, w_row), 0, 0));
+        av[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)offs(s_begin + r, a_row), 0, 0));
+        __builtin_amdgcn_sched_barrier(0);  // issue in ring order
+    }
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s = s_begin; s < s_end; s += kRing) {
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) {
+            acc = mfma_step<AT>(av[r], wv[r], acc);
+            const int nx = s + r + kRing;
+            wv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)offs(nx, w_row), 0, 0));
+            av[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)offs(nx, a_row), 0, 0));
+            // keep each refill right after the MFMA that frees its registers,
+            // so every step waits only for loads issued kRing steps earlier
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if (ksplit > 1) {
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (kpart != 0) return;
+        for (int p = 1; p < ksplit; ++p) {
+            const floatx4 o = red[wave + p][lane];
+            acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+        }
+    }
+    if (n0 + j >= N) return;
+    const float b = bias ? load_elem(bias, n0 + j, c_dt) : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tok = g * 4 + r;
+        if (tok < M) store_elem(C, (size_t)tok * N + n0 + j, acc[r] + b, c_dt);
+    }
+}
 
 template <int AT, int MT>
 __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(
@@ -119,8 +216,16 @@ hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const void *bias, int
     if (tiles < info.num_cus * 2) ksplit = 4;
     const int tiles_per_block = kWaves / ksplit;
     const int blocks = (tiles + tiles_per_block - 1) / tiles_per_block;
-    bf16_gemm_kernel<AT, MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K, ksplit,
-                                                                     C, c_dt);
+    // The streaming kernel's offsets are 32-bit: weights (plus one tile of
+    // rows past N) and 16 rows of activations must stay below 4 GiB.
+    const bool stream = MT == 1 && ((uint64_t)N + 16) * (uint64_t)K * 2 < (1ull << 31) &&
+                        16ull * (uint64_t)K * 2 < (1ull << 31);
+    if (stream)
+        bf16_stream_kernel<AT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
+                                                                       ksplit, C, c_dt);
+    else
+        bf16_gemm_kernel<AT, MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
+                                                                         ksplit, C, c_dt);
     return hipGetLastError();
 }
 
