@@ -78,26 +78,65 @@ class Dev:
             out.append(tuple(x.clone() for x in tensors))
         return out
 
-    def time_launches(self, fns, reps, warmup=3):
+    def time_launches(self, fns, reps, warmup=3, graph=True):
         """Average duration of each launch in fns: `reps` launches of one
         function back to back (f(i) for i = 0..reps-1, so rotating weight
-        copies change every launch) between one pair of HIP events on torch's
-        current stream, which the library launches on.  Back-to-back launches
-        keep the per-launch event overhead out of the average."""
+        copies change every launch) between one pair of HIP events.  With
+        graph=True the launches are captured once into a HIP graph on a side
+        stream and timed as one replay, so a kernel shorter than a Python call
+        is not timed at the rate the host can launch it; calls that cannot be
+        captured (host synchronisation, allocation) are timed eagerly on
+        torch's current stream, which the library launches on."""
         t = self.t
         out = []
         for f in fns:
             for i in range(warmup):
                 f(i)
             t.cuda.synchronize()
-            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-            e0.record()
-            for i in range(reps):
-                f(i)
-            e1.record()
-            t.cuda.synchronize()
-            out.append(e0.elapsed_time(e1) * 1e3 / reps)  # microseconds
+            us = self._time_graph(f, reps) if graph else None
+            if us is None:
+                e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(reps):
+                    f(i)
+                e1.record()
+                t.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+            out.append(us)  # microseconds
         return out
+
+    def _time_graph(self, f, reps):
+        t = self.t
+        side = t.cuda.Stream()
+        # warm up on the capture stream: the library keeps its scratch per
+        # stream and must not allocate while the stream is captured
+        with t.cuda.stream(side):
+            for i in range(2):
+                f(i)
+        t.cuda.synchronize()
+        try:
+            g = t.cuda.CUDAGraph()
+            with t.cuda.graph(g, stream=side):
+                for i in range(reps):
+                    f(i)
+        except Exception as e:  # not capturable: time eagerly
+            log("graph capture failed (%s); timing eagerly" % type(e).__name__)
+            t.cuda.synchronize()
+            return None
+        g.replay()
+        t.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            with t.cuda.stream(side):
+                e0.record(side)
+                g.replay()
+                e1.record(side)
+            t.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            best = us if best is None else min(best, us)
+        del g
+        return best
 
 
 def fused_source_hash():
@@ -264,7 +303,7 @@ def other_configs(d):
                     Wp, am = sets[i % len(sets)]
                     q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path=path)
                 fns.append(f)
-            us = d.time_launches(fns, reps=max(20, min(200, len(sets) * 2)))
+            us = d.time_launches(fns, reps=max(60, min(200, len(sets) * 2)))
             for path, u in zip(paths, us):
                 gbs = q4_bytes(M, N, K) / (u * 1e-6) / 1e9
                 rows["M=%d %s" % (M, path)] = {"us": round(u, 2), "GB/s": round(gbs, 1),
@@ -299,7 +338,7 @@ def other_configs(d):
 
             def f(i):
                 q4.bf16_gemm_skinny(A, sets[i % len(sets)][0], b, out=C)
-            u = d.time_launches([f], reps=max(20, min(200, len(sets) * 2)))[0]
+            u = d.time_launches([f], reps=max(60, min(200, len(sets) * 2)))[0]
             gbs = bf16_bytes(M, N, K, True) / (u * 1e-6) / 1e9
             rows["M=%d" % M] = {"us": round(u, 2), "GB/s": round(gbs, 1),
                                 "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
@@ -335,7 +374,7 @@ def other_configs(d):
         Wq = t.from_numpy(synth.weights_f32(N, K, 85)).to(d.dev).to(tdt)
         outs = (t.empty((N, K // 2), dtype=t.uint8, device=d.dev),
                 t.empty((N, K // BS), dtype=t.float32, device=d.dev))
-        u = d.time_launches([lambda i: q4.q4_quantize(Wq, cbq, BS, out=outs)], reps=20)[0]
+        u = d.time_launches([lambda i: q4.q4_quantize(Wq, cbq, BS, out=outs)], reps=20, graph=False)[0]
         nbytes = N * K * Wq.element_size() + N * K // 2 + 4 * N * K // BS
         gbs = nbytes / (u * 1e-6) / 1e9
         rows["%s W" % dtn] = {"us": round(u, 2), "GB/s": round(gbs, 1),

@@ -94,8 +94,9 @@ constexpr int KW = 8;  // waves per workgroup
 // segment slots the weight ring runs ahead, so every wave keeps TB*RS weight
 // loads in flight.  UF: slots per loop iteration, a multiple of RS with UF*TB
 // even, which makes the ring entry and the decode double-buffer index of
-// every unit compile-time constants.
-template <int AT, int SR, int TB, int RS, int UF>
+// every unit compile-time constants.  P: slots per scale-staging period (a
+// divisor of UF).
+template <int AT, int SR, int TB, int RS, int UF, int P>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
@@ -107,16 +108,20 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     static_assert(64 * KW >= 256, "one table entry per thread");
     __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
     __shared__ float red[KW][TB * SR][64];
-    // Raw block scales of the current and the next period of RS slots, one
-    // row per weight row of the chunk: the RS*KW*128/bs blocks the KW = 8
-    // waves cover in RS slots (16*RS at bs = 64).  There are 128/RS rows (one
-    // 16-byte piece per thread), at least TB*16: the threads past the chunk's
-    // rows write to spare rows, so the staging code has no branches.  Rows
-    // are RS*16 + 2 floats apart so the 16 rows a wave reads at once fall in
-    // distinct banks.
-    static_assert(TB * RS <= 8, "the chunk's rows fit the staging rows");
-    constexpr int kScaleStride = RS * 16 + 2;
-    __shared__ float scl[2][(128 / RS) * kScaleStride];
+    // Raw block scales of the current and the next period of P slots, one
+    // row per weight row of the chunk: the P*KW*128/bs blocks the KW = 8
+    // waves cover in P slots (16*P at bs = 64).  Each thread stages SP
+    // 16-byte pieces per period; there are SP*128/P rows, at least TB*16:
+    // the threads past the chunk's rows write to spare rows, so the staging
+    // code has no branches.  Rows are P*16 + 2 floats apart so the 16 rows a
+    // wave reads at once fall in distinct banks.
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8, "4*P divides the workgroup");
+    static_assert(UF % P == 0, "periods end inside a loop iteration");
+    constexpr int SP = (TB * P + 7) / 8;
+    constexpr int kScaleRows = SP * 128 / P;
+    static_assert(kScaleRows >= TB * 16, "the chunk's rows fit the staging rows");
+    constexpr int kScaleStride = P * 16 + 2;
+    __shared__ float scl[2][kScaleRows * kScaleStride];
     const int G = gridDim.x;
     const int my_chunks = (groups - (int)blockIdx.x + G - 1) / G;
     if (my_chunks <= 0) return;  // uniform over the workgroup
@@ -135,6 +140,14 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const int nseg = (K + 127) >> 7;
     const int spw = (nseg + KW - 1) / KW;  // segment slots per wave per chunk
     const uint32_t row_bytes = (uint32_t)K >> 1;
+    // Workgroups start their walk along K at different slots (whole scale
+    // periods), chosen by b / 8 so that the workgroups on one XCD do too:
+    // neighbouring workgroups then read different parts of their rows at any
+    // time, which spreads the loads over more DRAM banks and channels than a
+    // walk in lockstep (measured 10 % faster at 28672 x 8192).  Slot q of a
+    // chunk is slot (q + rot) % spw of the row.
+    const int nper = spw / P;  // whole periods per chunk
+    const int rot = spw % P == 0 ? (int)((blockIdx.x / 8u) % (uint32_t)nper) * P : 0;
     const uint32_t nb = (uint32_t)K >> bs_log2;
 
     const __amdgpu_buffer_rsrc_t wres = make_rsrc(Wp, (uint32_t)N * row_bytes);
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     uint32_t w_row0 = (group_of(0) * 16 + (uint32_t)j) * row_bytes + w_lane;
     bool w_live = true;
     auto w_seek = [&]() {
-        const int seg = wave + iq * KW;
+        const int seg = wave + ((iq + rot) % spw) * KW;
         w_live = ic < my_chunks && seg < nseg;
         w_row0 = (group_of(ic) * 16 + (uint32_t)j) * row_bytes + (uint32_t)seg * 64 + w_lane;
     };
@@ -174,36 +187,42 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         dst = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 0));
     };
 
-    // Scales are staged through LDS one period (RS slots) ahead: per period
-    // the workgroup needs the RS*KW*128/bs consecutive block scales of each of
-    // its TB*16 rows (64*RS bytes per row at bs = 64), which thread t fetches
-    // as 16-byte piece t % (4*RS) of chunk row t / (4*RS): at most one load
-    // per thread, whole cache lines with no duplicates.
-    const int s_row = tid / (4 * RS);
-    const bool s_thread = s_row < TB * 16;
-    const uint32_t s_piece = (uint32_t)(tid % (4 * RS)) * 16;
-    const uint32_t s_win = (uint32_t)(RS * KW * 128 * 4) >> bs_log2;  // bytes per row per period
+    // Scales are staged through LDS one period (P slots) ahead: per period
+    // the workgroup needs the P*KW*128/bs consecutive block scales of each of
+    // its TB*16 rows (64*P bytes per row at bs = 64), which thread t fetches
+    // as 16-byte piece t % (4*P) of chunk rows t / (4*P) + i*128/P, i < SP:
+    // whole cache lines with no duplicates.
+    const int s_row = tid / (4 * P);
+    const uint32_t s_piece = (uint32_t)(tid % (4 * P)) * 16;
+    const uint32_t s_win = (uint32_t)(P * KW * 128 * 4) >> bs_log2;  // bytes per row per period
     int sc = 0, sq = 0;  // scale cursor: the first slot of the period loaded next
-    auto load_scales = [&]() -> floatx4 {
-        const uint32_t w0 = ((uint32_t)sq * KW * 128 >> bs_log2) * 4;  // window start in the row
-        const uint32_t ns = (group_of(sc) + (uint32_t)(s_row >> 4) * (uint32_t)groups) * 16 +
-                            (uint32_t)(s_row & 15);
-        const bool live = s_thread && sc < my_chunks && s_piece < s_win && w0 + s_piece < nb * 4;
-        const uint32_t so = live ? ns * nb * 4 + w0 + s_piece : kPastEnd;
-        sq += RS;
+    auto load_scales = [&](floatx4 (&out)[SP]) {
+        const uint32_t w0 = ((uint32_t)((sq + rot) % spw) * KW * 128 >> bs_log2) * 4;  // window start
+        const bool live = sc < my_chunks && s_piece < s_win && w0 + s_piece < nb * 4;
+#pragma unroll
+        for (int i = 0; i < SP; ++i) {
+            const int row = s_row + i * (128 / P);
+            const uint32_t ns = (group_of(sc) + (uint32_t)(row >> 4) * (uint32_t)groups) * 16 +
+                                (uint32_t)(row & 15);
+            const uint32_t so = live && row < TB * 16 ? ns * nb * 4 + w0 + s_piece : kPastEnd;
+            out[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sres, (int)so, 0, 0));
+        }
+        sq += P;
         if (sq >= spw) {
             sq = 0;
             ++sc;
         }
-        return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sres, (int)so, 0, 0));
     };
-    // Writes a piece into the staging buffer; every thread writes, so the
-    // compiler has no branch to sink the scale load into and it stays a
-    // period ahead of its use.
-    auto stage_scales = [&](const floatx4 &v, int buf) {
-        float *row = &scl[buf][s_row * kScaleStride + (s_piece >> 2)];
-        *reinterpret_cast<floatx2 *>(row) = floatx2{v[0], v[1]};
-        *reinterpret_cast<floatx2 *>(row + 2) = floatx2{v[2], v[3]};
+    // Writes the pieces into the staging buffer; every thread writes, so the
+    // compiler has no branch to sink the scale loads into and they stay a
+    // period ahead of their use.
+    auto stage_scales = [&](const floatx4 (&v)[SP], int buf) {
+#pragma unroll
+        for (int i = 0; i < SP; ++i) {
+            float *row = &scl[buf][(s_row + i * (128 / P)) * kScaleStride + (s_piece >> 2)];
+            *reinterpret_cast<floatx2 *>(row) = floatx2{v[i][0], v[i][1]};
+            *reinterpret_cast<floatx2 *>(row + 2) = floatx2{v[i][2], v[i][3]};
+        }
     };
     // In slot u of a period, wave w applies the scales of the 64-wide blocks
     // e = 16u + 2w and e + 1 of the period window, which lie in bs-wide blocks
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;  // past the end of A for j >= M
     uint4 anext[4];
     auto load_a = [&](int q) {
-        const uint32_t kk = ((uint32_t)wave + (uint32_t)q * KW) * 128;
+        const uint32_t kk = ((uint32_t)wave + (uint32_t)((q + rot) % spw) * KW) * 128;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t k = kk + k_offset(g, t);
@@ -255,7 +274,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // then the table, then the first decode.
     uint4 wbuf[RS][TB];
     {
-        const floatx4 s0 = load_scales();
+        floatx4 s0[SP];
+        load_scales(s0);
         load_a(0);
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
@@ -284,14 +304,15 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         for (int r = 0; r < SR; ++r) acc[tr][r] = 0.f;
     int pq = 0;   // the slot being computed
     int qp = 0;   // periods done, for the staging buffer parity
-    floatx4 snext;  // the next period's scale piece
+    floatx4 snext[SP];  // the next period's scale pieces
 
     // One slot: TB units (tiles) of 16 rows x 128 k, software-pipelined one
     // unit ahead: the table reads of unit u+1 (the next tile, or tile 0 of
     // the next slot) are in flight while the MFMAs of unit u run, and each
     // ring entry is refilled RS slots ahead right after its decode.  The slot
     // loop starts every chunk at ring entry 0 and decode buffer 0, which holds
-    // when a workgroup has one chunk, or RS = 1 and TB is even.
+    // when a workgroup has one chunk, or when a chunk is a whole number of
+    // loop iterations (spw a multiple of UF).
     auto slot = [&](auto us_c) {
         constexpr int us = decltype(us_c)::value;
         constexpr int r_cur = us % RS, r_next = (us + 1) % RS;
@@ -322,8 +343,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 __asm__ volatile("" : "+v"(adup[h][s].x), "+v"(adup[h][s].y), "+v"(adup[h][s].z),
                                  "+v"(adup[h][s].w));
         load_a(pq + 1 == spw ? 0 : pq + 1);  // the activations of the next slot
-        if constexpr (us % RS == 0) snext = load_scales();  // and the next period's scales
-        const int s_blk = (16 * (us % RS) + 2 * wave) >> sh;
+        if constexpr (us % P == 0) load_scales(snext);  // and the next period's scales
+        const int s_blk = (16 * (us % P) + 2 * wave) >> sh;
         const int s_pick = sh == 0 ? -1 : (s_blk & 1);
         const float *scs = &scl[qp & 1][j * kScaleStride + (s_blk & ~1)];
         read_scales(scs, s_pick, am[(us * TB) & 1]);
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         // At the end of a period, publish the next period's scales.  The
         // buffer written here was last read in the previous period, which
         // every wave finished before the previous barrier.
-        if constexpr (us % RS == RS - 1) {
+        if constexpr (us % P == P - 1) {
             stage_scales(snext, (qp + 1) & 1);
             lds_barrier();
             ++qp;
@@ -374,8 +395,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // Chunk end: combine the KW partials of the chunk's tiles.  Output (tile,
     // token row) pair p is summed by wave p % KW in wave order (no atomics:
     // the result is deterministic).  The buffer is rewritten at the next
-    // chunk end, after at least one more period barrier (a workgroup with
-    // several chunks has RS = 1: a barrier every slot).  The stores of C sit
+    // chunk end, after at least one more period barrier (every chunk holds
+    // at least one period end).  The stores of C sit
     // outside the unrolled slot loop: a store makes the compiler wait for
     // every outstanding load before the next use of a loaded register, which
     // here happens once per chunk instead of once per slot.
@@ -426,11 +447,17 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // Ring depth TB*RS of about 8 units (8 KiB of weights in flight per wave).
     constexpr int RS = TB == 1 ? 8 : TB == 2 ? 4 : TB <= 4 ? 2 : 1;
     constexpr int UF = (RS * TB) % 2 == 0 ? RS : 2 * RS;
-    // With RS > 1 or an odd TB every workgroup must compute a single chunk (the
-    // ring entry and decode buffer of a chunk's first unit are fixed at compile
-    // time); TB < 8 gives that, since then groups <= CUs.
-    if ((RS > 1 || TB % 2) && groups > G) return hipErrorInvalidValue;
-    fused_mfma_kernel<AT, SR, TB, RS, UF><<<dim3(G), dim3(64 * KW), 0, s>>>(
+    // Scales are staged once per ring period: with one slot (TB >= 5) every
+    // slot, which lets workgroups start their walk at any slot; a barrier
+    // every slot costs more than it gains for shapes of one or two tiles per
+    // chunk (measured), which stage every RS slots.
+    constexpr int P = RS;
+    // The ring entry and decode buffer of a chunk's first unit are fixed at
+    // compile time: a workgroup with several chunks needs chunks of whole
+    // loop iterations.
+    const int spw = ((K + 127) / 128 + KW - 1) / KW;
+    if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
+    fused_mfma_kernel<AT, SR, TB, RS, UF, P><<<dim3(G), dim3(64 * KW), 0, s>>>(
         A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt);
     return hipGetLastError();
 }
