@@ -92,8 +92,12 @@ def _torch():
 
 
 def _stream(t):
+    """Raw handle of torch's current stream on t's device."""
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _dtype_code(dtype):
@@ -107,6 +111,12 @@ def _dtype_code(dtype):
 
 
 def _dev(t, name, dtype):
+    """Device pointer of a contiguous GPU tensor of dtype (raises otherwise)."""
+    try:
+        if t.is_cuda and t.dtype is dtype and t.is_contiguous():
+            return t.data_ptr()
+    except AttributeError:
+        pass
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -114,9 +124,7 @@ def _dev(t, name, dtype):
         raise ValueError("%s must be on a GPU" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    return ctypes.c_void_p(t.data_ptr())
+    raise ValueError("%s must be contiguous" % name)
 
 
 def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, path: str = "auto",
