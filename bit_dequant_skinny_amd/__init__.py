@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4skinny
 Q4_OK, Q4_ERR_INVALID_ARGUMENT, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = 0, 1, 2, 3
 Q4_DTYPE_BF16, Q4_DTYPE_FP32, Q4_DTYPE_FP16 = 0, 1, 2
 PATHS = {"auto": 0, "fused": 1, "split": 2}
-FUSED_PASS_M = 16
+FUSED_PASS_M = 32
 CROSSOVER_MAX = 65536
 
 # Every symbol include/q4skinny.h declares.

@@ -29,7 +29,7 @@ namespace {
 // Fused-versus-split threshold on MI355X (fused when M <= value).  Timed on
 // the decode layer shapes (K, N) = (5120, 8192), (5120, 5120), (17408, 5120),
 // (8192, 8192), the 28672 x 8192 FFN, the 4096 x 4096 GEMV and the 248320 x
-// 2560 output projection at M = 16 .. 256: the fused kernel in 16-row passes
+// 2560 output projection at M = 16 .. 256: the fused kernel in row passes
 // beats dequantize + GEMM at every point (1.1x to 7x), so by default every M
 // takes the fused path and the split path runs only when forced or when the
 // crossover is lowered.

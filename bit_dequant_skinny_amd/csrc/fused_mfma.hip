@@ -95,8 +95,9 @@ constexpr int KW = 8;  // waves per workgroup
 // loads in flight.  UF: slots per loop iteration, a multiple of RS with UF*TB
 // even, which makes the ring entry and the decode double-buffer index of
 // every unit compile-time constants.  P: slots per scale-staging period (a
-// divisor of UF).
-template <int AT, int SR, int TB, int RS, int UF, int P>
+// divisor of UF).  MB: blocks of 16 token rows per pass (1, or 2 for up to 32
+// tokens): the decoded weights of a unit feed the MFMAs of every block.
+template <int AT, int SR, int TB, int RS, int UF, int P, int MB>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
@@ -105,7 +106,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     static_assert(AT == kBf16 || AT == kF16, "bf16 or fp16 activations");
     constexpr int NA = AT == kF16 ? 2 : 1;  // bf16 terms per activation
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
-    static_assert(64 * KW >= 256, "one table entry per thread");
+    static_assert(64 * KW == 512, "two threads per table entry");
+    static_assert(MB == 1 || (MB == 2 && SR == 4 && AT == kBf16), "two blocks of full bf16 rows");
     __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
     __shared__ float red[KW][TB * SR][64];
     // Raw block scales of the current and the next period of P slots, one
@@ -241,14 +243,18 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // takes an offset past every buffer: both read zeros without touching
     // memory, which cancels whatever codes sit there.
     const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;  // past the end of A for j >= M
-    uint4 anext[4];
+    uint4 anext[MB][4];
     auto load_a = [&](int q) {
         const uint32_t kk = ((uint32_t)wave + (uint32_t)((q + rot) % spw) * KW) * 128;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t k = kk + k_offset(g, t);
-            const uint32_t off = k < (uint32_t)K ? a_row + k * 2 : kPastEnd;
-            anext[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)off, 0, 0));
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const uint32_t off = k < (uint32_t)K ? a_row + (uint32_t)(16 * b) * (uint32_t)K * 2 + k * 2
+                                                     : kPastEnd;
+                anext[b][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)off, 0, 0));
+            }
         }
     };
 
@@ -283,25 +289,37 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             for (int tr = 0; tr < TB; ++tr) issue(wbuf[r][tr], tr);
             w_advance();
         }
-        if (tid < 256) {
+        {
+            // Threads t and t + 256 write entry t & 255 into 16 copies each.
+            // Lane l of a wave starts at copy l % 32, so the 32 lanes of a
+            // half-wave write 32 different bank pairs (writing copy c from
+            // every lane at once would put all 64 lanes on one bank pair).
             const uint2 v = pair_table_entry(cb0, cb1);
-#pragma unroll 8
-            for (int c = 0; c < 32; ++c) table[e_tab * 32 + c] = v;
+            const int c0 = (tid >> 8) * 16 + e_tab;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) table[e_tab * 32 + ((c0 + c) & 31)] = v;
         }
         stage_scales(s0, 0);
         lds_barrier();
     }
-    uint2 e[2][16];
+    // Decoded units: double-buffered with one token block, so the table
+    // reads of the next unit fly while this unit's MFMAs run; with two
+    // blocks the 16 MFMAs of a unit cover that latency and the registers go
+    // to the second block's activations.
+    constexpr int DB = MB == 1 ? 2 : 1;
+    uint2 e[DB][16];
     float am[2][2];
     decode(wbuf[0][0], e[0]);
     issue(wbuf[0][0], 0);
 
     const floatx4 zerof = floatx4{0.f, 0.f, 0.f, 0.f};
-    float acc[TB][SR];
+    float acc[TB][MB][SR];
 #pragma unroll
     for (int tr = 0; tr < TB; ++tr)
 #pragma unroll
-        for (int r = 0; r < SR; ++r) acc[tr][r] = 0.f;
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int r = 0; r < SR; ++r) acc[tr][b][r] = 0.f;
     int pq = 0;   // the slot being computed
     int qp = 0;   // periods done, for the staging buffer parity
     floatx4 snext[SP];  // the next period's scale pieces
@@ -321,27 +339,32 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         // and pinned in registers: an MFMA whose operand a VALU instruction has
         // just written stalls for the hazard, so the compiler must not rebuild
         // these next to every MFMA.
-        uint4 adup[NA][8];
+        uint4 adup[MB][NA][8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if constexpr (AT == kBf16) {
-                adup[0][2 * t] = make_uint4(anext[t].x, anext[t].x, anext[t].y, anext[t].y);
-                adup[0][2 * t + 1] = make_uint4(anext[t].z, anext[t].z, anext[t].w, anext[t].w);
-            } else {
-                const uint2 x = f16x2_to_bf16_hilo(anext[t].x), y = f16x2_to_bf16_hilo(anext[t].y);
-                const uint2 z = f16x2_to_bf16_hilo(anext[t].z), w = f16x2_to_bf16_hilo(anext[t].w);
-                adup[0][2 * t] = make_uint4(x.x, x.x, y.x, y.x);
-                adup[0][2 * t + 1] = make_uint4(z.x, z.x, w.x, w.x);
-                adup[NA - 1][2 * t] = make_uint4(x.y, x.y, y.y, y.y);
-                adup[NA - 1][2 * t + 1] = make_uint4(z.y, z.y, w.y, w.y);
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint4 &an = anext[b][t];
+                if constexpr (AT == kBf16) {
+                    adup[b][0][2 * t] = make_uint4(an.x, an.x, an.y, an.y);
+                    adup[b][0][2 * t + 1] = make_uint4(an.z, an.z, an.w, an.w);
+                } else {
+                    const uint2 x = f16x2_to_bf16_hilo(an.x), y = f16x2_to_bf16_hilo(an.y);
+                    const uint2 z = f16x2_to_bf16_hilo(an.z), w = f16x2_to_bf16_hilo(an.w);
+                    adup[b][0][2 * t] = make_uint4(x.x, x.x, y.x, y.x);
+                    adup[b][0][2 * t + 1] = make_uint4(z.x, z.x, w.x, w.x);
+                    adup[b][NA - 1][2 * t] = make_uint4(x.y, x.y, y.y, y.y);
+                    adup[b][NA - 1][2 * t + 1] = make_uint4(z.y, z.y, w.y, w.y);
+                }
             }
-        }
 #pragma unroll
-        for (int h = 0; h < NA; ++h)
+        for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
-                __asm__ volatile("" : "+v"(adup[h][s].x), "+v"(adup[h][s].y), "+v"(adup[h][s].z),
-                                 "+v"(adup[h][s].w));
+            for (int h = 0; h < NA; ++h)
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    __asm__ volatile("" : "+v"(adup[b][h][s].x), "+v"(adup[b][h][s].y),
+                                     "+v"(adup[b][h][s].z), "+v"(adup[b][h][s].w));
         load_a(pq + 1 == spw ? 0 : pq + 1);  // the activations of the next slot
         if constexpr (us % P == 0) load_scales(snext);  // and the next period's scales
         const int s_blk = (16 * (us % P) + 2 * wave) >> sh;
@@ -351,35 +374,42 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
 #pragma unroll
         for (int tr = 0; tr < TB; ++tr) {
             const int cur = (us * TB + tr) & 1;
-            const uint2 *ev = e[cur];
-            // two independent chains, one per 64-wide block
-            floatx4 D0 = zerof, D1 = zerof;
+            const int ecur = DB == 2 ? cur : 0, enext = DB == 2 ? cur ^ 1 : 0;
+            const uint2 *ev = e[ecur];
+            // two independent chains per token block, one per 64-wide block
+            floatx4 D0[MB], D1[MB];
+#pragma unroll
+            for (int b = 0; b < MB; ++b) D0[b] = D1[b] = zerof;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
                 const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
 #pragma unroll
-                for (int h = 0; h < NA; ++h) {
-                    D0 = mfma_bf16_16x16x32(as_bf16x8(adup[h][s]), as_bf16x8(b0), D0);
-                    D1 = mfma_bf16_16x16x32(as_bf16x8(adup[h][4 + s]), as_bf16x8(b1), D1);
-                }
+                for (int b = 0; b < MB; ++b)
+#pragma unroll
+                    for (int h = 0; h < NA; ++h) {
+                        D0[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][h][s]), as_bf16x8(b0), D0[b]);
+                        D1[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][h][4 + s]), as_bf16x8(b1), D1[b]);
+                    }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (tr + 1 < TB) {
-                decode(wbuf[r_cur][tr + 1], e[cur ^ 1]);
+                decode(wbuf[r_cur][tr + 1], e[enext]);
                 read_scales(scs + (tr + 1) * 16 * kScaleStride, s_pick, am[cur ^ 1]);
                 issue(wbuf[r_cur][tr + 1], tr + 1);
             } else {
                 // tile 0 of the next slot: its weights are in the ring; its
                 // scales are read at the start of that slot
                 w_advance();
-                decode(wbuf[r_next][0], e[cur ^ 1]);
+                decode(wbuf[r_next][0], e[enext]);
                 issue(wbuf[r_next][0], 0);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < SR; ++r)
-                acc[tr][r] = fmaf(am[cur][1], D1[r], fmaf(am[cur][0], D0[r], acc[tr][r]));
+            for (int b = 0; b < MB; ++b)
+#pragma unroll
+                for (int r = 0; r < SR; ++r)
+                    acc[tr][b][r] = fmaf(am[cur][1], D1[b][r], fmaf(am[cur][0], D0[b][r], acc[tr][b][r]));
         }
         // At the end of a period, publish the next period's scales.  The
         // buffer written here was last read in the previous period, which
@@ -411,28 +441,34 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             if constexpr (UF > 6) { if (q0 + 6 < spw) slot(std::integral_constant<int, 6 % UF>{}); }
             if constexpr (UF > 7) { if (q0 + 7 < spw) slot(std::integral_constant<int, 7 % UF>{}); }
         }
-#pragma unroll
-        for (int tr = 0; tr < TB; ++tr)
-#pragma unroll
-            for (int r = 0; r < SR; ++r) {
-                red[wave][tr * SR + r][lane] = acc[tr][r];
-                acc[tr][r] = 0.f;
-            }
-        lds_barrier();
         const uint32_t grp = group_of(pc);
 #pragma unroll
-        for (int p0 = 0; p0 < TB * SR; p0 += KW) {
-            const int p = p0 + wave;
-            if (p < TB * SR) {
-                const int tr = p / SR, r = p % SR;
-                float v = red[0][p][lane];
+        for (int b = 0; b < MB; ++b) {
+            // token block b reuses the buffer: wait until every wave has read
+            // block b - 1
+            if (b > 0) lds_barrier();
 #pragma unroll
-                for (int w2 = 1; w2 < KW; ++w2) v += red[w2][p][lane];
-                const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
-                const int tok = 4 * g + r;
-                if (n < N && tok < M) {
-                    if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
-                    store_elem(C, (size_t)tok * N + n, v, c_dt);
+            for (int tr = 0; tr < TB; ++tr)
+#pragma unroll
+                for (int r = 0; r < SR; ++r) {
+                    red[wave][tr * SR + r][lane] = acc[tr][b][r];
+                    acc[tr][b][r] = 0.f;
+                }
+            lds_barrier();
+#pragma unroll
+            for (int p0 = 0; p0 < TB * SR; p0 += KW) {
+                const int p = p0 + wave;
+                if (p < TB * SR) {
+                    const int tr = p / SR, r = p % SR;
+                    float v = red[0][p][lane];
+#pragma unroll
+                    for (int w2 = 1; w2 < KW; ++w2) v += red[w2][p][lane];
+                    const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
+                    const int tok = 16 * b + 4 * g + r;
+                    if (n < N && tok < M) {
+                        if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
+                        store_elem(C, (size_t)tok * N + n, v, c_dt);
+                    }
                 }
             }
         }
@@ -440,7 +476,15 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     }
 }
 
-template <int AT, int SR, int TB>
+// Tiles per chunk: the tiles each CU must cover, at most 8.
+int tiles_per_chunk(int N) {
+    const int tiles = (N + 15) / 16;
+    const int cus = device_info().num_cus;
+    const int tb = (tiles + cus - 1) / cus;
+    return tb > 8 ? 8 : tb;
+}
+
+template <int AT, int SR, int MB, int TB>
 hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
                      void *C, int c_dt, int groups, int G, hipStream_t s) {
@@ -457,12 +501,12 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // loop iterations.
     const int spw = ((K + 127) / 128 + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
-    fused_mfma_kernel<AT, SR, TB, RS, UF, P><<<dim3(G), dim3(64 * KW), 0, s>>>(
+    fused_mfma_kernel<AT, SR, TB, RS, UF, P, MB><<<dim3(G), dim3(64 * KW), 0, s>>>(
         A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt);
     return hipGetLastError();
 }
 
-template <int AT, int SR>
+template <int AT, int SR, int MB>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
                      void *C, int c_dt, hipStream_t s) {
@@ -470,22 +514,24 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // TB = the tiles each CU must cover, up to 8, so that every chunk but the
     // last holds TB live tiles; a workgroup loops over ceil(groups / CUs)
     // chunks.
+    const int tb = tiles_per_chunk(N);
     const int tiles = (N + 15) / 16;
     const int cus = device_info().num_cus;
-    int tb = (tiles + cus - 1) / cus;
-    if (tb > 8) tb = 8;
     const int groups = (tiles + tb - 1) / tb;
     const int G = groups < cus ? groups : cus;
+#define Q4_LAUNCH_TB(T) \
+    return launch_tb<AT, SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s)
     switch (tb) {
-    case 1: return launch_tb<AT, SR, 1>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    case 2: return launch_tb<AT, SR, 2>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    case 3: return launch_tb<AT, SR, 3>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    case 4: return launch_tb<AT, SR, 4>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    case 5: return launch_tb<AT, SR, 5>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    case 6: return launch_tb<AT, SR, 6>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    case 7: return launch_tb<AT, SR, 7>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
-    default: return launch_tb<AT, SR, 8>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s);
+    case 1: Q4_LAUNCH_TB(1);
+    case 2: Q4_LAUNCH_TB(2);
+    case 3: Q4_LAUNCH_TB(3);
+    case 4: Q4_LAUNCH_TB(4);
+    case 5: Q4_LAUNCH_TB(5);
+    case 6: Q4_LAUNCH_TB(6);
+    case 7: Q4_LAUNCH_TB(7);
+    default: Q4_LAUNCH_TB(8);
     }
+#undef Q4_LAUNCH_TB
 }
 
 }  // namespace
@@ -493,12 +539,12 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
 // The kernel's byte offsets are 32-bit.  Weight and scale offsets reach the
 // rows of the last tile group, at most 8 tiles (128 rows) past the last row,
 // so the matrix plus 256 rows must stay below 4 GiB; activation offsets reach
-// 16 rows of K (the lanes of absent tokens read past the end of A), which must
+// 32 rows of K (the lanes of absent tokens read past the end of A), which must
 // stay below 4 GiB as well.
 bool q4_fused_mfma_fits(int M, int N, int K) {
     (void)M;
     return ((uint64_t)N + 256) * (uint64_t)K / 2 < (1ull << 32) &&
-           16ull * (uint64_t)K * 2 < (1ull << 32);
+           32ull * (uint64_t)K * 2 < (1ull << 32);
 }
 
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
@@ -506,24 +552,48 @@ hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt,
                                 hipStream_t s) {
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
+#define Q4_LAUNCH_SR(T, R, B) \
+    return launch_sr<T, R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s)
     if (a_dt == kF16) {
-        if (M <= 1) return launch_sr<kF16, 1>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
-        if (M <= 2) return launch_sr<kF16, 2>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
-        return launch_sr<kF16, 4>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+        if (M > 16) return hipErrorInvalidValue;
+        if (M <= 1) Q4_LAUNCH_SR(kF16, 1, 1);
+        if (M <= 2) Q4_LAUNCH_SR(kF16, 2, 1);
+        Q4_LAUNCH_SR(kF16, 4, 1);
     }
-    if (M <= 1) return launch_sr<kBf16, 1>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
-    if (M <= 2) return launch_sr<kBf16, 2>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
-    return launch_sr<kBf16, 4>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (M > 32) return hipErrorInvalidValue;
+    if (M <= 1) Q4_LAUNCH_SR(kBf16, 1, 1);
+    if (M <= 2) Q4_LAUNCH_SR(kBf16, 2, 1);
+    if (M <= 16) Q4_LAUNCH_SR(kBf16, 4, 1);
+    Q4_LAUNCH_SR(kBf16, 4, 2);
+#undef Q4_LAUNCH_SR
 }
 
+// Up to Q4_FUSED_PASS_M (32) token rows: bf16 activations on the matrix cores
+// in one pass (two token blocks), except where a chunk holds 8 tiles: there
+// the second block's registers spill and two 16-row passes are faster
+// (measured at 248320 x 2560).  fp16 activations, fp32 activations and
+// blocksize 32 run in passes of 16 rows.
 hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, const void *bias, int M, int N, int K,
                            int bs_log2, void *C, int c_dt, hipStream_t s) {
-    if (a_dt != kF32 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K))
+    const bool mfma = a_dt != kF32 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K);
+    if (mfma && a_dt == kBf16 && (M <= 16 || tiles_per_chunk(N) < 8))
         return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
                                     C, c_dt, s);
-    return launch_q4_fused_simt(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C,
-                                c_dt, s);
+    const size_t a_row = (size_t)K * (a_dt == kF32 ? 4 : 2);
+    const size_t c_row = (size_t)N * (c_dt == kF32 ? 4 : 2);
+    for (int m0 = 0; m0 < M; m0 += 16) {
+        const int mm = M - m0 < 16 ? M - m0 : 16;
+        const void *Am = static_cast<const char *>(A) + (size_t)m0 * a_row;
+        void *Cm = static_cast<char *>(C) + (size_t)m0 * c_row;
+        const hipError_t e =
+            mfma ? launch_q4_fused_mfma(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
+                                        Cm, c_dt, s)
+                 : launch_q4_fused_simt(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
+                                        Cm, c_dt, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q4

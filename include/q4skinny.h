@@ -50,8 +50,10 @@ enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
 
 /* Token rows one fused 4-bit pass handles; the fused path runs larger M in
  * passes over slabs of this many rows, each pass streaming the packed weights
- * again. */
-#define Q4_FUSED_PASS_M 16
+ * again.  (A pass of bf16 activations runs as one launch; other element
+ * types, blocksize 32 and matrices of more than 2048 * 16 rows per 256 CUs
+ * run a pass as launches of 16 rows.) */
+#define Q4_FUSED_PASS_M 32
 /* Largest crossover value q4_set_crossover_m accepts. */
 #define Q4_CROSSOVER_MAX 65536
 
