@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/q4skinny.h):
   q4_quantize(W, codebook, blocksize=64, out=None)   codebook: host sequence of 16 floats
   q4_codebook_preset(name)   "nf4_style" or "int4" -> numpy float32 [16]
   q4_get_crossover_m() / q4_set_crossover_m(m) / q4_release_workspace()
+  q4_set_crossover_shape(N, K, m) / q4_get_crossover_shape(N, K) / q4_clear_crossover_shapes()
   q4_copy_probe(src, dst) / q4_version()
 ``lib()`` returns the raw ctypes handle for callers that pass pointers.
 """
@@ -34,6 +35,7 @@ EXPORTS = (
     "q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex", "bf16_gemm_skinny", "q4_dequant",
     "q4_get_crossover_m", "q4_set_crossover_m", "q4_release_workspace", "q4_last_error",
     "q4_copy_probe", "q4_version", "q4_quantize", "q4_codebook_preset",
+    "q4_set_crossover_shape", "q4_get_crossover_shape", "q4_clear_crossover_shapes",
 )
 PRESETS = {"nf4_style": 0, "int4": 1}
 
@@ -69,10 +71,14 @@ def lib():
         L.q4_set_crossover_m.argtypes = [I]
         L.q4_quantize.argtypes = [P, I, P, I, I, I, P, P, P]
         L.q4_codebook_preset.argtypes = [I, P]
+        L.q4_set_crossover_shape.argtypes = [I, I, I]
+        L.q4_get_crossover_shape.argtypes = [I, I]
+        L.q4_get_crossover_shape.restype = ctypes.c_int
         for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
                      "bf16_gemm_skinny", "q4_dequant",
                      "q4_copy_probe", "q4_set_crossover_m", "q4_release_workspace",
-                     "q4_quantize", "q4_codebook_preset"):
+                     "q4_quantize", "q4_codebook_preset", "q4_set_crossover_shape",
+                     "q4_clear_crossover_shapes"):
             getattr(L, name).restype = ctypes.c_int
         L.q4_get_crossover_m.restype = ctypes.c_int
         L.q4_last_error.restype = ctypes.c_char_p
@@ -221,6 +227,19 @@ def q4_get_crossover_m() -> int:
 
 def q4_set_crossover_m(m: int) -> None:
     _check(lib().q4_set_crossover_m(int(m)))
+
+
+def q4_set_crossover_shape(N: int, K: int, m: int) -> None:
+    """Crossover for weight shape (N, K); m < 0 removes the entry."""
+    _check(lib().q4_set_crossover_shape(int(N), int(K), int(m)))
+
+
+def q4_get_crossover_shape(N: int, K: int) -> int:
+    return int(lib().q4_get_crossover_shape(int(N), int(K)))
+
+
+def q4_clear_crossover_shapes() -> None:
+    _check(lib().q4_clear_crossover_shapes())
 
 
 def q4_release_workspace() -> None:

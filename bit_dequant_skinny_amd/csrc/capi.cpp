@@ -14,6 +14,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -106,6 +107,41 @@ int crossover() {
     int expected = -1;
     g_crossover.compare_exchange_strong(expected, init);
     return g_crossover.load();
+}
+
+// Per-shape crossovers: an entry for (N, K) overrides the process-wide value
+// for that weight shape.  The table starts from the environment variable
+// Q4_CROSSOVER_TABLE ("N:K:m" items separated by commas) at first use; a
+// malformed item is skipped.
+std::mutex g_shape_mutex;
+std::map<std::pair<int, int>, int> g_shape_crossover;
+bool g_shape_loaded = false;
+
+void load_shape_table_locked() {
+    if (g_shape_loaded) return;
+    g_shape_loaded = true;
+    const char *e = std::getenv("Q4_CROSSOVER_TABLE");
+    if (!e) return;
+    const std::string text(e);
+    size_t pos = 0;
+    while (pos <= text.size()) {
+        size_t end = text.find(',', pos);
+        if (end == std::string::npos) end = text.size();
+        const std::string item = text.substr(pos, end - pos);
+        long n = 0, k = 0, m = 0;
+        char extra = 0;
+        if (std::sscanf(item.c_str(), "%ld:%ld:%ld%c", &n, &k, &m, &extra) == 3 && n > 0 &&
+            k > 0 && n <= INT32_MAX && k <= INT32_MAX && m >= 0 && m <= Q4_CROSSOVER_MAX)
+            g_shape_crossover[{(int)n, (int)k}] = (int)m;
+        pos = end + 1;
+    }
+}
+
+int crossover_for(int N, int K) {
+    std::lock_guard<std::mutex> lock(g_shape_mutex);
+    load_shape_table_locked();
+    const auto it = g_shape_crossover.find({N, K});
+    return it != g_shape_crossover.end() ? it->second : crossover();
 }
 
 // ---- split-path workspace: one buffer per (device, stream) ------------------
@@ -257,7 +293,7 @@ q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
     bool fused;
     if (path == Q4_PATH_FUSED) fused = true;
     else if (path == Q4_PATH_SPLIT) fused = false;
-    else fused = M <= crossover();
+    else fused = M <= crossover_for(N, K);
     if (!fused && a_dtype == Q4_DTYPE_FP32)
         return fail(Q4_ERR_UNSUPPORTED, "fp32 activations take the fused path only (M=%d)", M);
     if (M == 0 || N == 0) return ok();
@@ -411,6 +447,27 @@ q4_status q4_set_crossover_m(int m) {
     if (m < 0 || m > Q4_CROSSOVER_MAX)
         return fail(Q4_ERR_INVALID_ARGUMENT, "crossover %d not in 0..%d", m, Q4_CROSSOVER_MAX);
     g_crossover.store(m);
+    return ok();
+}
+
+q4_status q4_set_crossover_shape(int N, int K, int m) {
+    if (N <= 0 || K <= 0)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "shape N=%d K=%d must be positive", N, K);
+    if (m > Q4_CROSSOVER_MAX)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "crossover %d above %d", m, Q4_CROSSOVER_MAX);
+    std::lock_guard<std::mutex> lock(g_shape_mutex);
+    load_shape_table_locked();
+    if (m < 0) g_shape_crossover.erase({N, K});
+    else g_shape_crossover[{N, K}] = m;
+    return ok();
+}
+
+int q4_get_crossover_shape(int N, int K) { return crossover_for(N, K); }
+
+q4_status q4_clear_crossover_shapes(void) {
+    std::lock_guard<std::mutex> lock(g_shape_mutex);
+    g_shape_loaded = true;  // the environment's table is not read again
+    g_shape_crossover.clear();
     return ok();
 }
 

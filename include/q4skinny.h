@@ -224,6 +224,28 @@ q4_status q4_codebook_preset(int which, float *codebook);
 int q4_get_crossover_m(void);
 q4_status q4_set_crossover_m(int m);
 
+/*
+ * Per-shape crossovers: the crossover can be set for one weight shape (N
+ * rows, K columns), which then overrides the process-wide value for calls
+ * with that shape; the pull request above tunes its threshold per GPU and
+ * notes that the best switch point depends on the problem (section "Fused
+ * path support for M > 1" and the crossover table), and measured per-shape
+ * values on MI355X can be recorded here.  The table starts from the
+ * environment variable Q4_CROSSOVER_TABLE at first use: comma-separated
+ * "N:K:m" items (malformed items are skipped).
+ *  q4_set_crossover_shape   m in 0..Q4_CROSSOVER_MAX sets the entry, m < 0
+ *                           removes it; Q4_ERR_INVALID_ARGUMENT for N <= 0,
+ *                           K <= 0 or m > Q4_CROSSOVER_MAX.
+ *  q4_get_crossover_shape   the crossover calls of shape (N, K) use: the
+ *                           entry if present, else q4_get_crossover_m().
+ *  q4_clear_crossover_shapes removes every entry (the environment's table is
+ *                           not read again).
+ * Thread-safe (one mutex); a change applies to calls made after it returns.
+ */
+q4_status q4_set_crossover_shape(int N, int K, int m);
+int q4_get_crossover_shape(int N, int K);
+q4_status q4_clear_crossover_shapes(void);
+
 /* Frees the split-path workspaces of every device and stream (synchronises
  * the devices that own them).  Safe to call at any time between calls. */
 q4_status q4_release_workspace(void);

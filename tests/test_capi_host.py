@@ -140,6 +140,40 @@ def test_crossover_env_override():
     assert r.returncode == 0 and int(r.stdout.strip()) == q4.q4_get_crossover_m()
 
 
+def test_crossover_shape_table():
+    L = q4.lib()
+    q4.q4_clear_crossover_shapes()
+    base = q4.q4_get_crossover_m()
+    assert L.q4_set_crossover_shape(0, 64, 4) == INV
+    assert L.q4_set_crossover_shape(64, -1, 4) == INV
+    assert L.q4_set_crossover_shape(64, 128, q4.CROSSOVER_MAX + 1) == INV
+    try:
+        q4.q4_set_crossover_shape(4096, 4096, 8)
+        q4.q4_set_crossover_shape(5120, 8192, 0)
+        assert q4.q4_get_crossover_shape(4096, 4096) == 8
+        assert q4.q4_get_crossover_shape(5120, 8192) == 0
+        assert q4.q4_get_crossover_shape(8192, 5120) == base  # (N, K) is ordered
+        q4.q4_set_crossover_m(3)
+        assert q4.q4_get_crossover_shape(4096, 4096) == 8     # the entry wins
+        assert q4.q4_get_crossover_shape(100, 100) == 3       # no entry: global
+        q4.q4_set_crossover_shape(4096, 4096, -1)              # removes it
+        assert q4.q4_get_crossover_shape(4096, 4096) == 3
+    finally:
+        q4.q4_set_crossover_m(base)
+        q4.q4_clear_crossover_shapes()
+    assert q4.q4_get_crossover_shape(5120, 8192) == base
+
+
+def test_crossover_shape_table_from_environment():
+    code = ("import bit_dequant_skinny_amd as q; "
+            "print(q.q4_get_crossover_shape(4096, 4096), q.q4_get_crossover_shape(64, 128), "
+            "q.q4_get_crossover_shape(7, 7), q.q4_get_crossover_m())")
+    r = _in_subprocess(code, {"Q4_CROSSOVER_TABLE": "4096:4096:12, bad,64:128:0,7:7:-2,5:5:5x",
+                              "Q4_CROSSOVER_M": "9"})
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["12", "0", "9", "9"]
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     A = torch.zeros(1, 128, dtype=torch.bfloat16)

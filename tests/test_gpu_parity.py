@@ -190,6 +190,29 @@ def test_auto_path_follows_crossover():
     assert np.array_equal(Ca, Cs) and np.array_equal(Cb, Cf)
 
 
+def test_auto_path_follows_per_shape_crossover():
+    """A per-shape entry routes that shape alone; other shapes keep the
+    process-wide crossover."""
+    M, bs = 8, 64
+    pa = synth.q4_problem(M, 64, 512, bs, config=59, shape=0)
+    pb = synth.q4_problem(M, 48, 512, bs, config=59, shape=1)
+    da, db = q4_to_dev(pa), q4_to_dev(pb)
+    q4.q4_clear_crossover_shapes()
+    try:
+        q4.q4_set_crossover_shape(64, 512, 4)
+        Ca = bf16_host(q4.q4_gemm_skinny(*da, bs))
+        Cb = bf16_host(q4.q4_gemm_skinny(*db, bs))
+        Cas = bf16_host(q4.q4_gemm_skinny(*da, bs, path="split"))
+        Cbf = bf16_host(q4.q4_gemm_skinny(*db, bs, path="fused"))
+    finally:
+        q4.q4_clear_crossover_shapes()
+    Caf = bf16_host(q4.q4_gemm_skinny(*da, bs))
+    Ca_fused = bf16_host(q4.q4_gemm_skinny(*da, bs, path="fused"))
+    _sync()
+    assert np.array_equal(Ca, Cas) and np.array_equal(Cb, Cbf)
+    assert np.array_equal(Caf, Ca_fused)
+
+
 def test_empty_shapes_leave_output_untouched():
     t = torch()
     d = dev()
