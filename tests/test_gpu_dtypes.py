@@ -144,3 +144,39 @@ def test_dequant_f16_overflow_and_subnormals():
     t.cuda.synchronize()
     ref = oracle.dequant_f16(Wp, am, cb, N, K, bs)
     assert np.array_equal(w.cpu().view(t.int16).numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("M", [1, 8, 11])
+def test_fp32_activations_wide_exponent_range(M):
+    """fp32 activations with full 24-bit significands over 2^-60 .. 2^60 take
+    the matrix-core route as three exact bf16 planes."""
+    N, K, bs = 70, 512, 64
+    p = synth.q4_problem(M, N, K, bs, config=67, codebook=synth.random_codebook(81))
+    g = synth.rng(82)
+    mant = 1.0 + g.integers(0, 1 << 23, size=(M, K)) / float(1 << 23)
+    A_h = (np.where(g.random((M, K)) < 0.5, -1.0, 1.0) * mant *
+           np.exp2(g.integers(-60, 61, size=(M, K)))).astype(np.float32)
+    _, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(to_dev(A_h, "f32"), Wp, am, cb, bs, out_dtype=torch().float32)
+    torch().cuda.synchronize()
+    Cr, S = oracle.q4_gemm_ex(A_h, "fp32", p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(None, Cr, S, "fp32 wide range", out="fp32", values=host_f64(C))
+
+
+def test_fp32_activations_near_the_largest_float():
+    """Activations a few ulps below FLT_MAX split without overflow."""
+    M, N, K, bs = 2, 40, 128, 64
+    p = synth.q4_problem(M, N, K, bs, config=68)
+    A_h = np.zeros((M, K), np.float32)
+    big = np.finfo(np.float32).max
+    A_h[0, 3] = big
+    A_h[0, 77] = -np.nextafter(big, 0, dtype=np.float32)
+    A_h[1, 10] = np.float32(3.3961e38)
+    A_h[1, 100] = np.float32(1.5)
+    _, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(to_dev(A_h, "f32"), Wp, am, cb, bs, out_dtype=torch().float32)
+    torch().cuda.synchronize()
+    Cr, S = oracle.q4_gemm_ex(A_h, "fp32", p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    got = host_f64(C)
+    assert np.all(np.isfinite(got))
+    assert_within_tolerance(None, Cr, S, "fp32 near max", out="fp32", values=got)
