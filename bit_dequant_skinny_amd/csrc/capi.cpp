@@ -210,9 +210,9 @@ q4_status drain_prior_error() {
 bool known_dtype(int dt) { return dt == Q4_DTYPE_BF16 || dt == Q4_DTYPE_FP16 || dt == Q4_DTYPE_FP32; }
 size_t dtype_size(int dt) { return dt == Q4_DTYPE_FP32 ? 4 : 2; }
 
-q4_status run_fused_f32_planes(const float *A, const uint8_t *Wp, const float *am,
-                               const float *cb, const void *bias, int M, int N, int K,
-                               int bs_log2, void *C, int c_dt, hipStream_t s);
+q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const float *am,
+                           const float *cb, const void *bias, int M, int N, int K, int bs_log2,
+                           void *C, int c_dt, hipStream_t s);
 
 // The fused kernels take up to Q4_FUSED_PASS_M token rows per pass; larger M
 // runs in passes over consecutive row slabs, each streaming the packed
@@ -220,9 +220,8 @@ q4_status run_fused_f32_planes(const float *A, const uint8_t *Wp, const float *a
 q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
                     const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
                     hipStream_t s) {
-    if (a_dt == Q4_DTYPE_FP32 && bs_log2 >= 6 && q4::q4_fused_mfma_fits(M, N, K))
-        return run_fused_f32_planes(static_cast<const float *>(A), Wp, am, cb, bias, M, N, K,
-                                    bs_log2, C, c_dt, s);
+    if (a_dt != Q4_DTYPE_BF16 && bs_log2 >= 6 && q4::q4_fused_mfma_fits(M, N, K))
+        return run_fused_planes(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, C, c_dt, s);
     const size_t a_row = (size_t)K * dtype_size(a_dt), c_row = (size_t)N * dtype_size(c_dt);
     for (int m0 = 0; m0 < M; m0 += Q4_FUSED_PASS_M) {
         const int mm = M - m0 < Q4_FUSED_PASS_M ? M - m0 : Q4_FUSED_PASS_M;
@@ -235,33 +234,35 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
     return Q4_OK;
 }
 
-// fp32 activations with blocksize >= 64: the exact three-plane bf16 split of
-// each activation row (f32_planes.hip) runs through the matrix-core kernel as
-// 3M bf16 rows with fp32 partial outputs, then one pass sums the three
-// partials of each output, adds the bias and rounds once.  Planes and
-// partials live in the per-stream workspace.
-q4_status run_fused_f32_planes(const float *A, const uint8_t *Wp, const float *am,
-                               const float *cb, const void *bias, int M, int N, int K,
-                               int bs_log2, void *C, int c_dt, hipStream_t s) {
+// fp16 / fp32 activations with blocksize >= 64: the exact split of each
+// activation row into 2 / 3 bf16 planes (planes.hip) runs through the
+// matrix-core kernel as np*M bf16 rows with fp32 partial outputs, then one
+// pass sums the partials of each output, adds the bias and rounds once.
+// Planes and partials live in the per-stream workspace.
+q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const float *am,
+                           const float *cb, const void *bias, int M, int N, int K, int bs_log2,
+                           void *C, int c_dt, hipStream_t s) {
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(Q4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     }
-    const size_t plane_bytes = 3 * (size_t)M * (size_t)K * 2;
+    const int np = q4::activation_planes(a_dt);
+    const size_t plane_bytes = (size_t)np * (size_t)M * (size_t)K * 2;
     const size_t part_off = (plane_bytes + 255) & ~(size_t)255;
     void *ws = nullptr;
-    q4_status st = workspace(device, s, part_off + 3 * (size_t)M * (size_t)N * 4, &ws);
+    q4_status st = workspace(device, s, part_off + (size_t)np * (size_t)M * (size_t)N * 4, &ws);
     if (st != Q4_OK) return st;
     uint16_t *planes = static_cast<uint16_t *>(ws);
     float *parts = reinterpret_cast<float *>(static_cast<char *>(ws) + part_off);
-    st = check_launch(q4::launch_split_planes(A, (size_t)M * (size_t)K, planes, s), "planes");
+    st = check_launch(q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s),
+                      "planes");
     if (st != Q4_OK) return st;
-    st = run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, 3 * M, N, K, bs_log2, parts,
+    st = run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, np * M, N, K, bs_log2, parts,
                    Q4_DTYPE_FP32, s);
     if (st != Q4_OK) return st;
-    return check_launch(q4::launch_sum_planes(parts, M, N, bias, C, c_dt, s), "plane sum");
+    return check_launch(q4::launch_sum_planes(parts, np, M, N, bias, C, c_dt, s), "plane sum");
 }
 
 q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,

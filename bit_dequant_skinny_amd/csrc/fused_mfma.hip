@@ -88,8 +88,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 
 constexpr int KW = 8;  // waves per workgroup
 
-// AT: activation type, bf16 (one MFMA per operand pair) or fp16 (split
-// exactly into bf16 hi + lo, two MFMAs).  SR: accumulator rows kept per lane
+// Activations are bf16 (fp16 and fp32 activations reach this kernel as
+// exact bf16 planes).  SR: accumulator rows kept per lane
 // (min(M, 4)).  TB: tiles per chunk.  RS:
 // segment slots the weight ring runs ahead, so every wave keeps TB*RS weight
 // loads in flight.  UF: slots per loop iteration, a multiple of RS with UF*TB
@@ -97,17 +97,15 @@ constexpr int KW = 8;  // waves per workgroup
 // every unit compile-time constants.  P: slots per scale-staging period (a
 // divisor of UF).  MB: blocks of 16 token rows per pass (1, or 2 for up to 32
 // tokens): the decoded weights of a unit feed the MFMAs of every block.
-template <int AT, int SR, int TB, int RS, int UF, int P, int MB>
+template <int SR, int TB, int RS, int UF, int P, int MB>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
     const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups,
     void *__restrict__ C, int c_dt) {
-    static_assert(AT == kBf16 || AT == kF16, "bf16 or fp16 activations");
-    constexpr int NA = AT == kF16 ? 2 : 1;  // bf16 terms per activation
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
     static_assert(64 * KW == 512, "two threads per table entry");
-    static_assert(MB == 1 || (MB == 2 && SR == 4 && AT == kBf16), "two blocks of full bf16 rows");
+    static_assert(MB == 1 || (MB == 2 && SR == 4), "two blocks of full rows");
     __shared__ uint2 table[256 * 32];  // [byte][lane % 32]
     __shared__ float red[KW][TB * SR][64];
     // Raw block scales of the current and the next period of P slots, one
@@ -339,32 +337,21 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         // and pinned in registers: an MFMA whose operand a VALU instruction has
         // just written stalls for the hazard, so the compiler must not rebuild
         // these next to every MFMA.
-        uint4 adup[MB][NA][8];
+        uint4 adup[MB][8];
 #pragma unroll
         for (int b = 0; b < MB; ++b)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const uint4 &an = anext[b][t];
-                if constexpr (AT == kBf16) {
-                    adup[b][0][2 * t] = make_uint4(an.x, an.x, an.y, an.y);
-                    adup[b][0][2 * t + 1] = make_uint4(an.z, an.z, an.w, an.w);
-                } else {
-                    const uint2 x = f16x2_to_bf16_hilo(an.x), y = f16x2_to_bf16_hilo(an.y);
-                    const uint2 z = f16x2_to_bf16_hilo(an.z), w = f16x2_to_bf16_hilo(an.w);
-                    adup[b][0][2 * t] = make_uint4(x.x, x.x, y.x, y.x);
-                    adup[b][0][2 * t + 1] = make_uint4(z.x, z.x, w.x, w.x);
-                    adup[b][NA - 1][2 * t] = make_uint4(x.y, x.y, y.y, y.y);
-                    adup[b][NA - 1][2 * t + 1] = make_uint4(z.y, z.y, w.y, w.y);
-                }
+                adup[b][2 * t] = make_uint4(an.x, an.x, an.y, an.y);
+                adup[b][2 * t + 1] = make_uint4(an.z, an.z, an.w, an.w);
             }
 #pragma unroll
         for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int h = 0; h < NA; ++h)
-#pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    __asm__ volatile("" : "+v"(adup[b][h][s].x), "+v"(adup[b][h][s].y),
-                                     "+v"(adup[b][h][s].z), "+v"(adup[b][h][s].w));
+            for (int s = 0; s < 8; ++s)
+                __asm__ volatile("" : "+v"(adup[b][s].x), "+v"(adup[b][s].y), "+v"(adup[b][s].z),
+                                 "+v"(adup[b][s].w));
         load_a(pq + 1 == spw ? 0 : pq + 1);  // the activations of the next slot
         if constexpr (us % P == 0) load_scales(snext);  // and the next period's scales
         const int s_blk = (16 * (us % P) + 2 * wave) >> sh;
@@ -385,12 +372,10 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
                 const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
 #pragma unroll
-                for (int b = 0; b < MB; ++b)
-#pragma unroll
-                    for (int h = 0; h < NA; ++h) {
-                        D0[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][h][s]), as_bf16x8(b0), D0[b]);
-                        D1[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][h][4 + s]), as_bf16x8(b1), D1[b]);
-                    }
+                for (int b = 0; b < MB; ++b) {
+                    D0[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][s]), as_bf16x8(b0), D0[b]);
+                    D1[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][4 + s]), as_bf16x8(b1), D1[b]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (tr + 1 < TB) {
@@ -484,7 +469,7 @@ int tiles_per_chunk(int N) {
     return tb > 8 ? 8 : tb;
 }
 
-template <int AT, int SR, int MB, int TB>
+template <int SR, int MB, int TB>
 hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
                      void *C, int c_dt, int groups, int G, hipStream_t s) {
@@ -501,12 +486,12 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // loop iterations.
     const int spw = ((K + 127) / 128 + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
-    fused_mfma_kernel<AT, SR, TB, RS, UF, P, MB><<<dim3(G), dim3(64 * KW), 0, s>>>(
+    fused_mfma_kernel<SR, TB, RS, UF, P, MB><<<dim3(G), dim3(64 * KW), 0, s>>>(
         A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt);
     return hipGetLastError();
 }
 
-template <int AT, int SR, int MB>
+template <int SR, int MB>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
                      void *C, int c_dt, hipStream_t s) {
@@ -520,7 +505,7 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     const int groups = (tiles + tb - 1) / tb;
     const int G = groups < cus ? groups : cus;
 #define Q4_LAUNCH_TB(T) \
-    return launch_tb<AT, SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s)
+    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s)
     switch (tb) {
     case 1: Q4_LAUNCH_TB(1);
     case 2: Q4_LAUNCH_TB(2);
@@ -551,33 +536,28 @@ hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt,
                                 hipStream_t s) {
+    if (a_dt != kBf16 || M > 32) return hipErrorInvalidValue;
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
-#define Q4_LAUNCH_SR(T, R, B) \
-    return launch_sr<T, R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s)
-    if (a_dt == kF16) {
-        if (M > 16) return hipErrorInvalidValue;
-        if (M <= 1) Q4_LAUNCH_SR(kF16, 1, 1);
-        if (M <= 2) Q4_LAUNCH_SR(kF16, 2, 1);
-        Q4_LAUNCH_SR(kF16, 4, 1);
-    }
-    if (M > 32) return hipErrorInvalidValue;
-    if (M <= 1) Q4_LAUNCH_SR(kBf16, 1, 1);
-    if (M <= 2) Q4_LAUNCH_SR(kBf16, 2, 1);
-    if (M <= 16) Q4_LAUNCH_SR(kBf16, 4, 1);
-    Q4_LAUNCH_SR(kBf16, 4, 2);
+#define Q4_LAUNCH_SR(R, B) \
+    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s)
+    if (M <= 1) Q4_LAUNCH_SR(1, 1);
+    if (M <= 2) Q4_LAUNCH_SR(2, 1);
+    if (M <= 16) Q4_LAUNCH_SR(4, 1);
+    Q4_LAUNCH_SR(4, 2);
 #undef Q4_LAUNCH_SR
 }
 
-// Up to Q4_FUSED_PASS_M (32) token rows: bf16 activations on the matrix cores
-// in one pass (two token blocks), except where a chunk holds 8 tiles: there
-// the second block's registers spill and two 16-row passes are faster
-// (measured at 248320 x 2560).  fp16 activations, fp32 activations and
-// blocksize 32 run in passes of 16 rows.
+// Up to Q4_FUSED_PASS_M (32) token rows.  bf16 activations with blocksize
+// >= 64 run on the matrix cores in one pass (two token blocks), except where a
+// chunk holds 8 tiles: there the second block's registers spill and two
+// 16-row passes are faster (measured at 248320 x 2560).  Other activations
+// reaching this point (blocksize 32, or offsets beyond 32 bits) take the
+// vector-ALU kernel in passes of 16 rows.
 hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, const void *bias, int M, int N, int K,
                            int bs_log2, void *C, int c_dt, hipStream_t s) {
-    const bool mfma = a_dt != kF32 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K);
-    if (mfma && a_dt == kBf16 && (M <= 16 || tiles_per_chunk(N) < 8))
+    const bool mfma = a_dt == kBf16 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K);
+    if (mfma && (M <= 16 || tiles_per_chunk(N) < 8))
         return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
                                     C, c_dt, s);
     const size_t a_row = (size_t)K * (a_dt == kF32 ? 4 : 2);

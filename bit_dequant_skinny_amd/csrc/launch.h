@@ -35,12 +35,13 @@ hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt,
                                 hipStream_t s);
 
-// fp32 activations as three bf16 planes ([3][n], hi | mid | lo, exact for
-// |a| >= 2^-110) and the sum of the three planes' fp32 partials ([3][M][N])
-// plus bias, rounded once to c_dt.
-hipError_t launch_split_planes(const float *A, size_t n, uint16_t *planes, hipStream_t s);
-hipError_t launch_sum_planes(const float *P, int M, int N, const void *bias, void *C, int c_dt,
-                             hipStream_t s);
+// fp16 / fp32 activations as 2 / 3 exact bf16 planes ([np][n]) and the sum of
+// the planes' fp32 partials ([np][M][N]) plus bias, rounded once to c_dt.
+int activation_planes(int a_dt);
+hipError_t launch_split_planes(const void *A, int a_dt, size_t n, uint16_t *planes,
+                               hipStream_t s);
+hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *bias, void *C,
+                             int c_dt, hipStream_t s);
 bool q4_fused_mfma_fits(int M, int N, int K);
 
 // bf16-weight GEMM on the matrix cores, C = A * W^T (+ bias); A bf16 or fp16.
