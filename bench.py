@@ -127,18 +127,18 @@ class Dev:
             return None
         g.replay()
         t.cuda.synchronize()
-        best = None
-        for _ in range(3):
-            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-            with t.cuda.stream(side):
-                e0.record(side)
+        # The mean over three back-to-back replays: the part runs faster for
+        # the first millisecond or so after an idle gap than under sustained
+        # load, so one short replay would overstate the sustained rate.
+        e = [t.cuda.Event(enable_timing=True) for _ in range(4)]
+        with t.cuda.stream(side):
+            e[0].record(side)
+            for r in range(3):
                 g.replay()
-                e1.record(side)
-            t.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
-            best = us if best is None else min(best, us)
+                e[r + 1].record(side)
+        t.cuda.synchronize()
         del g
-        return best
+        return e[0].elapsed_time(e[3]) * 1e3 / (3 * reps)
 
 
 def fused_source_hash():
@@ -264,7 +264,7 @@ def headline(d, args):
     # Per-M kernel times: back-to-back launches of one M over the rotating
     # weight copies between one event pair.
     per_m_us = dict(zip(M_list, d.time_launches(
-        [lambda i, M=M: launch(M, i) for M in M_list], reps=4 * R)))
+        [lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)))
     total = args.steps * sum(q4_bytes(M, N, K) for M in M_list)
     per_m = {}
     for M in M_list:
