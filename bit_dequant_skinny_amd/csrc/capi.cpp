@@ -55,9 +55,10 @@ q4_status ok() {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// ---- test hook: Q4_TEST_FAIL_LAUNCH=<fused|dequant|gemm|copy>[:count] -------
-// Makes the next `count` launches of that kernel report a launch failure
-// without launching, so tests can check the error path and the recovery.
+// ---- test hook: Q4_TEST_FAIL_LAUNCH=<kernel>[:count] --------------------------
+// kernel: fused, dequant, gemm, planes, plane sum, quantize or copy.  Makes the
+// next `count` launches of that kernel report a launch failure without
+// launching, so tests can check the error path and the recovery.
 std::once_flag g_hook_once;
 std::string g_hook_kernel;
 std::atomic<int> g_hook_left{0};
@@ -81,15 +82,20 @@ bool injected_failure(const char *kernel) {
 }
 
 q4_status check_launch(hipError_t e, const char *kernel) {
-    if (injected_failure(kernel)) {
-        (void)hipGetLastError();
-        return fail(Q4_ERR_HIP, "%s: injected launch failure (Q4_TEST_FAIL_LAUNCH)", kernel);
-    }
     if (e != hipSuccess) {
         (void)hipGetLastError();  // drain the sticky error so the next call starts clean
         return fail(Q4_ERR_HIP, "%s: %s", kernel, hipGetErrorString(e));
     }
     return Q4_OK;
+}
+
+// Runs one launcher and checks its status; the test hook fails it before it
+// launches anything.
+template <class F>
+q4_status launch_checked(const char *kernel, F &&launch) {
+    if (injected_failure(kernel))
+        return fail(Q4_ERR_HIP, "%s: injected launch failure (Q4_TEST_FAIL_LAUNCH)", kernel);
+    return check_launch(launch(), kernel);
 }
 
 // ---- crossover -------------------------------------------------------------
@@ -225,10 +231,11 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
     const size_t a_row = (size_t)K * dtype_size(a_dt), c_row = (size_t)N * dtype_size(c_dt);
     for (int m0 = 0; m0 < M; m0 += Q4_FUSED_PASS_M) {
         const int mm = M - m0 < Q4_FUSED_PASS_M ? M - m0 : Q4_FUSED_PASS_M;
-        hipError_t e = q4::launch_q4_fused(static_cast<const char *>(A) + (size_t)m0 * a_row,
-                                           a_dt, Wp, am, cb, bias, mm, N, K, bs_log2,
-                                           static_cast<char *>(C) + (size_t)m0 * c_row, c_dt, s);
-        q4_status st = check_launch(e, "fused");
+        q4_status st = launch_checked("fused", [&] {
+            return q4::launch_q4_fused(static_cast<const char *>(A) + (size_t)m0 * a_row, a_dt,
+                                       Wp, am, cb, bias, mm, N, K, bs_log2,
+                                       static_cast<char *>(C) + (size_t)m0 * c_row, c_dt, s);
+        });
         if (st != Q4_OK) return st;
     }
     return Q4_OK;
@@ -256,13 +263,16 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
     if (st != Q4_OK) return st;
     uint16_t *planes = static_cast<uint16_t *>(ws);
     float *parts = reinterpret_cast<float *>(static_cast<char *>(ws) + part_off);
-    st = check_launch(q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s),
-                      "planes");
+    st = launch_checked("planes", [&] {
+        return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s);
+    });
     if (st != Q4_OK) return st;
     st = run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, np * M, N, K, bs_log2, parts,
                    Q4_DTYPE_FP32, s);
     if (st != Q4_OK) return st;
-    return check_launch(q4::launch_sum_planes(parts, np, M, N, bias, C, c_dt, s), "plane sum");
+    return launch_checked("plane sum", [&] {
+        return q4::launch_sum_planes(parts, np, M, N, bias, C, c_dt, s);
+    });
 }
 
 q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
@@ -278,11 +288,14 @@ q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am,
     const size_t bytes = (size_t)N * (size_t)K * 2;
     q4_status st = workspace(device, s, bytes, &ws);
     if (st != Q4_OK) return st;
-    e = q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, Q4_DTYPE_BF16, s);
-    st = check_launch(e, "dequant");
+    st = launch_checked("dequant", [&] {
+        return q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, Q4_DTYPE_BF16, s);
+    });
     if (st != Q4_OK) return st;
-    e = q4::launch_bf16_gemm(A, a_dt, static_cast<const uint16_t *>(ws), bias, M, N, K, C, c_dt, s);
-    return check_launch(e, "gemm");
+    return launch_checked("gemm", [&] {
+        return q4::launch_bf16_gemm(A, a_dt, static_cast<const uint16_t *>(ws), bias, M, N, K, C,
+                                    c_dt, s);
+    });
 }
 
 }  // namespace
@@ -380,10 +393,10 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
         return fail(Q4_ERR_INVALID_ARGUMENT,
                     "A and W must be 16-byte aligned, C and bias 2-byte aligned");
     drain_prior_error();
-    hipError_t e = q4::launch_bf16_gemm(A, Q4_DTYPE_BF16, static_cast<const uint16_t *>(W), bias,
-                                        M, N, K, C, Q4_DTYPE_BF16,
-                                        static_cast<hipStream_t>(stream));
-    q4_status st = check_launch(e, "gemm");
+    q4_status st = launch_checked("gemm", [&] {
+        return q4::launch_bf16_gemm(A, Q4_DTYPE_BF16, static_cast<const uint16_t *>(W), bias, M,
+                                    N, K, C, Q4_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    });
     return st == Q4_OK ? ok() : st;
 }
 
@@ -400,9 +413,10 @@ q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *c
     if (!aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) || !aligned(out, 16))
         return fail(Q4_ERR_INVALID_ARGUMENT, "Wpacked, absmax and out must be 16-byte aligned");
     drain_prior_error();
-    hipError_t e = q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, out, out_dtype,
-                                      static_cast<hipStream_t>(stream));
-    st = check_launch(e, "dequant");
+    st = launch_checked("dequant", [&] {
+        return q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, out, out_dtype,
+                                  static_cast<hipStream_t>(stream));
+    });
     return st == Q4_OK ? ok() : st;
 }
 
@@ -435,9 +449,10 @@ q4_status q4_quantize(const void *W, int w_dtype, const float *codebook, int N, 
         return fail(Q4_ERR_INVALID_ARGUMENT,
                     "W and Wpacked must be 16-byte aligned, absmax 4-byte aligned");
     drain_prior_error();
-    hipError_t e = q4::launch_quantize(W, w_dtype, N, K, bs_log2, tab, Wpacked, absmax,
-                                       static_cast<hipStream_t>(stream));
-    st = check_launch(e, "quantize");
+    st = launch_checked("quantize", [&] {
+        return q4::launch_quantize(W, w_dtype, N, K, bs_log2, tab, Wpacked, absmax,
+                                   static_cast<hipStream_t>(stream));
+    });
     return st == Q4_OK ? ok() : st;
 }
 
@@ -536,8 +551,9 @@ q4_status q4_copy_probe(const void *src, void *dst, size_t bytes, void *stream) 
     if (bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
         return fail(Q4_ERR_INVALID_ARGUMENT, "bytes and pointers must be multiples of 16");
     drain_prior_error();
-    hipError_t e = q4::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream));
-    q4_status st = check_launch(e, "copy");
+    q4_status st = launch_checked("copy", [&] {
+        return q4::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream));
+    });
     return st == Q4_OK ? ok() : st;
 }
 

@@ -1,0 +1,105 @@
+"""Launch-failure injection through the C ABI.
+
+The library's test hook Q4_TEST_FAIL_LAUNCH=<kernel>[:count] makes the next
+`count` launches of one kernel report a HIP failure before anything is
+launched (the host-forced failure pattern of the hipBLASLt int8 cache pull
+request).  Each case runs in a child process (the hook reads its variable
+once per process) and checks: the call returns Q4_ERR_HIP with a message
+naming the kernel, the output is untouched, and the next call succeeds with
+the right result.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CHILD = r'''
+import sys
+import numpy as np
+import torch
+import bit_dequant_skinny_amd as q4
+import oracle, synth
+sys.path.insert(0, "tests")
+from gpu_util import assert_within_tolerance, bf16_host, host_f64, q4_to_dev, to_dev
+
+case = sys.argv[1]
+dev = torch.device("cuda:0")
+M, N, K, bs = 3, 80, 512, 64
+p = synth.q4_problem(M, N, K, bs, config=70)
+A, Wp, am, cb = q4_to_dev(p)
+
+def expect_failure(fn, out, kernel):
+    before = out.clone()
+    try:
+        fn()
+    except q4.Q4Error as e:
+        assert e.status == q4.Q4_ERR_HIP, e.status
+        assert kernel in str(e) and "injected" in str(e), str(e)
+    else:
+        raise AssertionError("no failure reported")
+    torch.cuda.synchronize()
+    assert torch.equal(out, before), "output written by a failed call"
+
+if case in ("fused", "dequant_split", "gemm_split"):
+    path = "fused" if case == "fused" else "split"
+    kernel = {"fused": "fused", "dequant_split": "dequant", "gemm_split": "gemm"}[case]
+    C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=dev)
+    expect_failure(lambda: q4.q4_gemm_skinny(A, Wp, am, cb, bs, out=C, path=path), C, kernel)
+    q4.q4_gemm_skinny(A, Wp, am, cb, bs, out=C, path=path)
+    torch.cuda.synchronize()
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(bf16_host(C), Cr, S, case)
+elif case == "plane_sum":
+    A32 = synth.activations(M, K, 71, "fp32")
+    C = torch.full((M, N), 7.0, dtype=torch.float32, device=dev)
+    dA = to_dev(A32, "f32")
+    expect_failure(lambda: q4.q4_gemm_skinny(dA, Wp, am, cb, bs, out=C, out_dtype=torch.float32),
+                   C, "plane sum")
+    q4.q4_gemm_skinny(dA, Wp, am, cb, bs, out=C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Cr, S = oracle.q4_gemm_ex(A32, "fp32", p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(None, Cr, S, case, out="fp32", values=host_f64(C))
+elif case == "dequant":
+    out = torch.full((N, K), 3.0, dtype=torch.bfloat16, device=dev)
+    expect_failure(lambda: q4.q4_dequant(Wp, am, cb, bs, out=out), out, "dequant")
+    q4.q4_dequant(Wp, am, cb, bs, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
+    assert np.array_equal(bf16_host(out), ref)
+elif case == "gemm":
+    W = to_dev(synth.bf16_weights(N, K, 72), "bf16")
+    C = torch.full((M, N), 5.0, dtype=torch.bfloat16, device=dev)
+    expect_failure(lambda: q4.bf16_gemm_skinny(A, W, None, out=C), C, "gemm")
+    q4.bf16_gemm_skinny(A, W, None, out=C)
+    C2 = q4.bf16_gemm_skinny(A, W, None)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+else:
+    raise SystemExit("unknown case " + case)
+print("ok", case)
+'''
+
+CASES = {
+    "fused": "fused:1",
+    "dequant_split": "dequant:1",
+    "gemm_split": "gemm:1",
+    "plane_sum": "plane sum:1",
+    "dequant": "dequant:1",
+    "gemm": "gemm:1",
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_injected_launch_failure_and_recovery(case):
+    env = dict(os.environ)
+    env["Q4_TEST_FAIL_LAUNCH"] = CASES[case]
+    env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+    r = subprocess.run([sys.executable, "-c", CHILD, case], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert ("ok " + case) in r.stdout
