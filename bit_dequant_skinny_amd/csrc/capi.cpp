@@ -275,6 +275,11 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
     });
 }
 
+// Token rows above which the split path's GEMM takes the tiled kernel (which
+// reuses each weight tile from LDS for 128 tokens) instead of the streaming
+// kernel (which reads the weights once per 16-row slab).
+constexpr int kTiledGemmMinM = 16;
+
 q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
                     const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
                     hipStream_t s) {
@@ -284,17 +289,42 @@ q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am,
         (void)hipGetLastError();
         return fail(Q4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     }
+    // Workspace: the bf16 weights, then (fp16 activations on the tiled GEMM)
+    // two bf16 planes of A and their fp32 partial outputs.
+    const bool tiled = M > kTiledGemmMinM && q4::gemm_tiled_fits(2 * M, N, K);
+    const bool planes = tiled && a_dt == Q4_DTYPE_FP16;
+    const size_t w_bytes = ((size_t)N * (size_t)K * 2 + 255) & ~(size_t)255;
+    const size_t p_bytes = planes ? ((2 * (size_t)M * (size_t)K * 2 + 255) & ~(size_t)255) : 0;
+    const size_t s_bytes = planes ? 2 * (size_t)M * (size_t)N * 4 : 0;
     void *ws = nullptr;
-    const size_t bytes = (size_t)N * (size_t)K * 2;
-    q4_status st = workspace(device, s, bytes, &ws);
+    q4_status st = workspace(device, s, w_bytes + p_bytes + s_bytes, &ws);
     if (st != Q4_OK) return st;
+    const uint16_t *Wd = static_cast<const uint16_t *>(ws);
     st = launch_checked("dequant", [&] {
         return q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, Q4_DTYPE_BF16, s);
     });
     if (st != Q4_OK) return st;
-    return launch_checked("gemm", [&] {
-        return q4::launch_bf16_gemm(A, a_dt, static_cast<const uint16_t *>(ws), bias, M, N, K, C,
-                                    c_dt, s);
+    if (!tiled)
+        return launch_checked("gemm", [&] {
+            return q4::launch_bf16_gemm(A, a_dt, Wd, bias, M, N, K, C, c_dt, s);
+        });
+    if (!planes)
+        return launch_checked("gemm", [&] {
+            return q4::launch_gemm_tiled(static_cast<const uint16_t *>(A), Wd, bias, M, N, K, C,
+                                         c_dt, s);
+        });
+    uint16_t *pl = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w_bytes);
+    float *parts = reinterpret_cast<float *>(static_cast<char *>(ws) + w_bytes + p_bytes);
+    st = launch_checked("planes", [&] {
+        return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, pl, s);
+    });
+    if (st != Q4_OK) return st;
+    st = launch_checked("gemm", [&] {
+        return q4::launch_gemm_tiled(pl, Wd, nullptr, 2 * M, N, K, parts, Q4_DTYPE_FP32, s);
+    });
+    if (st != Q4_OK) return st;
+    return launch_checked("plane sum", [&] {
+        return q4::launch_sum_planes(parts, 2, M, N, bias, C, c_dt, s);
     });
 }
 

@@ -44,6 +44,12 @@ hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *b
                              int c_dt, hipStream_t s);
 bool q4_fused_mfma_fits(int M, int N, int K);
 
+// Tiled bf16 GEMM (bf16 A, 128 x 128 tiles through LDS) for the split path at
+// larger M; gemm_tiled_fits checks its 32-bit offsets.
+bool gemm_tiled_fits(int M, int N, int K);
+hipError_t launch_gemm_tiled(const uint16_t *A, const uint16_t *W, const void *bias, int M,
+                             int N, int K, void *C, int c_dt, hipStream_t s);
+
 // bf16-weight GEMM on the matrix cores, C = A * W^T (+ bias); A bf16 or fp16.
 hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,
                             int N, int K, void *C, int c_dt, hipStream_t s);
