@@ -289,13 +289,16 @@ q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am,
         (void)hipGetLastError();
         return fail(Q4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     }
-    // Workspace: the bf16 weights, then (fp16 activations on the tiled GEMM)
-    // two bf16 planes of A and their fp32 partial outputs.
+    // Workspace: the bf16 weights, then (on the tiled GEMM) the bf16 planes of
+    // fp16 activations and the fp32 partial outputs of the planes and K parts.
     const bool tiled = M > kTiledGemmMinM && q4::gemm_tiled_fits(2 * M, N, K);
-    const bool planes = tiled && a_dt == Q4_DTYPE_FP16;
+    const int np = tiled && a_dt == Q4_DTYPE_FP16 ? 2 : 1;
+    int ks = tiled ? q4::gemm_tiled_ksplit(np * M, N, K) : 1;
+    if (np * ks > 4) ks = 4 / np;
+    const bool partials = np * ks > 1;
     const size_t w_bytes = ((size_t)N * (size_t)K * 2 + 255) & ~(size_t)255;
-    const size_t p_bytes = planes ? ((2 * (size_t)M * (size_t)K * 2 + 255) & ~(size_t)255) : 0;
-    const size_t s_bytes = planes ? 2 * (size_t)M * (size_t)N * 4 : 0;
+    const size_t p_bytes = np > 1 ? ((np * (size_t)M * (size_t)K * 2 + 255) & ~(size_t)255) : 0;
+    const size_t s_bytes = partials ? (size_t)(np * ks) * (size_t)M * (size_t)N * 4 : 0;
     void *ws = nullptr;
     q4_status st = workspace(device, s, w_bytes + p_bytes + s_bytes, &ws);
     if (st != Q4_OK) return st;
@@ -308,23 +311,28 @@ q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am,
         return launch_checked("gemm", [&] {
             return q4::launch_bf16_gemm(A, a_dt, Wd, bias, M, N, K, C, c_dt, s);
         });
-    if (!planes)
+    if (!partials)
         return launch_checked("gemm", [&] {
-            return q4::launch_gemm_tiled(static_cast<const uint16_t *>(A), Wd, bias, M, N, K, C,
-                                         c_dt, s);
+            return q4::launch_gemm_tiled(static_cast<const uint16_t *>(A), Wd, bias, M, N, K, 1,
+                                         C, c_dt, s);
         });
-    uint16_t *pl = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w_bytes);
+    const uint16_t *Ab = static_cast<const uint16_t *>(A);
+    if (np > 1) {
+        uint16_t *pl = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + w_bytes);
+        st = launch_checked("planes", [&] {
+            return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, pl, s);
+        });
+        if (st != Q4_OK) return st;
+        Ab = pl;
+    }
+    // np*ks fp32 slabs of M x N: [K part][plane][M][N]
     float *parts = reinterpret_cast<float *>(static_cast<char *>(ws) + w_bytes + p_bytes);
-    st = launch_checked("planes", [&] {
-        return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, pl, s);
-    });
-    if (st != Q4_OK) return st;
     st = launch_checked("gemm", [&] {
-        return q4::launch_gemm_tiled(pl, Wd, nullptr, 2 * M, N, K, parts, Q4_DTYPE_FP32, s);
+        return q4::launch_gemm_tiled(Ab, Wd, nullptr, np * M, N, K, ks, parts, Q4_DTYPE_FP32, s);
     });
     if (st != Q4_OK) return st;
     return launch_checked("plane sum", [&] {
-        return q4::launch_sum_planes(parts, 2, M, N, bias, C, c_dt, s);
+        return q4::launch_sum_planes(parts, np * ks, M, N, bias, C, c_dt, s);
     });
 }
 

@@ -17,7 +17,9 @@
 // buffer loads whose range check returns zeros past the end of A or W (rows
 // past M or N); k past K is masked per 16-byte piece (K % 8 == 0).  The grid
 // runs the token blocks of one feature block next to each other, so a W tile
-// is fetched from HBM once and the other token blocks find it in L2.
+// is fetched from HBM once and the other token blocks find it in L2.  When
+// there are too few tiles to give every CU two workgroups, K is split into up
+// to 4 parts whose fp32 partial outputs a separate pass sums in part order.
 #include "device.h"
 #include "launch.h"
 
@@ -38,14 +40,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 
 __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
-    const void *__restrict__ bias, int M, int N, int K, int m_blocks,
-    void *__restrict__ C, int c_dt) {
+    const void *__restrict__ bias, int M, int N, int K, int m_blocks, int mn_blocks,
+    int k_steps, void *__restrict__ C, int c_dt) {
     __shared__ __attribute__((aligned(16))) char lds[2][2][kTileBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = (int)(blockIdx.x % (uint32_t)m_blocks) * BM;
-    const int n0 = (int)(blockIdx.x / (uint32_t)m_blocks) * BN;
+    // Block b: token block b % m_blocks, feature block (b % mn_blocks) /
+    // m_blocks, and K part b / mn_blocks (k_steps steps of 64 from
+    // part * k_steps); part p writes its own fp32 output slab C + p*M*N.
+    const uint32_t blk = blockIdx.x % (uint32_t)mn_blocks;
+    const int part = (int)(blockIdx.x / (uint32_t)mn_blocks);
+    const int m0 = (int)(blk % (uint32_t)m_blocks) * BM;
+    const int n0 = (int)(blk / (uint32_t)m_blocks) * BN;
+    const int kt0 = part * k_steps;
     const int j = lane & 15, g = lane >> 4;
 
     const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
@@ -80,14 +88,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk_all = (K + BK - 1) / BK;
+    const int nk = nk_all - kt0 < k_steps ? nk_all - kt0 : k_steps;
+    if (part > 0) C = static_cast<char *>(C) + (size_t)part * (size_t)M * (size_t)N * 4;
     uint4 ra[4], rw[4];
-    gload(0, ra, rw);
+    gload(kt0 * BK, ra, rw);
     lstore(0, ra, rw);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK, ra, rw);
+        if (kt + 1 < nk) gload((kt0 + kt + 1) * BK, ra, rw);
         const char *as = lds[cur][0];
         const char *ws = lds[cur][1];
 #pragma unroll
@@ -133,13 +143,25 @@ bool gemm_tiled_fits(int M, int N, int K) {
     return (uint64_t)M * (uint64_t)K * 2 < (1ull << 31) && (uint64_t)N * (uint64_t)K * 2 < (1ull << 31);
 }
 
+int gemm_tiled_ksplit(int M, int N, int K) {
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int want = 2 * device_info().num_cus;  // two workgroups per CU
+    const int nk = (K + BK - 1) / BK;
+    int ks = 1;
+    while (ks < 4 && tiles * ks < want && nk >= 4 * (ks + 1)) ++ks;
+    return ks;
+}
+
 hipError_t launch_gemm_tiled(const uint16_t *A, const uint16_t *W, const void *bias, int M,
-                             int N, int K, void *C, int c_dt, hipStream_t s) {
+                             int N, int K, int ksplit, void *C, int c_dt, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
+    if (ksplit < 1 || (ksplit > 1 && (bias || c_dt != kF32))) return hipErrorInvalidValue;
     const int m_blocks = (M + BM - 1) / BM;
     const int n_blocks = (N + BN - 1) / BN;
-    gemm_tiled_kernel<<<dim3((unsigned)(m_blocks * n_blocks)), dim3(kThreads), 0, s>>>(
-        A, W, bias, M, N, K, m_blocks, C, c_dt);
+    const int nk = (K + BK - 1) / BK;
+    const int k_steps = (nk + ksplit - 1) / ksplit;
+    gemm_tiled_kernel<<<dim3((unsigned)(m_blocks * n_blocks * ksplit)), dim3(kThreads), 0, s>>>(
+        A, W, bias, M, N, K, m_blocks, m_blocks * n_blocks, k_steps, C, c_dt);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
                                 hipStream_t s);
 
 // fp16 / fp32 activations as 2 / 3 exact bf16 planes ([np][n]) and the sum of
-// the planes' fp32 partials ([np][M][N]) plus bias, rounded once to c_dt.
+// np (2..4) fp32 partials ([np][M][N]) plus bias, rounded once to c_dt.
 int activation_planes(int a_dt);
 hipError_t launch_split_planes(const void *A, int a_dt, size_t n, uint16_t *planes,
                                hipStream_t s);
@@ -46,9 +46,12 @@ bool q4_fused_mfma_fits(int M, int N, int K);
 
 // Tiled bf16 GEMM (bf16 A, 128 x 128 tiles through LDS) for the split path at
 // larger M; gemm_tiled_fits checks its 32-bit offsets.
+// ksplit > 1 writes ksplit fp32 partial outputs [ksplit][M][N] (no bias) for
+// launch_sum_planes to add; gemm_tiled_ksplit picks the split for a shape.
 bool gemm_tiled_fits(int M, int N, int K);
+int gemm_tiled_ksplit(int M, int N, int K);
 hipError_t launch_gemm_tiled(const uint16_t *A, const uint16_t *W, const void *bias, int M,
-                             int N, int K, void *C, int c_dt, hipStream_t s);
+                             int N, int K, int ksplit, void *C, int c_dt, hipStream_t s);
 
 // bf16-weight GEMM on the matrix cores, C = A * W^T (+ bias); A bf16 or fp16.
 hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,

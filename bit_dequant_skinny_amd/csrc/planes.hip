@@ -16,7 +16,8 @@
 // The NP planes form NP*M bf16 rows, [hi rows | (mid rows) | lo rows], which
 // the bf16 matrix-core kernel multiplies into fp32 partials without a bias;
 // the sum kernel then adds the partials of each output in plane order, adds
-// the bias in fp32 and rounds once to the output type.  Both kernels are
+// the bias in fp32 and rounds once to the output type.  The same sum combines
+// the K parts of the split path's tiled GEMM (up to 4 partials).  Both kernels are
 // elementwise and HBM-bound.
 #include "device.h"
 #include "launch.h"
@@ -60,7 +61,8 @@ __global__ __launch_bounds__(kThreads) void sum_planes_kernel(const float *__res
     for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < mn;
          i += (size_t)gridDim.x * kThreads) {
         float v = P[i] + P[mn + i];
-        if constexpr (NP == 3) v += P[2 * mn + i];
+        if constexpr (NP >= 3) v += P[2 * mn + i];
+        if constexpr (NP >= 4) v += P[3 * mn + i];
         if (bias) v += load_elem(bias, i % (size_t)N, c_dt);  // before the single rounding
         store_elem(C, i, v, c_dt);
     }
@@ -89,7 +91,8 @@ hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *b
                              int c_dt, hipStream_t s) {
     const size_t mn = (size_t)M * (size_t)N;
     if (mn == 0) return hipSuccess;
-    if (np == 3) sum_planes_kernel<3><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
+    if (np == 4) sum_planes_kernel<4><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
+    else if (np == 3) sum_planes_kernel<3><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
     else if (np == 2) sum_planes_kernel<2><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
     else return hipErrorInvalidValue;
     return hipGetLastError();
