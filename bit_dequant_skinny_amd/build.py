@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     # mixed-precision fma with a single rounding and lose the sign of zero)
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results land in ordinary VGPRs, so the fp32 epilogues that
+    # scale them (absmax per block) read them without v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

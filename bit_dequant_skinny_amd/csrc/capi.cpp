@@ -216,18 +216,84 @@ q4_status drain_prior_error() {
 bool known_dtype(int dt) { return dt == Q4_DTYPE_BF16 || dt == Q4_DTYPE_FP16 || dt == Q4_DTYPE_FP32; }
 size_t dtype_size(int dt) { return dt == Q4_DTYPE_FP32 ? 4 : 2; }
 
+// Token rows above which the fused path takes the tiled matrix-core kernel
+// (each decoded weight serves a 64-row token block) instead of passes of the
+// skinny kernels over 32-row slabs, which read the packed weights once per
+// slab.  Q4_FUSED_TILED_MIN_M overrides it at first use.
+constexpr int kFusedTiledMinM = 32;
+
+int fused_tiled_min_m() {
+    static const int v = [] {
+        if (const char *e = std::getenv("Q4_FUSED_TILED_MIN_M")) {
+            char *end = nullptr;
+            const long x = std::strtol(e, &end, 10);
+            if (end != e && *end == '\0' && x >= 0 && x <= Q4_CROSSOVER_MAX) return (int)x;
+        }
+        return kFusedTiledMinM;
+    }();
+    return v;
+}
+
+bool fused_tiled(int rows, int N, int K, int bs_log2) {
+    return bs_log2 >= 6 && rows > fused_tiled_min_m() && q4::q4_fused_tiled_fits(rows, N, K);
+}
+
+q4_status current_device(int *device) {
+    const hipError_t e = hipGetDevice(device);
+    if (e == hipSuccess) return Q4_OK;
+    (void)hipGetLastError();
+    return fail(Q4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+}
+
+// The tiled fused kernel on bf16 activations (rows = token rows, or np*M rows
+// of activation planes).  When K is split over workgroups (ksplit > 1) the
+// kernel writes ksplit fp32 partial outputs to `parts` and one pass sums them
+// in part order with the bias.
+q4_status run_fused_tiled(const uint16_t *A, const uint8_t *Wp, const float *am, const float *cb,
+                          const void *bias, int rows, int N, int K, int bs_log2, int ksplit,
+                          float *parts, void *C, int c_dt, hipStream_t s) {
+    if (ksplit == 1)
+        return launch_checked("fused", [&] {
+            return q4::launch_q4_fused_tiled(A, Wp, am, cb, bias, rows, N, K, bs_log2, 1, C,
+                                             c_dt, s);
+        });
+    return launch_checked("fused", [&] {
+        return q4::launch_q4_fused_tiled(A, Wp, am, cb, nullptr, rows, N, K, bs_log2, ksplit,
+                                         parts, Q4_DTYPE_FP32, s);
+    });
+}
+
 q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const float *am,
                            const float *cb, const void *bias, int M, int N, int K, int bs_log2,
                            void *C, int c_dt, hipStream_t s);
 
-// The fused kernels take up to Q4_FUSED_PASS_M token rows per pass; larger M
-// runs in passes over consecutive row slabs, each streaming the packed
-// weights once more.
+// bf16 activations: the tiled kernel above kFusedTiledMinM rows, else the
+// skinny kernels in passes of up to Q4_FUSED_PASS_M token rows over
+// consecutive row slabs, each streaming the packed weights once more.
 q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
                     const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
                     hipStream_t s) {
     if (a_dt != Q4_DTYPE_BF16 && bs_log2 >= 6 && q4::q4_fused_mfma_fits(M, N, K))
         return run_fused_planes(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, C, c_dt, s);
+    if (a_dt == Q4_DTYPE_BF16 && fused_tiled(M, N, K, bs_log2)) {
+        const int ks = q4::q4_fused_tiled_ksplit(M, N, K);
+        float *parts = nullptr;
+        if (ks > 1) {
+            int device = 0;
+            q4_status st = current_device(&device);
+            if (st != Q4_OK) return st;
+            void *ws = nullptr;
+            st = workspace(device, s, (size_t)ks * (size_t)M * (size_t)N * 4, &ws);
+            if (st != Q4_OK) return st;
+            parts = static_cast<float *>(ws);
+        }
+        q4_status st = run_fused_tiled(static_cast<const uint16_t *>(A), Wp, am, cb, bias, M, N,
+                                       K, bs_log2, ks, parts, C, c_dt, s);
+        if (st != Q4_OK || ks == 1) return st;
+        return launch_checked("plane sum", [&] {
+            return q4::launch_sum_planes(parts, ks, M, N, bias, C, c_dt, s);
+        });
+    }
     const size_t a_row = (size_t)K * dtype_size(a_dt), c_row = (size_t)N * dtype_size(c_dt);
     for (int m0 = 0; m0 < M; m0 += Q4_FUSED_PASS_M) {
         const int mm = M - m0 < Q4_FUSED_PASS_M ? M - m0 : Q4_FUSED_PASS_M;
@@ -243,23 +309,25 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
 
 // fp16 / fp32 activations with blocksize >= 64: the exact split of each
 // activation row into 2 / 3 bf16 planes (planes.hip) runs through the
-// matrix-core kernel as np*M bf16 rows with fp32 partial outputs, then one
-// pass sums the partials of each output, adds the bias and rounds once.
-// Planes and partials live in the per-stream workspace.
+// matrix-core kernels as np*M bf16 rows with fp32 partial outputs (times the
+// K parts of the tiled kernel, at most 4 slabs in all), then one pass sums
+// the partials of each output, adds the bias and rounds once.  Planes and
+// partials live in the per-stream workspace.
 q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const float *am,
                            const float *cb, const void *bias, int M, int N, int K, int bs_log2,
                            void *C, int c_dt, hipStream_t s) {
     int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(Q4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    }
+    q4_status st = current_device(&device);
+    if (st != Q4_OK) return st;
     const int np = q4::activation_planes(a_dt);
-    const size_t plane_bytes = (size_t)np * (size_t)M * (size_t)K * 2;
+    const int rows = np * M;
+    const bool tiled = fused_tiled(rows, N, K, bs_log2);
+    int ks = tiled ? q4::q4_fused_tiled_ksplit(rows, N, K) : 1;
+    if (np * ks > 4) ks = 4 / np;
+    const size_t plane_bytes = (size_t)rows * (size_t)K * 2;
     const size_t part_off = (plane_bytes + 255) & ~(size_t)255;
     void *ws = nullptr;
-    q4_status st = workspace(device, s, part_off + (size_t)np * (size_t)M * (size_t)N * 4, &ws);
+    st = workspace(device, s, part_off + (size_t)(ks * np) * (size_t)M * (size_t)N * 4, &ws);
     if (st != Q4_OK) return st;
     uint16_t *planes = static_cast<uint16_t *>(ws);
     float *parts = reinterpret_cast<float *>(static_cast<char *>(ws) + part_off);
@@ -267,11 +335,13 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
         return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s);
     });
     if (st != Q4_OK) return st;
-    st = run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, np * M, N, K, bs_log2, parts,
-                   Q4_DTYPE_FP32, s);
+    st = tiled ? run_fused_tiled(planes, Wp, am, cb, nullptr, rows, N, K, bs_log2, ks, parts,
+                                 parts, Q4_DTYPE_FP32, s)
+               : run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, rows, N, K, bs_log2,
+                           parts, Q4_DTYPE_FP32, s);
     if (st != Q4_OK) return st;
     return launch_checked("plane sum", [&] {
-        return q4::launch_sum_planes(parts, np, M, N, bias, C, c_dt, s);
+        return q4::launch_sum_planes(parts, ks * np, M, N, bias, C, c_dt, s);
     });
 }
 

@@ -72,6 +72,41 @@ __device__ __forceinline__ void store_elem(void *p, size_t i, float v, int dt) {
     else reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16_rne(v);
 }
 
+// Packed-byte decode table of the matrix-core kernels.  Entry e (a packed
+// byte, low nibble = even k) holds x = (hi(cb[e & 15]), hi(cb[e >> 4])) and
+// y = (lo(cb[e & 15]), lo(cb[e >> 4])) in bf16, where hi = bf16(cb) and
+// lo = bf16(cb - hi): hi + lo equals the fp32 codebook value to within 2^-18
+// relative.  Two entries back to back, [x0 y0 x1 y1], form the operand
+// [hi(c0) hi(c1) lo(c0) lo(c1) hi(c2) hi(c3) lo(c2) lo(c3)] of
+// v_mfma_f32_16x16x32_bf16, which against the activations [a0 a1 a0 a1 a2 a3
+// a2 a3] forms a*hi + a*lo exactly in the fp32 accumulator.
+__device__ __forceinline__ uint2 pair_table_entry(float c0, float c1) {
+    const uint32_t h0 = f32_to_bf16_rne(c0), h1 = f32_to_bf16_rne(c1);
+    const uint32_t l0 = f32_to_bf16_rne(c0 - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(c1 - __uint_as_float(h1 << 16));
+    return make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
+}
+
+// A lane of group g = lane / 16 loads 16 packed bytes (32 codes) at byte
+// 16*g of a 128-wide segment of one weight row.  One v_permlane32_swap of
+// dwords (0, 2) and one of (1, 3) leave lanes 0-31 with their own dwords 0,1
+// and dwords 0,1 of the lane 32 above, and lanes 32-63 with dwords 2,3 of the
+// lane 32 below and their own dwords 2,3, so that dwords 0,1 of every lane
+// hold codes of the segment's first 64 k and dwords 2,3 codes of the second.
+// This is the k offset, within the segment, of the 8 codes in dword t.
+__device__ __forceinline__ uint32_t swapped_k_offset(int g, int t) {
+    return 32 * (g & 1) + 16 * (g >> 1) + 8 * (t & 1) + 64 * (t >> 1);
+}
+
+__device__ __forceinline__ void permlane32_swap_dwords(uint4 &w) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+    w.x = s02[0];
+    w.z = s02[1];
+    w.y = s13[0];
+    w.w = s13[1];
+}
+
 __device__ __forceinline__ floatx4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

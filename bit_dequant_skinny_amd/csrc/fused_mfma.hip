@@ -58,21 +58,6 @@ namespace q4 {
 
 namespace {
 
-// Table entry e (a packed byte): x = (hi(cb[e & 15]), hi(cb[e >> 4])),
-// y = (lo(cb[e & 15]), lo(cb[e >> 4])), low nibble = even k = low half.
-__device__ __forceinline__ uint2 pair_table_entry(float c0, float c1) {
-    const uint32_t h0 = f32_to_bf16_rne(c0), h1 = f32_to_bf16_rne(c1);
-    const uint32_t l0 = f32_to_bf16_rne(c0 - __uint_as_float(h0 << 16));
-    const uint32_t l1 = f32_to_bf16_rne(c1 - __uint_as_float(h1 << 16));
-    return make_uint2(h0 | (h1 << 16), l0 | (l1 << 16));
-}
-
-// Offset (in k) of the 8 codes in dword t of lane group g's 16 bytes after
-// the permlane32 swap.
-__device__ __forceinline__ uint32_t k_offset(int g, int t) {
-    return 32 * (g & 1) + 16 * (g >> 1) + 8 * (t & 1) + 64 * (t >> 1);
-}
-
 // LDS-only barrier: waits for this wave's LDS operations, not for its global
 // loads still in flight, then synchronises the workgroup.
 __device__ __forceinline__ void lds_barrier() {
@@ -246,7 +231,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         const uint32_t kk = ((uint32_t)wave + (uint32_t)((q + rot) % spw) * KW) * 128;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t k = kk + k_offset(g, t);
+            const uint32_t k = kk + swapped_k_offset(g, t);
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
                 const uint32_t off = k < (uint32_t)K ? a_row + (uint32_t)(16 * b) * (uint32_t)K * 2 + k * 2
