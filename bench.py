@@ -271,7 +271,7 @@ def headline(d, args):
         gbs = q4_bytes(M, N, K) / (per_m_us[M] * 1e-6) / 1e9
         per_m[str(M)] = {"us": round(per_m_us[M], 2), "GB/s": round(gbs, 1),
                          "pct_peak": round(100 * gbs / PEAK_GBS, 1),
-                         "path": "fused" if M <= q4.q4_get_crossover_m() else "split"}
+                         "path": "fused" if M <= q4.q4_get_crossover_shape(N, K) else "split"}
     # The roofline kernel is the M=1 launch, timed as above.
     m1_us = per_m_us[1]
     ach = q4_bytes(1, N, K) / (m1_us * 1e-6) / 1e9
@@ -351,6 +351,18 @@ def other_configs(d):
                 break
         cross["K=%d N=%d" % (K, N)] = mstar
     res["crossover (first M of 1,4,8,16 where split beats fused)"] = cross
+    log("fused vs split at 32..256 token rows")
+    big = {}
+    for shape, (K, N) in enumerate([(5120, 8192), (5120, 5120), (17408, 5120), (8192, 8192),
+                                    (8192, 28672)]):
+        Ms = [32, 64, 128, 256]
+        rows = q4_cfg("q4 K=%d N=%d M=32..256" % (K, N), Ms, N, K, 2, shape,
+                      paths=("fused", "split"))
+        first = next((M for M in Ms if rows["M=%d split" % M]["us"] < rows["M=%d fused" % M]["us"]),
+                     None)
+        big["K=%d N=%d" % (K, N)] = {"first M of 32..256 where split beats fused": first,
+                                     "library: fused when M <=": q4.q4_get_crossover_shape(N, K)}
+    res["crossover at 32..256 rows"] = big
     log("C4 bf16 skinny")
     for shape, N in enumerate([96, 2048, 16384, 31040]):
         K = 2560

@@ -27,14 +27,33 @@
 
 namespace {
 
-// Fused-versus-split threshold on MI355X (fused when M <= value).  Timed on
-// the decode layer shapes (K, N) = (5120, 8192), (5120, 5120), (17408, 5120),
+// Fused-versus-split threshold on MI355X (fused when M <= value) for weight
+// shapes without an entry of their own.  Timed at M = 17 .. 512 on the decode
+// layer shapes (K, N) = (5120, 8192), (5120, 5120), (17408, 5120),
 // (8192, 8192), the 28672 x 8192 FFN, the 4096 x 4096 GEMV and the 248320 x
-// 2560 output projection at M = 16 .. 256: the fused kernel in row passes
-// beats dequantize + GEMM at every point (1.1x to 7x), so by default every M
-// takes the fused path and the split path runs only when forced or when the
-// crossover is lowered.
-constexpr int kDefaultCrossoverM = Q4_CROSSOVER_MAX;
+// 2560 output projection: below M = 96 the fused kernels win on every shape
+// (1.4x to 2.7x at M = 64), and dequantize + tiled GEMM first wins between
+// M = 96 and M = 384 depending on the shape; 128 keeps every measured shape
+// within 5 % of its faster path up to its own crossover.
+constexpr int kDefaultCrossoverM = 128;
+
+// Measured crossovers of those shapes: (N, K) -> the largest M the fused path
+// takes.  They seed the per-shape table, which the caller can change or clear.
+struct ShapeEntry {
+    int n, k, m;
+};
+constexpr ShapeEntry kMeasuredCrossovers[] = {
+    {8192, 5120, 128}, {5120, 5120, 192}, {5120, 17408, 192}, {8192, 8192, 128},
+    {28672, 8192, 192}, {4096, 4096, 256}, {248320, 2560, 192},
+};
+
+// Fused path above 32 token rows: the tiled kernel, except on shapes where
+// the skinny kernel's 32-row passes measured faster up to the given M (the
+// 28672 x 8192 FFN, whose skinny kernel streams its weights at the highest
+// rate of any shape: passes 152 us against tiled 211 us at M = 96).
+constexpr ShapeEntry kPassesPreferred[] = {
+    {28672, 8192, 192},
+};
 
 thread_local std::string tl_error;
 
@@ -116,9 +135,9 @@ int crossover() {
 }
 
 // Per-shape crossovers: an entry for (N, K) overrides the process-wide value
-// for that weight shape.  The table starts from the environment variable
-// Q4_CROSSOVER_TABLE ("N:K:m" items separated by commas) at first use; a
-// malformed item is skipped.
+// for that weight shape.  The table starts from the measured entries above,
+// then the environment variable Q4_CROSSOVER_TABLE ("N:K:m" items separated
+// by commas) at first use; a malformed item is skipped.
 std::mutex g_shape_mutex;
 std::map<std::pair<int, int>, int> g_shape_crossover;
 bool g_shape_loaded = false;
@@ -126,6 +145,7 @@ bool g_shape_loaded = false;
 void load_shape_table_locked() {
     if (g_shape_loaded) return;
     g_shape_loaded = true;
+    for (const ShapeEntry &x : kMeasuredCrossovers) g_shape_crossover[{x.n, x.k}] = x.m;
     const char *e = std::getenv("Q4_CROSSOVER_TABLE");
     if (!e) return;
     const std::string text(e);
@@ -219,23 +239,27 @@ size_t dtype_size(int dt) { return dt == Q4_DTYPE_FP32 ? 4 : 2; }
 // Token rows above which the fused path takes the tiled matrix-core kernel
 // (each decoded weight serves a 64-row token block) instead of passes of the
 // skinny kernels over 32-row slabs, which read the packed weights once per
-// slab.  Q4_FUSED_TILED_MIN_M overrides it at first use.
+// slab: 32, or the shape's entry in kPassesPreferred.  Q4_FUSED_TILED_MIN_M
+// (0 .. Q4_CROSSOVER_MAX) replaces both at first use.
 constexpr int kFusedTiledMinM = 32;
 
-int fused_tiled_min_m() {
-    static const int v = [] {
+int fused_tiled_min_m(int N, int K) {
+    static const int env = [] {
         if (const char *e = std::getenv("Q4_FUSED_TILED_MIN_M")) {
             char *end = nullptr;
             const long x = std::strtol(e, &end, 10);
             if (end != e && *end == '\0' && x >= 0 && x <= Q4_CROSSOVER_MAX) return (int)x;
         }
-        return kFusedTiledMinM;
+        return -1;
     }();
-    return v;
+    if (env >= 0) return env;
+    for (const ShapeEntry &x : kPassesPreferred)
+        if (x.n == N && x.k == K) return x.m;
+    return kFusedTiledMinM;
 }
 
 bool fused_tiled(int rows, int N, int K, int bs_log2) {
-    return bs_log2 >= 6 && rows > fused_tiled_min_m() && q4::q4_fused_tiled_fits(rows, N, K);
+    return bs_log2 >= 6 && rows > fused_tiled_min_m(N, K) && q4::q4_fused_tiled_fits(rows, N, K);
 }
 
 q4_status current_device(int *device) {

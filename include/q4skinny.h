@@ -82,9 +82,14 @@ enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
  *    not 16-byte aligned, codebook not 4-byte aligned, C not 2-byte aligned.
  *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}; M or N above
  *    2^30/K-sized limits (N * K / 2 must fit in 2^40 bytes).
- *  Which kernel runs: M <= the crossover take the fused kernel (in passes of
- *  Q4_FUSED_PASS_M rows); other M take the split path (dequantize to bf16 into
- *  a library-owned workspace of N*K*2 bytes, then an MFMA bf16 GEMM).
+ *  Which kernel runs: M <= the crossover (q4_get_crossover_shape(N, K)) take
+ *  the fused path: up to 32 rows the skinny matrix-core kernel, above that
+ *  the tiled matrix-core kernel (output tiles of 64 tokens x 64 features,
+ *  K split over workgroups into fp32 partials in the workspace when its
+ *  tiles cannot fill the GPU), or on shapes where they measured faster,
+ *  passes of the skinny kernel over Q4_FUSED_PASS_M rows.  Other M take the
+ *  split path (dequantize to bf16 into a library-owned workspace of N*K*2
+ *  bytes, then an MFMA bf16 GEMM).
  */
 q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *absmax,
                          const float *codebook, int M, int N, int K, int blocksize,
@@ -230,16 +235,18 @@ q4_status q4_set_crossover_m(int m);
  * with that shape; the pull request above tunes its threshold per GPU and
  * notes that the best switch point depends on the problem (section "Fused
  * path support for M > 1" and the crossover table), and measured per-shape
- * values on MI355X can be recorded here.  The table starts from the
- * environment variable Q4_CROSSOVER_TABLE at first use: comma-separated
- * "N:K:m" items (malformed items are skipped).
+ * values on MI355X can be recorded here.  The table starts from the values
+ * measured on MI355X for the decode layer shapes compiled into the library,
+ * then the environment variable Q4_CROSSOVER_TABLE at first use:
+ * comma-separated "N:K:m" items (malformed items are skipped).
  *  q4_set_crossover_shape   m in 0..Q4_CROSSOVER_MAX sets the entry, m < 0
  *                           removes it; Q4_ERR_INVALID_ARGUMENT for N <= 0,
  *                           K <= 0 or m > Q4_CROSSOVER_MAX.
  *  q4_get_crossover_shape   the crossover calls of shape (N, K) use: the
  *                           entry if present, else q4_get_crossover_m().
- *  q4_clear_crossover_shapes removes every entry (the environment's table is
- *                           not read again).
+ *  q4_clear_crossover_shapes removes every entry, the measured ones
+ *                           included (neither they nor the environment's
+ *                           table are read again).
  * Thread-safe (one mutex); a change applies to calls made after it returns.
  */
 q4_status q4_set_crossover_shape(int N, int K, int m);
