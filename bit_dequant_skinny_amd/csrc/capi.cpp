@@ -28,14 +28,17 @@
 namespace {
 
 // Fused-versus-split threshold on MI355X (fused when M <= value) for weight
-// shapes without an entry of their own.  Timed at M = 17 .. 512 on the decode
+// shapes without an entry of their own.  Timed at M = 33 .. 512 on the decode
 // layer shapes (K, N) = (5120, 8192), (5120, 5120), (17408, 5120),
 // (8192, 8192), the 28672 x 8192 FFN, the 4096 x 4096 GEMV and the 248320 x
-// 2560 output projection: below M = 96 the fused kernels win on every shape
-// (1.4x to 2.7x at M = 64), and dequantize + tiled GEMM first wins between
-// M = 96 and M = 384 depending on the shape; 128 keeps every measured shape
-// within 5 % of its faster path up to its own crossover.
-constexpr int kDefaultCrossoverM = 128;
+// 2560 output projection: the fused path (the tiled kernel above 32 rows)
+// wins on every shape up to M = 192 (1.4x to 3x at M = 64), and dequantize +
+// tiled GEMM first wins between M = 256 and M = 512 depending on the shape.
+// The smallest of those switch points is the default: the routing principle
+// of the bitsandbytes pull request "[ROCm] Optimize
+// kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1"
+// (maintainer's comment) prefers a missed win to a regression.
+constexpr int kDefaultCrossoverM = 192;
 
 // Measured crossovers of those shapes: (N, K) -> the largest M the fused path
 // takes.  They seed the per-shape table, which the caller can change or clear.
@@ -43,16 +46,8 @@ struct ShapeEntry {
     int n, k, m;
 };
 constexpr ShapeEntry kMeasuredCrossovers[] = {
-    {8192, 5120, 128}, {5120, 5120, 192}, {5120, 17408, 192}, {8192, 8192, 128},
-    {28672, 8192, 192}, {4096, 4096, 256}, {248320, 2560, 192},
-};
-
-// Fused path above 32 token rows: the tiled kernel, except on shapes where
-// the skinny kernel's 32-row passes measured faster up to the given M (the
-// 28672 x 8192 FFN, whose skinny kernel streams its weights at the highest
-// rate of any shape: passes 152 us against tiled 211 us at M = 96).
-constexpr ShapeEntry kPassesPreferred[] = {
-    {28672, 8192, 192},
+    {8192, 5120, 384}, {5120, 5120, 384}, {5120, 17408, 192}, {8192, 8192, 384},
+    {28672, 8192, 384}, {4096, 4096, 512}, {248320, 2560, 384},
 };
 
 thread_local std::string tl_error;
@@ -237,29 +232,34 @@ bool known_dtype(int dt) { return dt == Q4_DTYPE_BF16 || dt == Q4_DTYPE_FP16 || 
 size_t dtype_size(int dt) { return dt == Q4_DTYPE_FP32 ? 4 : 2; }
 
 // Token rows above which the fused path takes the tiled matrix-core kernel
-// (each decoded weight serves a 64-row token block) instead of passes of the
-// skinny kernels over 32-row slabs, which read the packed weights once per
-// slab: 32, or the shape's entry in kPassesPreferred.  Q4_FUSED_TILED_MIN_M
-// (0 .. Q4_CROSSOVER_MAX) replaces both at first use.
+// (each decoded weight serves a 64-row token block) instead of the skinny
+// kernel's passes over 32-row slabs, which read the packed weights once per
+// slab.  Test hooks, read once: Q4_FUSED_TILED_MIN_M (0 .. Q4_CROSSOVER_MAX)
+// replaces the threshold, Q4_FUSED_TILED_LAYOUT (0 or 1) forces the tiled
+// kernel's work layout.
 constexpr int kFusedTiledMinM = 32;
 
-int fused_tiled_min_m(int N, int K) {
-    static const int env = [] {
-        if (const char *e = std::getenv("Q4_FUSED_TILED_MIN_M")) {
-            char *end = nullptr;
-            const long x = std::strtol(e, &end, 10);
-            if (end != e && *end == '\0' && x >= 0 && x <= Q4_CROSSOVER_MAX) return (int)x;
-        }
-        return -1;
-    }();
-    if (env >= 0) return env;
-    for (const ShapeEntry &x : kPassesPreferred)
-        if (x.n == N && x.k == K) return x.m;
-    return kFusedTiledMinM;
+int env_int(const char *name, int lo, int hi, int dflt) {
+    if (const char *e = std::getenv(name)) {
+        char *end = nullptr;
+        const long x = std::strtol(e, &end, 10);
+        if (end != e && *end == '\0' && x >= lo && x <= hi) return (int)x;
+    }
+    return dflt;
+}
+
+int fused_tiled_min_m() {
+    static const int v = env_int("Q4_FUSED_TILED_MIN_M", 0, Q4_CROSSOVER_MAX, kFusedTiledMinM);
+    return v;
+}
+
+int fused_tiled_layout() {
+    static const int v = env_int("Q4_FUSED_TILED_LAYOUT", 0, 1, -1);
+    return v;
 }
 
 bool fused_tiled(int rows, int N, int K, int bs_log2) {
-    return bs_log2 >= 6 && rows > fused_tiled_min_m(N, K) && q4::q4_fused_tiled_fits(rows, N, K);
+    return bs_log2 >= 6 && rows > fused_tiled_min_m() && q4::q4_fused_tiled_fits(rows, N, K);
 }
 
 q4_status current_device(int *device) {
@@ -271,18 +271,18 @@ q4_status current_device(int *device) {
 
 // The tiled fused kernel on bf16 activations (rows = token rows, or np*M rows
 // of activation planes).  When K is split over workgroups (ksplit > 1) the
-// kernel writes ksplit fp32 partial outputs to `parts` and one pass sums them
-// in part order with the bias.
+// kernel writes ksplit fp32 partial outputs to `parts` for the caller to sum.
 q4_status run_fused_tiled(const uint16_t *A, const uint8_t *Wp, const float *am, const float *cb,
-                          const void *bias, int rows, int N, int K, int bs_log2, int ksplit,
-                          float *parts, void *C, int c_dt, hipStream_t s) {
-    if (ksplit == 1)
+                          const void *bias, int rows, int N, int K, int bs_log2,
+                          const q4::TiledPlan &plan, float *parts, void *C, int c_dt,
+                          hipStream_t s) {
+    if (plan.ksplit == 1)
         return launch_checked("fused", [&] {
-            return q4::launch_q4_fused_tiled(A, Wp, am, cb, bias, rows, N, K, bs_log2, 1, C,
+            return q4::launch_q4_fused_tiled(A, Wp, am, cb, bias, rows, N, K, bs_log2, plan, C,
                                              c_dt, s);
         });
     return launch_checked("fused", [&] {
-        return q4::launch_q4_fused_tiled(A, Wp, am, cb, nullptr, rows, N, K, bs_log2, ksplit,
+        return q4::launch_q4_fused_tiled(A, Wp, am, cb, nullptr, rows, N, K, bs_log2, plan,
                                          parts, Q4_DTYPE_FP32, s);
     });
 }
@@ -300,7 +300,8 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
     if (a_dt != Q4_DTYPE_BF16 && bs_log2 >= 6 && q4::q4_fused_mfma_fits(M, N, K))
         return run_fused_planes(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, C, c_dt, s);
     if (a_dt == Q4_DTYPE_BF16 && fused_tiled(M, N, K, bs_log2)) {
-        const int ks = q4::q4_fused_tiled_ksplit(M, N, K);
+        const q4::TiledPlan plan = q4::q4_fused_tiled_plan(M, N, K, 4, fused_tiled_layout());
+        const int ks = plan.ksplit;
         float *parts = nullptr;
         if (ks > 1) {
             int device = 0;
@@ -312,7 +313,7 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
             parts = static_cast<float *>(ws);
         }
         q4_status st = run_fused_tiled(static_cast<const uint16_t *>(A), Wp, am, cb, bias, M, N,
-                                       K, bs_log2, ks, parts, C, c_dt, s);
+                                       K, bs_log2, plan, parts, C, c_dt, s);
         if (st != Q4_OK || ks == 1) return st;
         return launch_checked("plane sum", [&] {
             return q4::launch_sum_planes(parts, ks, M, N, bias, C, c_dt, s);
@@ -346,8 +347,10 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
     const int np = q4::activation_planes(a_dt);
     const int rows = np * M;
     const bool tiled = fused_tiled(rows, N, K, bs_log2);
-    int ks = tiled ? q4::q4_fused_tiled_ksplit(rows, N, K) : 1;
-    if (np * ks > 4) ks = 4 / np;
+    // at most 4 partial slabs in all (planes times K parts)
+    const q4::TiledPlan plan =
+        tiled ? q4::q4_fused_tiled_plan(rows, N, K, 4 / np, fused_tiled_layout()) : q4::TiledPlan{0, 1};
+    const int ks = plan.ksplit;
     const size_t plane_bytes = (size_t)rows * (size_t)K * 2;
     const size_t part_off = (plane_bytes + 255) & ~(size_t)255;
     void *ws = nullptr;
@@ -359,7 +362,7 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
         return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s);
     });
     if (st != Q4_OK) return st;
-    st = tiled ? run_fused_tiled(planes, Wp, am, cb, nullptr, rows, N, K, bs_log2, ks, parts,
+    st = tiled ? run_fused_tiled(planes, Wp, am, cb, nullptr, rows, N, K, bs_log2, plan, parts,
                                  parts, Q4_DTYPE_FP32, s)
                : run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, rows, N, K, bs_log2,
                            parts, Q4_DTYPE_FP32, s);

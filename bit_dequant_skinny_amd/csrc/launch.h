@@ -44,15 +44,22 @@ hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *b
                              int c_dt, hipStream_t s);
 bool q4_fused_mfma_fits(int M, int N, int K);
 
-// Fused 4-bit GEMM with output tiles of 64 (32 for M <= 32) tokens x 64
-// features (bf16 A, blocksize >= 64), for tens to hundreds of token rows.
+// Fused 4-bit GEMM with output tiles of 64 (32 for M <= 32) tokens (bf16 A,
+// blocksize >= 64), for tens to hundreds of token rows.  Layout 0: 4 waves
+// split K over a 64-feature tile; layout 1: 8 waves split a 256-feature tile.
 // ksplit > 1 writes ksplit fp32 partial outputs [ksplit][M][N] (no bias) for
-// launch_sum_planes to add; q4_fused_tiled_ksplit picks the split.
+// launch_sum_planes to add.  q4_fused_tiled_plan picks both for a shape
+// (ksplit <= max_ks; layout -1 = by shape, 0 or 1 = forced).
+struct TiledPlan {
+    int layout;
+    int ksplit;
+};
 bool q4_fused_tiled_fits(int M, int N, int K);
-int q4_fused_tiled_ksplit(int M, int N, int K);
+TiledPlan q4_fused_tiled_plan(int M, int N, int K, int max_ks, int layout);
 hipError_t launch_q4_fused_tiled(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
                                  const float *codebook, const void *bias, int M, int N, int K,
-                                 int bs_log2, int ksplit, void *C, int c_dt, hipStream_t s);
+                                 int bs_log2, const TiledPlan &plan, void *C, int c_dt,
+                                 hipStream_t s);
 
 // Tiled bf16 GEMM (bf16 A, 128 x 128 tiles through LDS) for the split path at
 // larger M; gemm_tiled_fits checks its 32-bit offsets.

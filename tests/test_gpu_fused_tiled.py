@@ -9,8 +9,11 @@ kernel takes (64, 128, 256), the K-split partial sums, every activation and
 output type with a bias, and the 28672 x 8192 FFN at full size on sampled
 columns.  Structured checks: 2A gives 2C bit for bit, repeated calls are
 bitwise equal, zero and extreme block scales, and one-hot rows return the
-dequantized weights.  A child process lowers the tiled threshold to 0 to run
-the 32-row tile variant on 1..32 rows.
+dequantized weights.  The kernel has two work layouts (waves splitting K over
+64-feature tiles, or splitting 256-feature tiles by N with the activations
+staged through LDS), chosen per shape; child processes force each layout on
+every case, and lower the tiled threshold to 0 to run the 32-row tiles on
+1..32 rows.
 """
 import os
 import subprocess
@@ -165,26 +168,81 @@ import torch
 import bit_dequant_skinny_amd as q4
 import oracle, synth
 sys.path.insert(0, "tests")
-from gpu_util import assert_within_tolerance, bf16_host, q4_to_dev
+from gpu_util import (assert_within_tolerance, bf16_host, host_f64, q4_to_dev, to_dev,
+                      to_dev_dtype)
 
-for M in (1, 5, 16, 17, 32):
-    for (N, K, bs) in ((300, 1088, 64), (70, 2048, 128)):
-        p = synth.q4_problem(M, N, K, bs, config=85, shape=N % 7,
-                             codebook=synth.random_codebook(90))
-        A, Wp, am, cb = q4_to_dev(p)
-        C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused")
-        torch.cuda.synchronize()
-        Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
-        assert_within_tolerance(bf16_host(C), Cr, S, "32-row tiles M=%d N=%d" % (M, N))
-        print("ok", M, N, flush=True)
+which = sys.argv[1]
+sync = torch.cuda.synchronize
+if which == "few_rows":
+    cases = [(M, N, K, bs) for M in (1, 5, 16, 17, 32)
+             for (N, K, bs) in ((300, 1088, 64), (70, 2048, 128), (600, 512, 64))]
+else:
+    cases = [(M, N, K, bs) for M in (33, 64, 100, 129)
+             for (N, K, bs) in ((300, 1088, 64), (64, 4096, 128), (517, 2048, 256),
+                                (1000, 640, 64), (2100, 1024, 64))]
+for (M, N, K, bs) in cases:
+    p = synth.q4_problem(M, N, K, bs, config=85, shape=N % 7, codebook=synth.random_codebook(90))
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused")
+    C2 = q4.q4_gemm_skinny(A * 2, Wp, am, cb, bs, path="fused")
+    sync()
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    assert_within_tolerance(bf16_host(C), Cr, S, "%s M=%d N=%d K=%d" % (which, M, N, K))
+    assert torch.equal(C2, C * 2), "2A != 2C"
+    print("ok", M, N, K, flush=True)
+if which != "few_rows":
+    M, N, K, bs = 48, 333, 1024, 64
+    p = synth.q4_problem(M, N, K, bs, config=83, codebook=synth.random_codebook(87))
+    _, Wp, am, cb = q4_to_dev(p)
+    for adt in ("bf16", "fp16", "fp32"):
+        for cdt, tdt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+            A_h = synth.activations(M, K, 88, adt)
+            b_h = synth.bias(N, 89, cdt)
+            C = q4.q4_gemm_skinny(to_dev_dtype(A_h, adt), Wp, am, cb, bs, path="fused",
+                                  bias=to_dev_dtype(b_h, cdt), out_dtype=tdt)
+            sync()
+            Cr, S = oracle.q4_gemm_ex(A_h, adt, p["Wpacked"], p["absmax"], p["codebook"], M, N,
+                                      K, bs, bias=b_h, bias_dtype=cdt)
+            assert_within_tolerance(None, Cr, S, "%s %s->%s" % (which, adt, cdt), out=cdt,
+                                    values=host_f64(C))
+            print("ok", adt, cdt, flush=True)
+print("done", flush=True)
 '''
 
 
-def test_fused_tiled_32_row_tiles_on_few_rows():
+def _child(which, env_extra):
     env = dict(os.environ)
-    env["Q4_FUSED_TILED_MIN_M"] = "0"
+    env.update(env_extra)
     env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
-    r = subprocess.run([sys.executable, "-c", CHILD], cwd=ROOT, env=env, capture_output=True,
-                       text=True, timeout=240)
+    r = subprocess.run([sys.executable, "-c", CHILD, which], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=280)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
-    assert r.stdout.count("ok ") == 10
+    assert "done" in r.stdout
+    return r.stdout
+
+
+@pytest.mark.parametrize("layout", ["0", "1"])
+def test_fused_tiled_each_layout(layout):
+    """Every case with the layout forced: 20 shapes and 6 type pairs."""
+    out = _child("layouts", {"Q4_FUSED_TILED_LAYOUT": layout})
+    assert out.count("ok ") == 20 + 6
+
+
+@pytest.mark.parametrize("layout", ["0", "1"])
+def test_fused_tiled_32_row_tiles_on_few_rows(layout):
+    out = _child("few_rows", {"Q4_FUSED_TILED_MIN_M": "0", "Q4_FUSED_TILED_LAYOUT": layout})
+    assert out.count("ok ") == 15
+
+
+def test_fused_tiled_n_split_layout_at_scale():
+    """A shape the dispatcher gives the N-split layout (many 256-feature
+    tiles): 100 rows over 9984 features, K = 1088 (ragged), sampled columns."""
+    M, N, K, bs = 100, 9984, 1088, 64
+    p = synth.q4_problem(M, N, K, bs, config=86)
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused")
+    _sync()
+    cols = sample_cols(N, 600, 91)
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs,
+                           cols=cols)
+    assert_within_tolerance(bf16_host(C)[:, cols], Cr, S, "N-split at scale")
