@@ -12,6 +12,9 @@ Workloads (seeded synthetic stand-ins for the pages' model layers):
   C4 bf16 skinny, M=1..5, K=2560, N in {96, 2048, 16384, 31040}, with and
      without bias
   C5 K=2560, N=248320: fused 4-bit at M=1,8 and bf16 skinny at M=1..5
+Beyond the decode sizes, the dispatcher's routes at these shapes: the tiled
+fused kernel in both work layouts (M = 64 .. 384) and dequantize + tiled GEMM
+above the shape's crossover (M = 400 on the decode layers).
 """
 import numpy as np
 import pytest
@@ -60,6 +63,18 @@ def test_c3_decode_layers(shape, M):
     _q4_case(M, N, K, config=2, shape=shape)
 
 
+@pytest.mark.parametrize("M", [64, 200, 400])
+@pytest.mark.parametrize("shape", range(len(C3)))
+def test_c3_beyond_16_rows(shape, M):
+    K, N = C3[shape]
+    _q4_case(M, N, K, config=2, shape=shape, ncols=256)
+
+
+@pytest.mark.parametrize("M", [100, 384])
+def test_c2_ffn_beyond_16_rows(M):
+    _q4_case(M, 28672, 8192, config=1, shape=0, ncols=256)
+
+
 @pytest.mark.parametrize("shape", range(len(C3)))
 def test_c3_split_path(shape):
     K, N = C3[shape]
@@ -90,7 +105,7 @@ def test_c4_bf16_skinny(shape, M, with_bias):
     _bf16_case(M, C4_N[shape], 2560, with_bias, config=3, shape=shape)
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 8, 64])
 def test_c5_lm_head_q4(M):
     _q4_case(M, 248320, 2560, config=4, shape=0)
 
