@@ -214,8 +214,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // e >> sh and (e + 1) >> sh: one 8-byte read at the even block below, then
     // a select (both halves for bs = 64, one half twice for bs = 128 and 256).
     const int sh = bs_log2 - 6;
-    auto read_scales = [&](const float *p, int pick, float (&out)[2]) {
-        const floatx2 a2 = *reinterpret_cast<const floatx2 *>(p);
+    auto read_scales = [&](const float *p) { return *reinterpret_cast<const floatx2 *>(p); };
+    auto pick_scales = [&](const floatx2 &a2, int pick, float (&out)[2]) {
         out[0] = pick == 1 ? a2[1] : a2[0];
         out[1] = pick == 0 ? a2[0] : a2[1];
     };
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // to the second block's activations.
     constexpr int DB = MB == 1 ? 2 : 1;
     uint2 e[DB][16];
-    float am[2][2];
+    floatx2 am[2];  // raw scale pairs; the pick is applied where they are used
     decode(wbuf[0][0], e[0]);
     issue(wbuf[0][0], 0);
 
@@ -342,12 +342,32 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         const int s_blk = (16 * (us % P) + 2 * wave) >> sh;
         const int s_pick = sh == 0 ? -1 : (s_blk & 1);
         const float *scs = &scl[qp & 1][j * kScaleStride + (s_blk & ~1)];
-        read_scales(scs, s_pick, am[(us * TB) & 1]);
+        am[(us * TB) & 1] = read_scales(scs);
 #pragma unroll
         for (int tr = 0; tr < TB; ++tr) {
             const int cur = (us * TB + tr) & 1;
             const int ecur = DB == 2 ? cur : 0, enext = DB == 2 ? cur ^ 1 : 0;
             const uint2 *ev = e[ecur];
+            // The next unit's table reads, scale read and ring refill: before
+            // this unit's MFMAs when the decode is double-buffered, so the
+            // reads fly while the MFMAs run; after them otherwise (one buffer).
+            auto next_unit = [&]() {
+                if (tr + 1 < TB) {
+                    decode(wbuf[r_cur][tr + 1], e[enext]);
+                    am[cur ^ 1] = read_scales(scs + (tr + 1) * 16 * kScaleStride);
+                    issue(wbuf[r_cur][tr + 1], tr + 1);
+                } else {
+                    // tile 0 of the next slot: its weights are in the ring; its
+                    // scales are read at the start of that slot
+                    w_advance();
+                    decode(wbuf[r_next][0], e[enext]);
+                    issue(wbuf[r_next][0], 0);
+                }
+            };
+            if constexpr (DB == 2) {
+                next_unit();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             // two independent chains per token block, one per 64-wide block
             floatx4 D0[MB], D1[MB];
 #pragma unroll
@@ -363,23 +383,21 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (tr + 1 < TB) {
-                decode(wbuf[r_cur][tr + 1], e[enext]);
-                read_scales(scs + (tr + 1) * 16 * kScaleStride, s_pick, am[cur ^ 1]);
-                issue(wbuf[r_cur][tr + 1], tr + 1);
-            } else {
-                // tile 0 of the next slot: its weights are in the ring; its
-                // scales are read at the start of that slot
-                w_advance();
-                decode(wbuf[r_next][0], e[enext]);
-                issue(wbuf[r_next][0], 0);
+            if constexpr (DB == 1) {
+                next_unit();
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            // The pick (for blocksizes above 64) runs here, not next to the
+            // read: a use right after the read would wait for it, and LDS
+            // reads complete in order, so also for the table reads of the
+            // next unit issued just before it.
+            float sc[2];
+            pick_scales(am[cur], s_pick, sc);
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
                 for (int r = 0; r < SR; ++r)
-                    acc[tr][b][r] = fmaf(am[cur][1], D1[b][r], fmaf(am[cur][0], D0[b][r], acc[tr][b][r]));
+                    acc[tr][b][r] = fmaf(sc[1], D1[b][r], fmaf(sc[0], D0[b][r], acc[tr][b][r]));
         }
         // At the end of a period, publish the next period's scales.  The
         // buffer written here was last read in the previous period, which
