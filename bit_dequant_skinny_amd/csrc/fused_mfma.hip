@@ -242,21 +242,28 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     };
 
     // Table lookups of one tile: 16 packed bytes -> 32 bf16 hi/lo pairs.
-    auto decode = [&](const uint4 &wv, uint2 (&ev)[16]) {
-        uint32_t x[4] = {wv.x, wv.y, wv.z, wv.w};
+    auto swap_w = [&](const uint4 &wv, uint32_t (&x)[4]) {
+        x[0] = wv.x; x[1] = wv.y; x[2] = wv.z; x[3] = wv.w;
         // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
         // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
         const auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
         const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
         x[0] = s02[0]; x[2] = s02[1];
         x[1] = s13[0]; x[3] = s13[1];
+    };
+    auto lookups = [&](const uint32_t (&x)[4], uint2 (&ev)[16], int i0, int i1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = i0; i < i1; ++i) {
             // address = byte * 256 + lane_off: byte 1 from the packed
             // dword, byte 0 from lane_off, bytes 2-3 zero
             const uint32_t addr = __builtin_amdgcn_perm(x[i >> 2], lane_off, 0x0c0c0000u | ((4 + (i & 3)) << 8));
             ev[i] = *reinterpret_cast<const uint2 *>(tab_bytes + addr);
         }
+    };
+    auto decode = [&](const uint4 &wv, uint2 (&ev)[16]) {
+        uint32_t x[4];
+        swap_w(wv, x);
+        lookups(x, ev, 0, 16);
     };
 
     // Prologue: the scales and activations of slot 0, RS slots of weights,
@@ -348,43 +355,66 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             const int cur = (us * TB + tr) & 1;
             const int ecur = DB == 2 ? cur : 0, enext = DB == 2 ? cur ^ 1 : 0;
             const uint2 *ev = e[ecur];
-            // The next unit's table reads, scale read and ring refill: before
-            // this unit's MFMAs when the decode is double-buffered, so the
-            // reads fly while the MFMAs run; after them otherwise (one buffer).
-            auto next_unit = [&]() {
+            // two independent chains per token block, one per 64-wide block
+            floatx4 D0[MB], D1[MB];
+#pragma unroll
+            for (int b = 0; b < MB; ++b) D0[b] = D1[b] = zerof;
+            auto mfma_steps = [&](int s0, int s1) {
+#pragma unroll
+                for (int s = s0; s < s1; ++s) {
+                    const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
+                    const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
+#pragma unroll
+                    for (int b = 0; b < MB; ++b) {
+                        D0[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][s]), as_bf16x8(b0), D0[b]);
+                        D1[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][4 + s]), as_bf16x8(b1), D1[b]);
+                    }
+                }
+            };
+            if constexpr (DB == 2) {
+                // The next unit's decode in two halves around this unit's
+                // MFMAs, so its table reads fly while the MFMAs run.  Halves
+                // of 8 reads keep the reads in flight at any wait within the
+                // 4-bit LDS counter (at most 15 outstanding): with all 17
+                // reads issued at once, waiting for an older read also waited
+                // for the first of them.
+                uint32_t xn[4];
+                if (tr + 1 < TB) {
+                    swap_w(wbuf[r_cur][tr + 1], xn);
+                } else {
+                    // tile 0 of the next slot: its weights are in the ring;
+                    // its scales are read at the start of that slot
+                    w_advance();
+                    swap_w(wbuf[r_next][0], xn);
+                }
+                lookups(xn, e[enext], 0, 8);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_steps(0, 2);
+                __builtin_amdgcn_sched_barrier(0);
+                lookups(xn, e[enext], 8, 16);
+                if (tr + 1 < TB) {
+                    am[cur ^ 1] = read_scales(scs + (tr + 1) * 16 * kScaleStride);
+                    issue(wbuf[r_cur][tr + 1], tr + 1);
+                } else {
+                    issue(wbuf[r_next][0], 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_steps(2, 4);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // One decode buffer: the next unit's table reads follow this
+                // unit's MFMAs.
+                mfma_steps(0, 4);
+                __builtin_amdgcn_sched_barrier(0);
                 if (tr + 1 < TB) {
                     decode(wbuf[r_cur][tr + 1], e[enext]);
                     am[cur ^ 1] = read_scales(scs + (tr + 1) * 16 * kScaleStride);
                     issue(wbuf[r_cur][tr + 1], tr + 1);
                 } else {
-                    // tile 0 of the next slot: its weights are in the ring; its
-                    // scales are read at the start of that slot
                     w_advance();
                     decode(wbuf[r_next][0], e[enext]);
                     issue(wbuf[r_next][0], 0);
                 }
-            };
-            if constexpr (DB == 2) {
-                next_unit();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // two independent chains per token block, one per 64-wide block
-            floatx4 D0[MB], D1[MB];
-#pragma unroll
-            for (int b = 0; b < MB; ++b) D0[b] = D1[b] = zerof;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 b0 = make_uint4(ev[2 * s].x, ev[2 * s].y, ev[2 * s + 1].x, ev[2 * s + 1].y);
-                const uint4 b1 = make_uint4(ev[8 + 2 * s].x, ev[8 + 2 * s].y, ev[9 + 2 * s].x, ev[9 + 2 * s].y);
-#pragma unroll
-                for (int b = 0; b < MB; ++b) {
-                    D0[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][s]), as_bf16x8(b0), D0[b]);
-                    D1[b] = mfma_bf16_16x16x32(as_bf16x8(adup[b][4 + s]), as_bf16x8(b1), D1[b]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (DB == 1) {
-                next_unit();
                 __builtin_amdgcn_sched_barrier(0);
             }
             // The pick (for blocksizes above 64) runs here, not next to the
