@@ -298,7 +298,10 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // to the second block's activations.
     constexpr int DB = MB == 1 ? 2 : 1;
     uint2 e[DB][16];
-    floatx2 am[2];  // raw scale pairs; the pick is applied where they are used
+    // Scale pairs of the current and the next unit: with the double-buffered
+    // decode raw (the pick is applied where they are used), else picked at
+    // the read (fewer live registers for two token blocks).
+    floatx2 am[2];
     decode(wbuf[0][0], e[0]);
     issue(wbuf[0][0], 0);
 
@@ -348,8 +351,13 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         if constexpr (us % P == 0) load_scales(snext);  // and the next period's scales
         const int s_blk = (16 * (us % P) + 2 * wave) >> sh;
         const int s_pick = sh == 0 ? -1 : (s_blk & 1);
+        auto picked = [&](const floatx2 &a2) {
+            float o[2];
+            pick_scales(a2, s_pick, o);
+            return floatx2{o[0], o[1]};
+        };
         const float *scs = &scl[qp & 1][j * kScaleStride + (s_blk & ~1)];
-        am[(us * TB) & 1] = read_scales(scs);
+        am[(us * TB) & 1] = DB == 2 ? read_scales(scs) : picked(read_scales(scs));
 #pragma unroll
         for (int tr = 0; tr < TB; ++tr) {
             const int cur = (us * TB + tr) & 1;
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 __builtin_amdgcn_sched_barrier(0);
                 if (tr + 1 < TB) {
                     decode(wbuf[r_cur][tr + 1], e[enext]);
-                    am[cur ^ 1] = read_scales(scs + (tr + 1) * 16 * kScaleStride);
+                    am[cur ^ 1] = picked(read_scales(scs + (tr + 1) * 16 * kScaleStride));
                     issue(wbuf[r_cur][tr + 1], tr + 1);
                 } else {
                     w_advance();
@@ -417,12 +425,12 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // The pick (for blocksizes above 64) runs here, not next to the
-            // read: a use right after the read would wait for it, and LDS
-            // reads complete in order, so also for the table reads of the
-            // next unit issued just before it.
-            float sc[2];
-            pick_scales(am[cur], s_pick, sc);
+            // With the double-buffered decode the pick (for blocksizes above
+            // 64) runs here, not next to the read: a use right after the read
+            // would wait for it, and LDS reads complete in order, so also for
+            // the table reads of the next unit issued just before it.
+            float sc[2] = {am[cur][0], am[cur][1]};
+            if constexpr (DB == 2) pick_scales(am[cur], s_pick, sc);
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
