@@ -233,10 +233,12 @@ size_t dtype_size(int dt) { return dt == Q4_DTYPE_FP32 ? 4 : 2; }
 
 // Token rows above which the fused path takes the tiled matrix-core kernel
 // (each decoded weight serves a 64-row token block) instead of the skinny
-// kernel's passes over 32-row slabs, which read the packed weights once per
-// slab.  Test hooks, read once: Q4_FUSED_TILED_MIN_M (0 .. Q4_CROSSOVER_MAX)
-// replaces the threshold, Q4_FUSED_TILED_LAYOUT (0 or 1) forces the tiled
-// kernel's work layout.
+// kernel, which reads the packed weights once per pass of up to 32 rows: 32,
+// or 16 on shapes where the skinny kernel runs 17..32 rows as two 16-row
+// launches (8 tiles per chunk; measured at 248320 x 2560, M = 32: 174 us
+// tiled, 210 us in two launches).  Test hooks, read once:
+// Q4_FUSED_TILED_MIN_M (0 .. Q4_CROSSOVER_MAX) replaces the threshold,
+// Q4_FUSED_TILED_LAYOUT (0 or 1) forces the tiled kernel's work layout.
 constexpr int kFusedTiledMinM = 32;
 
 int env_int(const char *name, int lo, int hi, int dflt) {
@@ -248,9 +250,10 @@ int env_int(const char *name, int lo, int hi, int dflt) {
     return dflt;
 }
 
-int fused_tiled_min_m() {
-    static const int v = env_int("Q4_FUSED_TILED_MIN_M", 0, Q4_CROSSOVER_MAX, kFusedTiledMinM);
-    return v;
+int fused_tiled_min_m(int N) {
+    static const int env = env_int("Q4_FUSED_TILED_MIN_M", 0, Q4_CROSSOVER_MAX, -1);
+    if (env >= 0) return env;
+    return q4::q4_fused_mfma_two_blocks(N) ? kFusedTiledMinM : 16;
 }
 
 int fused_tiled_layout() {
@@ -259,7 +262,7 @@ int fused_tiled_layout() {
 }
 
 bool fused_tiled(int rows, int N, int K, int bs_log2) {
-    return bs_log2 >= 6 && rows > fused_tiled_min_m() && q4::q4_fused_tiled_fits(rows, N, K);
+    return bs_log2 >= 6 && rows > fused_tiled_min_m(N) && q4::q4_fused_tiled_fits(rows, N, K);
 }
 
 q4_status current_device(int *device) {

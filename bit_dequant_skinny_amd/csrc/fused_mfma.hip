@@ -567,6 +567,10 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
 // so the matrix plus 256 rows must stay below 4 GiB; activation offsets reach
 // 32 rows of K (the lanes of absent tokens read past the end of A), which must
 // stay below 4 GiB as well.
+// One launch takes two token blocks unless 8 tiles per chunk leave no
+// registers for the second (then 17..32 rows run as two 16-row launches).
+bool q4_fused_mfma_two_blocks(int N) { return tiles_per_chunk(N) < 8; }
+
 bool q4_fused_mfma_fits(int M, int N, int K) {
     (void)M;
     return ((uint64_t)N + 256) * (uint64_t)K / 2 < (1ull << 32) &&

@@ -43,6 +43,7 @@ hipError_t launch_split_planes(const void *A, int a_dt, size_t n, uint16_t *plan
 hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *bias, void *C,
                              int c_dt, hipStream_t s);
 bool q4_fused_mfma_fits(int M, int N, int K);
+bool q4_fused_mfma_two_blocks(int N);
 
 // Fused 4-bit GEMM with output tiles of 64 (32 for M <= 32) tokens (bf16 A,
 // blocksize >= 64), for tens to hundreds of token rows.  Layout 0: 4 waves

@@ -5,7 +5,9 @@ blocks of 16 token rows that share each decoded weight unit; matrices of more
 than 8 tiles per CU run that pass as two 16-row launches instead.  Each output
 is computed by the same MFMA sequence and summation order as in a 16-row
 pass, so the two-block result must equal the two 16-row passes bit for bit,
-and it must meet the elementwise tolerance against the fp64 oracle.
+and it must meet the elementwise tolerance against the fp64 oracle.  Shapes
+with 8 tiles per chunk (more than 2048 weight rows per CU) take the tiled
+kernel at 17..32 rows instead; they are checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -36,7 +38,7 @@ def test_two_block_pass_parity(M, N, K, bs):
 
 
 @pytest.mark.parametrize("M", [18, 32])
-@pytest.mark.parametrize("N,K", [(300, 1024), (28672, 256), (40000, 128)])
+@pytest.mark.parametrize("N,K", [(300, 1024), (28672, 256)])
 def test_two_block_pass_equals_16_row_passes(M, N, K):
     """Rows 0..15 and 16..M-1 computed in one pass equal two separate calls."""
     bs = 64
@@ -47,6 +49,19 @@ def test_two_block_pass_equals_16_row_passes(M, N, K):
     C1 = bf16_host(q4.q4_gemm_skinny(A[16:].contiguous(), Wp, am, cb, bs, path="fused"))
     _sync()
     assert np.array_equal(C, np.concatenate([C0, C1], axis=0))
+
+
+@pytest.mark.parametrize("M", [17, 32])
+def test_eight_tile_shapes_take_the_tiled_kernel(M):
+    N, K, bs = 40000, 128, 64
+    p = synth.q4_problem(M, N, K, bs, config=64)
+    A, Wp, am, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused")
+    _sync()
+    cols = sample_cols(N, 512, 65 + M)
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs,
+                           cols=cols)
+    assert_within_tolerance(bf16_host(C)[:, cols], Cr, S, "8-tile shape M=%d" % M)
 
 
 def test_two_block_one_hot_rows_return_dequantized_rows():
