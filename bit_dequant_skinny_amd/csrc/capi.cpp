@@ -294,9 +294,10 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
                            const float *cb, const void *bias, int M, int N, int K, int bs_log2,
                            void *C, int c_dt, hipStream_t s);
 
-// bf16 activations: the tiled kernel above kFusedTiledMinM rows, else the
+// bf16 activations: the tiled kernel above fused_tiled_min_m rows, else the
 // skinny kernels in passes of up to Q4_FUSED_PASS_M token rows over
-// consecutive row slabs, each streaming the packed weights once more.
+// consecutive row slabs, each streaming the packed weights once more (more
+// than one pass only where the tiled kernel cannot run).
 q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
                     const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
                     hipStream_t s) {

@@ -48,11 +48,12 @@ typedef enum q4_status {
 enum { Q4_DTYPE_BF16 = 0, Q4_DTYPE_FP32 = 1, Q4_DTYPE_FP16 = 2 };
 enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
 
-/* Token rows one fused 4-bit pass handles; the fused path runs larger M in
- * passes over slabs of this many rows, each pass streaming the packed weights
- * again.  (A pass of bf16 activations runs as one launch; other element
- * types, blocksize 32 and matrices of more than 2048 * 16 rows per 256 CUs
- * run a pass as launches of 16 rows.) */
+/* Token rows one pass of the skinny fused kernels handles.  Where the tiled
+ * kernel cannot run (blocksize 32, shapes beyond its 32-bit offsets), the
+ * fused path runs larger M in passes over slabs of this many rows, each pass
+ * streaming the packed weights again (as launches of 16 rows for other
+ * element types than bf16, blocksize 32 and matrices of more than 2048 * 16
+ * rows per 256 CUs). */
 #define Q4_FUSED_PASS_M 32
 /* Largest crossover value q4_set_crossover_m accepts. */
 #define Q4_CROSSOVER_MAX 65536
@@ -83,13 +84,14 @@ enum { Q4_PATH_AUTO = 0, Q4_PATH_FUSED = 1, Q4_PATH_SPLIT = 2 };
  *  Q4_ERR_UNSUPPORTED: blocksize not in {32, 64, 128, 256}; M or N above
  *    2^30/K-sized limits (N * K / 2 must fit in 2^40 bytes).
  *  Which kernel runs: M <= the crossover (q4_get_crossover_shape(N, K)) take
- *  the fused path: up to 32 rows the skinny matrix-core kernel, above that
- *  the tiled matrix-core kernel (output tiles of 64 tokens x 64 features,
- *  K split over workgroups into fp32 partials in the workspace when its
- *  tiles cannot fill the GPU), or on shapes where they measured faster,
- *  passes of the skinny kernel over Q4_FUSED_PASS_M rows.  Other M take the
- *  split path (dequantize to bf16 into a library-owned workspace of N*K*2
- *  bytes, then an MFMA bf16 GEMM).
+ *  the fused path: up to 32 rows (16 on shapes of more than 2048 weight rows
+ *  per CU) the skinny matrix-core kernel, above that the tiled matrix-core
+ *  kernel (output tiles of 64 tokens x 64 or 256 features, K split over
+ *  workgroups into fp32 partials in the workspace when its tiles cannot
+ *  fill the GPU).  Blocksize 32 (and shapes beyond the kernels' 32-bit
+ *  offsets) take the vector-ALU kernel in passes of Q4_FUSED_PASS_M rows.
+ *  Other M take the split path (dequantize to bf16 into a library-owned
+ *  workspace of N*K*2 bytes, then an MFMA bf16 GEMM).
  */
 q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *absmax,
                          const float *codebook, int M, int N, int K, int blocksize,
