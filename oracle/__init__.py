@@ -21,6 +21,8 @@ Function map (steps as numbered in the C file):
   dequant_f16     O9  O3 rounded to binary16
   q4_gemm_ex      O10 O5 with bf16 / fp16 / fp32 activations and a bias
   quantize        O11 blockwise absmax + nearest-entry codes (inverse of O3)
+  tile_offset     O12 where byte j of packed row n sits in the tile layout
+  repack_tiles    O12 the row-major packed bytes moved to the tile layout
 
 Element types are named "bf16", "fp16", "fp32" (uint16 bit patterns for the
 two 16-bit types, float32 arrays for fp32).
@@ -95,6 +97,9 @@ class Oracle:
                                           P, I, P, P]
         lib.oracle_quantize.argtypes = [P, ctypes.c_int, P, I, I, I, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_tile_offset.argtypes = [I, I, I, I]
+        lib.oracle_tile_offset.restype = I
+        lib.oracle_repack_tiles.argtypes = [P, I, I, P]
         self.lib = lib
         self.path = lib_path
 
@@ -224,6 +229,16 @@ class Oracle:
         absmax = np.empty((N, K // bs), dtype=np.float32)
         self.lib.oracle_quantize(_ptr(Wa), code, _ptr(cb), N, K, bs, _ptr(codes), _ptr(absmax))
         return codes, absmax
+
+    def tile_offset(self, N, K, n, j) -> int:
+        return int(self.lib.oracle_tile_offset(N, K, n, j))
+
+    def repack_tiles(self, Wpacked, N, K) -> np.ndarray:
+        """uint8 [N, K/2] holding the tile layout of row-major Wpacked."""
+        Wp = _c(Wpacked, np.uint8)
+        out = np.empty((N, K // 2), dtype=np.uint8)
+        self.lib.oracle_repack_tiles(_ptr(Wp), N, K, _ptr(out))
+        return out
 
     def gemm_f32w(self, A_bf16, W_f32, M, N, K):
         A, W = _c(A_bf16, np.uint16), _c(W_f32, np.float32)

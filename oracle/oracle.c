@@ -391,6 +391,33 @@ void oracle_quantize(const void *W, int w_dtype, const float *codebook, int64_t 
         }
 }
 
+/* O12  The tile layout of the packed weights (a layout of this library, not
+ * of the pages; the pages leave the packed-weight layout to the kernel).
+ * Rows form tiles of 16 (tile t = rows 16t..16t+15); a row's bytes form
+ * segments of 64 (segment s = bytes 64s..64s+63, i.e. k = 128s..128s+127);
+ * the 16 rows x 64 bytes of (t, s) become one unit of 1024 bytes, stored
+ * unit after unit in the order (t, s) with s fastest; inside a unit, piece
+ * p = 0..63 of 16 bytes holds bytes 16*(p / 16) .. +15 of segment s of row
+ * 16t + p % 16.  Requires N % 16 == 0 and K % 128 == 0.
+ * oracle_tile_offset gives where byte j of row n goes; oracle_repack_tiles
+ * moves every byte there. */
+int64_t oracle_tile_offset(int64_t N, int64_t K, int64_t n, int64_t j)
+{
+    (void)N;
+    int64_t segs = K / 128;     /* segments per row */
+    int64_t t = n / 16, r = n % 16;
+    int64_t s = j / 64, q = j % 64;
+    int64_t piece = r + 16 * (q / 16);
+    return (t * segs + s) * 1024 + piece * 16 + q % 16;
+}
+
+void oracle_repack_tiles(const uint8_t *Wpacked, int64_t N, int64_t K, uint8_t *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t j = 0; j < K / 2; j++)
+            out[oracle_tile_offset(N, K, n, j)] = Wpacked[n * (K / 2) + j];
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
