@@ -219,12 +219,16 @@ def headline(d, args):
     cb = d.raw(p["codebook"])
     sets = d.copies(w, q4_bytes(1, N, K))
     R = len(sets)
+    # The timed path reads the weights in args.layout; the per-M times of the
+    # other layout are reported beside them.
+    tsets = [(q4.q4_repack_tiles(Wp), am) for Wp, am in sets]
+    by_layout = {"rows": sets, "tiles": tsets}
     A = {M: d.bf16(p["A"][M]) for M in M_list}
     C = {M: t.empty((M, N), dtype=t.bfloat16, device=d.dev) for M in M_list}
 
-    def launch(M, i):
-        Wp, am = sets[i % R]
-        q4.q4_gemm_skinny(A[M], Wp, am, cb, BS, out=C[M])
+    def launch(M, i, layout=args.layout):
+        Wp, am = by_layout[layout][i % R]
+        q4.q4_gemm_skinny(A[M], Wp, am, cb, BS, out=C[M], layout=layout)
 
     n = 0
     for _ in range(args.warmup):
@@ -265,13 +269,18 @@ def headline(d, args):
     # weight copies between one event pair.
     per_m_us = dict(zip(M_list, d.time_launches(
         [lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)))
+    # (not with --quick: profiling runs launch one layout only)
+    other = "rows" if args.layout == "tiles" else "tiles"
+    other_us = {} if args.quick else dict(zip(M_list, d.time_launches(
+        [lambda i, M=M: launch(M, i, other) for M in M_list], reps=12 * R)))
     total = args.steps * sum(q4_bytes(M, N, K) for M in M_list)
     per_m = {}
     for M in M_list:
         gbs = q4_bytes(M, N, K) / (per_m_us[M] * 1e-6) / 1e9
         per_m[str(M)] = {"us": round(per_m_us[M], 2), "GB/s": round(gbs, 1),
                          "pct_peak": round(100 * gbs / PEAK_GBS, 1),
-                         "path": "fused" if M <= q4.q4_get_crossover_shape(N, K) else "split"}
+                         "path": "fused" if M <= q4.q4_get_crossover_shape(N, K) else "split",
+                         other + "_us": round(other_us[M], 2) if other_us else None}
     # The roofline kernel is the M=1 launch, timed as above.
     m1_us = per_m_us[1]
     ach = q4_bytes(1, N, K) / (m1_us * 1e-6) / 1e9
@@ -280,7 +289,7 @@ def headline(d, args):
             "frac": round(ach / PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic / (m1_us * 1e-6) / 1e9, 1),
             "traffic_bytes_per_launch": traffic,
-            "kernel": "fused q4 M=1, K=8192, N=28672",
+            "kernel": "fused q4 M=1, K=8192, N=28672, %s layout" % args.layout,
             "launch_us": round(m1_us, 2),
             "algorithmic_bytes_per_launch": q4_bytes(1, N, K)}
     out = {
@@ -298,14 +307,15 @@ def headline(d, args):
         "data": "synthetic",
         "config": {"workload": "fused 4-bit skinny GEMM, K=8192, N=28672, blocksize 64, "
                                "M=1,2,4,8 per step",
-                   "M": M_list, "K": K, "N": N, "blocksize": BS, "weight_copies": R},
+                   "M": M_list, "K": K, "N": N, "blocksize": BS, "weight_copies": R,
+                   "weight_layout": args.layout},
         "pct_of_peak": round(100 * total / wall / 1e9 / PEAK_GBS, 1),
         "timed_as": "one replay of a HIP graph holding the K steps",
         "eager_GB/s": round(total / eager_wall / 1e9, 1),
         "per_m": per_m,
         "roofline": roof,
     }
-    del sets, w
+    del sets, tsets, by_layout, w
     return out, p, M_list
 
 
@@ -315,35 +325,40 @@ def other_configs(d):
     t = d.t
     res = {}
 
-    def q4_cfg(name, M_list, N, K, config, shape, paths=("auto",)):
+    def q4_cfg(name, M_list, N, K, config, shape, paths=("auto",), layouts=("rows",)):
         p = synth.q4_problem(1, N, K, BS, config=config, shape=shape)
         sets = d.copies((d.raw(p["Wpacked"]), d.raw(p["absmax"])), q4_bytes(1, N, K))
+        by_layout = {"rows": sets}
+        if "tiles" in layouts:
+            by_layout["tiles"] = [(q4.q4_repack_tiles(Wp), am) for Wp, am in sets]
+        cases = [(path, lay) for lay in layouts for path in paths]
         cb = d.raw(p["codebook"])
         rows = {}
         for M in M_list:
             A = d.bf16(synth.activations_bf16(M, K, synth.seed(config, shape, 10 * M + 1)))
             C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
             fns = []
-            for path in paths:
-                def f(i, path=path):
-                    Wp, am = sets[i % len(sets)]
-                    q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path=path)
+            for path, lay in cases:
+                def f(i, path=path, lay=lay):
+                    Wp, am = by_layout[lay][i % len(sets)]
+                    q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path=path, layout=lay)
                 fns.append(f)
             us = d.time_launches(fns, reps=max(60, min(200, len(sets) * 2)))
-            for path, u in zip(paths, us):
+            for (path, lay), u in zip(cases, us):
                 gbs = q4_bytes(M, N, K) / (u * 1e-6) / 1e9
-                rows["M=%d %s" % (M, path)] = {"us": round(u, 2), "GB/s": round(gbs, 1),
-                                               "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+                key = "M=%d %s" % (M, path) + ("" if lay == "rows" else " tiles")
+                rows[key] = {"us": round(u, 2), "GB/s": round(gbs, 1),
+                             "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
         res[name] = rows
         return rows
 
     log("C1 GEMV 4096x4096")
-    q4_cfg("q4 M=1 K=4096 N=4096", [1], 4096, 4096, 0, 0)
+    q4_cfg("q4 M=1 K=4096 N=4096", [1], 4096, 4096, 0, 0, layouts=("rows", "tiles"))
     log("C3 decode layers")
     cross = {}
     for shape, (K, N) in enumerate([(5120, 8192), (5120, 5120), (17408, 5120), (8192, 8192)]):
         rows = q4_cfg("q4 K=%d N=%d" % (K, N), [1, 4, 8, 16], N, K, 2, shape,
-                      paths=("fused", "split"))
+                      paths=("fused", "split"), layouts=("rows", "tiles"))
         mstar = None
         for M in [1, 4, 8, 16]:
             if rows["M=%d split" % M]["us"] < rows["M=%d fused" % M]["us"]:
@@ -420,7 +435,7 @@ def other_configs(d):
         del Wq, outs
     res["q4_quantize N=28672 K=8192 bs=64"] = rows
     log("C5 large-vocabulary projection")
-    q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0)
+    q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0, layouts=("rows", "tiles"))
     K, N = 2560, 248320
     W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
     rows = {}
@@ -457,6 +472,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--m", type=int, nargs="+", default=[1, 2, 4, 8],
                     help="token rows per step (profiling runs use --m 1)")
+    ap.add_argument("--layout", choices=("tiles", "rows"), default="tiles",
+                    help="packed-weight layout of the timed step (q4_repack_tiles or row-major)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel (counter calibration)")
     args = ap.parse_args()

@@ -36,6 +36,7 @@ EXPORTS = (
     "q4_get_crossover_m", "q4_set_crossover_m", "q4_release_workspace", "q4_last_error",
     "q4_copy_probe", "q4_version", "q4_quantize", "q4_codebook_preset",
     "q4_set_crossover_shape", "q4_get_crossover_shape", "q4_clear_crossover_shapes",
+    "q4_repack_tiles", "q4_gemm_skinny_tiles", "q4_dequant_tiles",
 )
 PRESETS = {"nf4_style": 0, "int4": 1}
 
@@ -67,6 +68,9 @@ def lib():
         L.q4_gemm_skinny_ex.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
         L.bf16_gemm_skinny.argtypes = [P, P, P, I, I, I, P, P]
         L.q4_dequant.argtypes = [P, P, P, I, I, I, P, I, P]
+        L.q4_gemm_skinny_tiles.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
+        L.q4_dequant_tiles.argtypes = [P, P, P, I, I, I, P, I, P]
+        L.q4_repack_tiles.argtypes = [P, P, I, I, P]
         L.q4_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
         L.q4_set_crossover_m.argtypes = [I]
         L.q4_quantize.argtypes = [P, I, P, I, I, I, P, P, P]
@@ -134,12 +138,16 @@ def _dev(t, name, dtype):
 
 
 def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, path: str = "auto",
-                   bias=None, out_dtype=None):
+                   bias=None, out_dtype=None, layout: str = "rows"):
     """C[M,N] = A[M,K] * dequant(W)[N,K]^T (+ bias), fp32 accumulation.
 
     A may be bf16, fp16 or fp32; C (and bias) have out_dtype, by default A's
-    dtype.  bf16 in and out without a bias calls q4_gemm_skinny_path, anything
-    else q4_gemm_skinny_ex."""
+    dtype.  layout "rows": Wpacked holds row-major packed rows; bf16 in and
+    out without a bias calls q4_gemm_skinny_path, anything else
+    q4_gemm_skinny_ex.  layout "tiles": Wpacked holds the output of
+    q4_repack_tiles (same [N, K/2] shape) and q4_gemm_skinny_tiles runs."""
+    if layout not in ("rows", "tiles"):
+        raise ValueError("layout must be 'rows' or 'tiles'")
     torch = _torch()
     if A.dim() != 2 or Wpacked.dim() != 2:
         raise ValueError("A must be [M, K] and Wpacked [N, K/2]")
@@ -159,14 +167,15 @@ def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, 
         out = torch.empty((M, N), dtype=out_dtype, device=A.device)
     elif tuple(out.shape) != (M, N):
         raise ValueError("out must be [M, N]")
-    if a_code == Q4_DTYPE_BF16 and c_code == Q4_DTYPE_BF16 and bias is None:
+    if layout == "rows" and a_code == Q4_DTYPE_BF16 and c_code == Q4_DTYPE_BF16 and bias is None:
         _check(lib().q4_gemm_skinny_path(
             _dev(A, "A", torch.bfloat16), _dev(Wpacked, "Wpacked", torch.uint8),
             _dev(absmax, "absmax", torch.float32), _dev(codebook, "codebook", torch.float32),
             M, N, K, blocksize, _dev(out, "out", torch.bfloat16), _stream(A), PATHS[path]))
         return out
     bptr = None if bias is None else _dev(bias, "bias", out_dtype)
-    _check(lib().q4_gemm_skinny_ex(
+    fn = lib().q4_gemm_skinny_ex if layout == "rows" else lib().q4_gemm_skinny_tiles
+    _check(fn(
         _dev(A, "A", A.dtype), a_code, _dev(Wpacked, "Wpacked", torch.uint8),
         _dev(absmax, "absmax", torch.float32), _dev(codebook, "codebook", torch.float32), bptr,
         M, N, K, blocksize, _dev(out, "out", out_dtype), c_code, _stream(A), PATHS[path]))
@@ -193,8 +202,14 @@ def bf16_gemm_skinny(A, W, bias=None, out=None):
     return out
 
 
-def q4_dequant(Wpacked, absmax, codebook, blocksize: int = 64, out_dtype=None, out=None):
-    """W[N,K] = codebook[code] * absmax, as bf16 (default), fp16 or fp32."""
+def q4_dequant(Wpacked, absmax, codebook, blocksize: int = 64, out_dtype=None, out=None,
+               layout: str = "rows"):
+    """W[N,K] = codebook[code] * absmax, as bf16 (default), fp16 or fp32.
+
+    layout "tiles" reads weights made by q4_repack_tiles; the output is
+    row-major either way."""
+    if layout not in ("rows", "tiles"):
+        raise ValueError("layout must be 'rows' or 'tiles'")
     torch = _torch()
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     N, K = Wpacked.shape[0], Wpacked.shape[1] * 2
@@ -203,10 +218,28 @@ def q4_dequant(Wpacked, absmax, codebook, blocksize: int = 64, out_dtype=None, o
     elif tuple(out.shape) != (N, K) or out.dtype != out_dtype:
         raise ValueError("out must be [N, K] of out_dtype")
     code = _dtype_code(out_dtype)
-    _check(lib().q4_dequant(
+    fn = lib().q4_dequant if layout == "rows" else lib().q4_dequant_tiles
+    _check(fn(
         _dev(Wpacked, "Wpacked", torch.uint8), _dev(absmax, "absmax", torch.float32),
         _dev(codebook, "codebook", torch.float32), N, K, blocksize, _dev(out, "out", out_dtype),
         code, _stream(Wpacked)))
+    return out
+
+
+def q4_repack_tiles(Wpacked, out=None):
+    """The tile layout of row-major packed weights [N, K/2] (uint8, same shape:
+    16-row tiles of 1 KiB units; N % 16 == 0, K % 128 == 0)."""
+    torch = _torch()
+    if Wpacked.dim() != 2:
+        raise ValueError("Wpacked must be [N, K/2]")
+    N, K = Wpacked.shape[0], Wpacked.shape[1] * 2
+    if out is None:
+        out = torch.empty_like(Wpacked)
+    elif tuple(out.shape) != (N, K // 2):
+        raise ValueError("out must be [N, K/2]")
+    _check(lib().q4_repack_tiles(
+        _dev(Wpacked, "Wpacked", torch.uint8), _dev(out, "out", torch.uint8), N, K,
+        _stream(Wpacked)))
     return out
 
 

@@ -276,33 +276,33 @@ q4_status current_device(int *device) {
 // of activation planes).  When K is split over workgroups (ksplit > 1) the
 // kernel writes ksplit fp32 partial outputs to `parts` for the caller to sum.
 q4_status run_fused_tiled(const uint16_t *A, const uint8_t *Wp, const float *am, const float *cb,
-                          const void *bias, int rows, int N, int K, int bs_log2,
+                          const void *bias, int rows, int N, int K, int bs_log2, int wl,
                           const q4::TiledPlan &plan, float *parts, void *C, int c_dt,
                           hipStream_t s) {
     if (plan.ksplit == 1)
         return launch_checked("fused", [&] {
-            return q4::launch_q4_fused_tiled(A, Wp, am, cb, bias, rows, N, K, bs_log2, plan, C,
+            return q4::launch_q4_fused_tiled(A, Wp, am, cb, bias, rows, N, K, bs_log2, wl, plan, C,
                                              c_dt, s);
         });
     return launch_checked("fused", [&] {
-        return q4::launch_q4_fused_tiled(A, Wp, am, cb, nullptr, rows, N, K, bs_log2, plan,
+        return q4::launch_q4_fused_tiled(A, Wp, am, cb, nullptr, rows, N, K, bs_log2, wl, plan,
                                          parts, Q4_DTYPE_FP32, s);
     });
 }
 
 q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const float *am,
                            const float *cb, const void *bias, int M, int N, int K, int bs_log2,
-                           void *C, int c_dt, hipStream_t s);
+                           int wl, void *C, int c_dt, hipStream_t s);
 
 // bf16 activations: the tiled kernel above fused_tiled_min_m rows, else the
 // skinny kernels in passes of up to Q4_FUSED_PASS_M token rows over
 // consecutive row slabs, each streaming the packed weights once more (more
 // than one pass only where the tiled kernel cannot run).
 q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
-                    const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
+                    const void *bias, int M, int N, int K, int bs_log2, int wl, void *C, int c_dt,
                     hipStream_t s) {
     if (a_dt != Q4_DTYPE_BF16 && bs_log2 >= 6 && q4::q4_fused_mfma_fits(M, N, K))
-        return run_fused_planes(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, C, c_dt, s);
+        return run_fused_planes(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, wl, C, c_dt, s);
     if (a_dt == Q4_DTYPE_BF16 && fused_tiled(M, N, K, bs_log2)) {
         const q4::TiledPlan plan = q4::q4_fused_tiled_plan(M, N, K, 4, fused_tiled_layout());
         const int ks = plan.ksplit;
@@ -317,7 +317,7 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
             parts = static_cast<float *>(ws);
         }
         q4_status st = run_fused_tiled(static_cast<const uint16_t *>(A), Wp, am, cb, bias, M, N,
-                                       K, bs_log2, plan, parts, C, c_dt, s);
+                                       K, bs_log2, wl, plan, parts, C, c_dt, s);
         if (st != Q4_OK || ks == 1) return st;
         return launch_checked("plane sum", [&] {
             return q4::launch_sum_planes(parts, ks, M, N, bias, C, c_dt, s);
@@ -329,7 +329,7 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
         q4_status st = launch_checked("fused", [&] {
             return q4::launch_q4_fused(static_cast<const char *>(A) + (size_t)m0 * a_row, a_dt,
                                        Wp, am, cb, bias, mm, N, K, bs_log2,
-                                       static_cast<char *>(C) + (size_t)m0 * c_row, c_dt, s);
+                                       static_cast<char *>(C) + (size_t)m0 * c_row, c_dt, wl, s);
         });
         if (st != Q4_OK) return st;
     }
@@ -344,7 +344,7 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
 // partials live in the per-stream workspace.
 q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const float *am,
                            const float *cb, const void *bias, int M, int N, int K, int bs_log2,
-                           void *C, int c_dt, hipStream_t s) {
+                           int wl, void *C, int c_dt, hipStream_t s) {
     int device = 0;
     q4_status st = current_device(&device);
     if (st != Q4_OK) return st;
@@ -366,9 +366,9 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
         return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s);
     });
     if (st != Q4_OK) return st;
-    st = tiled ? run_fused_tiled(planes, Wp, am, cb, nullptr, rows, N, K, bs_log2, plan, parts,
-                                 parts, Q4_DTYPE_FP32, s)
-               : run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, rows, N, K, bs_log2,
+    st = tiled ? run_fused_tiled(planes, Wp, am, cb, nullptr, rows, N, K, bs_log2, wl, plan,
+                                 parts, parts, Q4_DTYPE_FP32, s)
+               : run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, rows, N, K, bs_log2, wl,
                            parts, Q4_DTYPE_FP32, s);
     if (st != Q4_OK) return st;
     return launch_checked("plane sum", [&] {
@@ -382,7 +382,7 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
 constexpr int kTiledGemmMinM = 16;
 
 q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
-                    const void *bias, int M, int N, int K, int bs_log2, void *C, int c_dt,
+                    const void *bias, int M, int N, int K, int bs_log2, int wl, void *C, int c_dt,
                     hipStream_t s) {
     int device = 0;
     hipError_t e = hipGetDevice(&device);
@@ -405,7 +405,7 @@ q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am,
     if (st != Q4_OK) return st;
     const uint16_t *Wd = static_cast<const uint16_t *>(ws);
     st = launch_checked("dequant", [&] {
-        return q4::launch_dequant(Wp, am, cb, N, K, bs_log2, ws, Q4_DTYPE_BF16, s);
+        return q4::launch_dequant(Wp, am, cb, N, K, bs_log2, wl, ws, Q4_DTYPE_BF16, s);
     });
     if (st != Q4_OK) return st;
     if (!tiled)
@@ -435,6 +435,82 @@ q4_status run_split(const void *A, int a_dt, const uint8_t *Wp, const float *am,
     return launch_checked("plane sum", [&] {
         return q4::launch_sum_planes(parts, np * ks, M, N, bias, C, c_dt, s);
     });
+}
+
+// The tile layout: N % 16 == 0 and K % 128 == 0 (whole 16-row tiles of
+// whole 128-wide segments), offsets within the 32-bit range of the
+// matrix-core kernels (no vector-ALU fallback reads tiles), blocksize >= 64.
+q4_status check_tiles(int M, int N, int K, int blocksize) {
+    if (N % 16 != 0 || K % 128 != 0)
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "the tile layout needs N %% 16 == 0 and K %% 128 == 0 (N=%d, K=%d)", N, K);
+    if (blocksize < 64)
+        return fail(Q4_ERR_UNSUPPORTED, "the tile layout needs blocksize >= 64 (got %d)",
+                    blocksize);
+    if (!q4::q4_fused_mfma_fits(M, N, K))
+        return fail(Q4_ERR_UNSUPPORTED, "tile-layout matrix too large (N=%d, K=%d)", N, K);
+    return Q4_OK;
+}
+
+q4_status gemm_impl(const void *A, int a_dtype, const uint8_t *Wpacked, int wl,
+                    const float *absmax, const float *codebook, const void *bias, int M, int N,
+                    int K, int blocksize, void *C, int c_dtype, void *stream, int path) {
+    if (path != Q4_PATH_AUTO && path != Q4_PATH_FUSED && path != Q4_PATH_SPLIT)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown path %d", path);
+    if (!known_dtype(a_dtype) || !known_dtype(c_dtype))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown dtype (a_dtype=%d, c_dtype=%d)", a_dtype,
+                    c_dtype);
+    if (M < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d)", M);
+    int bs_log2 = 0;
+    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
+    if (st != Q4_OK) return st;
+    if ((int64_t)M * K > (int64_t(1) << 40))
+        return fail(Q4_ERR_UNSUPPORTED, "M*K too large");
+    if (wl && (st = check_tiles(M, N, K, blocksize)) != Q4_OK) return st;
+    bool fused;
+    if (path == Q4_PATH_FUSED) fused = true;
+    else if (path == Q4_PATH_SPLIT) fused = false;
+    else fused = M <= crossover_for(N, K);
+    if (!fused && a_dtype == Q4_DTYPE_FP32)
+        return fail(Q4_ERR_UNSUPPORTED, "fp32 activations take the fused path only (M=%d)", M);
+    if (M == 0 || N == 0) return ok();
+    if (!A || !Wpacked || !absmax || !codebook || !C)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    const size_t cs = dtype_size(c_dtype);
+    if (!aligned(A, 16) || !aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) ||
+        !aligned(C, cs) || (bias && !aligned(bias, cs)))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "A, Wpacked and absmax must be 16-byte aligned, C and bias aligned to "
+                    "their element size");
+    drain_prior_error();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = fused ? run_fused(A, a_dtype, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, C,
+                           c_dtype, s)
+               : run_split(A, a_dtype, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, C,
+                           c_dtype, s);
+    return st == Q4_OK ? ok() : st;
+}
+
+q4_status dequant_impl(const uint8_t *Wpacked, int wl, const float *absmax,
+                       const float *codebook, int N, int K, int blocksize, void *out,
+                       int out_dtype, void *stream) {
+    if (!known_dtype(out_dtype))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
+    int bs_log2 = 0;
+    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
+    if (st != Q4_OK) return st;
+    if (wl && (st = check_tiles(0, N, K, blocksize)) != Q4_OK) return st;
+    if (N == 0) return ok();
+    if (!Wpacked || !absmax || !codebook || !out)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) || !aligned(out, 16))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "Wpacked, absmax and out must be 16-byte aligned");
+    drain_prior_error();
+    st = launch_checked("dequant", [&] {
+        return q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, wl, out, out_dtype,
+                                  static_cast<hipStream_t>(stream));
+    });
+    return st == Q4_OK ? ok() : st;
 }
 
 }  // namespace
@@ -468,39 +544,16 @@ q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
                             const float *absmax, const float *codebook, const void *bias, int M,
                             int N, int K, int blocksize, void *C, int c_dtype, void *stream,
                             int path) {
-    if (path != Q4_PATH_AUTO && path != Q4_PATH_FUSED && path != Q4_PATH_SPLIT)
-        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown path %d", path);
-    if (!known_dtype(a_dtype) || !known_dtype(c_dtype))
-        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown dtype (a_dtype=%d, c_dtype=%d)", a_dtype,
-                    c_dtype);
-    if (M < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d)", M);
-    int bs_log2 = 0;
-    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
-    if (st != Q4_OK) return st;
-    if ((int64_t)M * K > (int64_t(1) << 40))
-        return fail(Q4_ERR_UNSUPPORTED, "M*K too large");
-    bool fused;
-    if (path == Q4_PATH_FUSED) fused = true;
-    else if (path == Q4_PATH_SPLIT) fused = false;
-    else fused = M <= crossover_for(N, K);
-    if (!fused && a_dtype == Q4_DTYPE_FP32)
-        return fail(Q4_ERR_UNSUPPORTED, "fp32 activations take the fused path only (M=%d)", M);
-    if (M == 0 || N == 0) return ok();
-    if (!A || !Wpacked || !absmax || !codebook || !C)
-        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-    const size_t cs = dtype_size(c_dtype);
-    if (!aligned(A, 16) || !aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) ||
-        !aligned(C, cs) || (bias && !aligned(bias, cs)))
-        return fail(Q4_ERR_INVALID_ARGUMENT,
-                    "A, Wpacked and absmax must be 16-byte aligned, C and bias aligned to "
-                    "their element size");
-    drain_prior_error();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = fused ? run_fused(A, a_dtype, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C,
-                           c_dtype, s)
-               : run_split(A, a_dtype, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C,
-                           c_dtype, s);
-    return st == Q4_OK ? ok() : st;
+    return gemm_impl(A, a_dtype, Wpacked, 0, absmax, codebook, bias, M, N, K, blocksize, C,
+                     c_dtype, stream, path);
+}
+
+q4_status q4_gemm_skinny_tiles(const void *A, int a_dtype, const uint8_t *Wtiles,
+                               const float *absmax, const float *codebook, const void *bias,
+                               int M, int N, int K, int blocksize, void *C, int c_dtype,
+                               void *stream, int path) {
+    return gemm_impl(A, a_dtype, Wtiles, 1, absmax, codebook, bias, M, N, K, blocksize, C,
+                     c_dtype, stream, path);
 }
 
 q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
@@ -541,20 +594,33 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
 
 q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook, int N,
                      int K, int blocksize, void *out, int out_dtype, void *stream) {
-    if (!known_dtype(out_dtype))
-        return fail(Q4_ERR_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
-    int bs_log2 = 0;
-    q4_status st = check_q4_shape(N, K, blocksize, &bs_log2);
-    if (st != Q4_OK) return st;
+    return dequant_impl(Wpacked, 0, absmax, codebook, N, K, blocksize, out, out_dtype, stream);
+}
+
+q4_status q4_dequant_tiles(const uint8_t *Wtiles, const float *absmax, const float *codebook,
+                           int N, int K, int blocksize, void *out, int out_dtype, void *stream) {
+    return dequant_impl(Wtiles, 1, absmax, codebook, N, K, blocksize, out, out_dtype, stream);
+}
+
+q4_status q4_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K, void *stream) {
+    if (N < 0 || K < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (N=%d, K=%d)", N, K);
+    if (K == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "K must be positive");
+    if (N % 16 != 0 || K % 128 != 0)
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "the tile layout needs N %% 16 == 0 and K %% 128 == 0 (N=%d, K=%d)", N, K);
+    if ((uint64_t)N * (uint64_t)K / 2 >= (1ull << 32))
+        return fail(Q4_ERR_UNSUPPORTED, "tile-layout matrix too large (N=%d, K=%d)", N, K);
     if (N == 0) return ok();
-    if (!Wpacked || !absmax || !codebook || !out)
-        return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-    if (!aligned(Wpacked, 16) || !aligned(absmax, 16) || !aligned(codebook, 4) || !aligned(out, 16))
-        return fail(Q4_ERR_INVALID_ARGUMENT, "Wpacked, absmax and out must be 16-byte aligned");
+    if (!Wpacked || !Wtiles) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(Wpacked, 16) || !aligned(Wtiles, 16))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "Wpacked and Wtiles must be 16-byte aligned");
+    const size_t bytes = (size_t)N * (size_t)K / 2;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(Wpacked), b = reinterpret_cast<uintptr_t>(Wtiles);
+    if (a < b + bytes && b < a + bytes)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "Wtiles must not overlap Wpacked");
     drain_prior_error();
-    st = launch_checked("dequant", [&] {
-        return q4::launch_dequant(Wpacked, absmax, codebook, N, K, bs_log2, out, out_dtype,
-                                  static_cast<hipStream_t>(stream));
+    q4_status st = launch_checked("repack", [&] {
+        return q4::launch_repack_tiles(Wpacked, Wtiles, N, K, static_cast<hipStream_t>(stream));
     });
     return st == Q4_OK ? ok() : st;
 }

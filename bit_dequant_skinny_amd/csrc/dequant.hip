@@ -12,6 +12,11 @@
 // has four such words in flight.  Because K % bs == 0, blocking the flattened
 // matrix equals blocking each row, so the scale of flat code index i is
 // absmax[i >> bs_log2].
+//
+// Weights in the tile layout (16-row tiles of 1 KiB units, see
+// repack_tiles_kernel) are gathered: flat word i of row n = i / (K/8) is read
+// from its place in the unit of (n / 16, segment); the output order, the
+// scales and the arithmetic are the row-major ones.
 #include "device.h"
 #include "launch.h"
 
@@ -27,6 +32,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
                                                            const float *__restrict__ absmax,
                                                            const float *__restrict__ codebook,
                                                            uint64_t words, int bs_log2,
+                                                           int wl, uint32_t kw, uint32_t nseg,
                                                            void *__restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int table = __float_as_int(codebook[lane & 15]);
@@ -41,7 +47,15 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t i = base + u * 64 + lane;
             const uint64_t ic = i < words ? i : words - 1;
-            d[u] = packed[ic];
+            uint64_t src = ic;
+            if (wl) {
+                // word c of row n: 16-byte piece c / 4 of segment c / 16, held
+                // by lane (n % 16) + 16 * ((c / 4) % 4) of unit (n / 16, segment)
+                const uint32_t n = (uint32_t)ic / kw, c = (uint32_t)ic - n * kw;
+                const uint32_t l = (n & 15) + 16 * ((c >> 2) & 3);
+                src = ((uint64_t)((n >> 4) * nseg + (c >> 4)) << 8) + 4 * l + (c & 3);
+            }
+            d[u] = packed[src];
             am[u] = absmax[(ic * 8) >> bs_log2];
         }
 #pragma unroll
@@ -82,10 +96,48 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
     }
 }
 
+// Row-major packed codes -> tile layout.  Tile t holds rows 16t..16t+15;
+// (tile t, segment s) is the 1 KiB unit (t * K/128 + s): 64 pieces of 16
+// bytes, piece l being bytes 64s + 16(l / 16) .. +16 of row 16t + l % 16 (the
+// 16 bytes a matrix-core lane l decodes for one 128-wide segment).  A pure
+// permutation of 16-byte pieces; each thread moves one piece per step, so
+// the writes are contiguous and each wave reads 64-byte runs of 16 rows.
+__global__ __launch_bounds__(kThreads) void repack_tiles_kernel(const uint4 *__restrict__ src,
+                                                                uint4 *__restrict__ dst,
+                                                                uint32_t pieces, uint32_t nseg,
+                                                                uint32_t row_pieces) {
+    const uint32_t stride = gridDim.x * kThreads;
+    for (uint32_t p = blockIdx.x * kThreads + threadIdx.x; p < pieces; p += stride) {
+        const uint32_t unit = p >> 6, l = p & 63;
+        const uint32_t t = unit / nseg, seg = unit - t * nseg;
+        const uint32_t n = 16 * t + (l & 15);
+        dst[p] = src[n * row_pieces + 4 * seg + (l >> 4)];
+    }
+}
+
 }  // namespace
 
+hipError_t launch_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
+                               hipStream_t s) {
+    if (N % 16 != 0 || K % 128 != 0 || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32))
+        return hipErrorInvalidValue;
+    const uint32_t pieces = (uint32_t)((uint64_t)N * (uint64_t)K / 32);
+    const DeviceInfo info = device_info();
+    uint32_t blocks = (pieces + kThreads - 1) / kThreads;
+    const uint32_t cap = (uint32_t)info.num_cus * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks == 0) return hipSuccess;
+    repack_tiles_kernel<<<dim3(blocks), dim3(kThreads), 0, s>>>(
+        reinterpret_cast<const uint4 *>(Wpacked), reinterpret_cast<uint4 *>(Wtiles), pieces,
+        (uint32_t)K / 128, (uint32_t)K / 32);
+    return hipGetLastError();
+}
+
 hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
-                          int N, int K, int bs_log2, void *out, int out_dt, hipStream_t s) {
+                          int N, int K, int bs_log2, int wl, void *out, int out_dt, hipStream_t s) {
+    if (wl && (N % 16 != 0 || K % 128 != 0 || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32)))
+        return hipErrorInvalidValue;
+    const uint32_t kw = (uint32_t)K / 8, nseg = (uint32_t)K / 128;
     const uint64_t words = (uint64_t)N * (uint64_t)K / 8;
     const DeviceInfo info = device_info();
     const uint64_t per_block = (uint64_t)kThreads * kUnroll;
@@ -96,13 +148,13 @@ hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const flo
     const uint32_t *packed = reinterpret_cast<const uint32_t *>(Wpacked);
     if (out_dt == kBf16)
         dequant_kernel<kBf16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            packed, absmax, codebook, words, bs_log2, out);
+            packed, absmax, codebook, words, bs_log2, wl, kw, nseg, out);
     else if (out_dt == kF16)
         dequant_kernel<kF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            packed, absmax, codebook, words, bs_log2, out);
+            packed, absmax, codebook, words, bs_log2, wl, kw, nseg, out);
     else
         dequant_kernel<kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            packed, absmax, codebook, words, bs_log2, out);
+            packed, absmax, codebook, words, bs_log2, wl, kw, nseg, out);
     return hipGetLastError();
 }
 

@@ -86,7 +86,7 @@ template <int SR, int TB, int RS, int UF, int P, int MB>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups, int wl,
     void *__restrict__ C, int c_dt) {
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
     static_assert(64 * KW == 512, "two threads per table entry");
@@ -145,19 +145,26 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // waves of a workgroup read 64*KW contiguous bytes of each row at a time).
     auto group_of = [&](int c) { return (uint32_t)blockIdx.x + (uint32_t)c * (uint32_t)G; };
     const uint32_t w_tile_step = 16u * (uint32_t)groups * row_bytes;
-    const uint32_t w_lane = 16 * g;
+    // The lane's part of a weight offset, and the shift from a segment to its
+    // offset.  Row-major: segment s of row n is the 64 bytes at
+    // n*row_bytes + 64*s, lane (j, g) reads 16 of them at 16*g.  Tile layout:
+    // the 16 rows x 64 bytes of (tile, segment) are one 1 KiB unit at
+    // (tile*nseg + s) * 1024 that holds lane l's 16 bytes at 16*l.  A tile
+    // spans 16*row_bytes bytes in both.
+    const uint32_t w_lane = wl ? 16u * (uint32_t)lane : (uint32_t)j * row_bytes + 16u * (uint32_t)g;
+    const int seg_sh = wl ? 10 : 6;
 
     // Weight issue cursor: the (chunk, slot) whose loads are issued next.
     // Slots past this workgroup's last chunk and segments past the end of a
     // row take an offset beyond the buffer: they read zeros without touching
     // memory.
     int ic = 0, iq = 0;
-    uint32_t w_row0 = (group_of(0) * 16 + (uint32_t)j) * row_bytes + w_lane;
+    uint32_t w_row0 = group_of(0) * 16 * row_bytes + w_lane;
     bool w_live = true;
     auto w_seek = [&]() {
         const int seg = wave + ((iq + rot) % spw) * KW;
         w_live = ic < my_chunks && seg < nseg;
-        w_row0 = (group_of(ic) * 16 + (uint32_t)j) * row_bytes + (uint32_t)seg * 64 + w_lane;
+        w_row0 = group_of(ic) * 16 * row_bytes + ((uint32_t)seg << seg_sh) + w_lane;
     };
     auto w_advance = [&]() {
         if (++iq == spw) {
@@ -513,7 +520,7 @@ int tiles_per_chunk(int N) {
 template <int SR, int MB, int TB>
 hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
-                     void *C, int c_dt, int groups, int G, hipStream_t s) {
+                     void *C, int c_dt, int groups, int G, int wl, hipStream_t s) {
     // Ring depth TB*RS of about 8 units (8 KiB of weights in flight per wave).
     constexpr int RS = TB == 1 ? 8 : TB == 2 ? 4 : TB <= 4 ? 2 : 1;
     constexpr int UF = (RS * TB) % 2 == 0 ? RS : 2 * RS;
@@ -528,14 +535,14 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     const int spw = ((K + 127) / 128 + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
     fused_mfma_kernel<SR, TB, RS, UF, P, MB><<<dim3(G), dim3(64 * KW), 0, s>>>(
-        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt);
+        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, wl, C, c_dt);
     return hipGetLastError();
 }
 
 template <int SR, int MB>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
-                     void *C, int c_dt, hipStream_t s) {
+                     void *C, int c_dt, int wl, hipStream_t s) {
     // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS).
     // TB = the tiles each CU must cover, up to 8, so that every chunk but the
     // last holds TB live tiles; a workgroup loops over ceil(groups / CUs)
@@ -546,7 +553,7 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     const int groups = (tiles + tb - 1) / tb;
     const int G = groups < cus ? groups : cus;
 #define Q4_LAUNCH_TB(T) \
-    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, s)
+    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, wl, s)
     switch (tb) {
     case 1: Q4_LAUNCH_TB(1);
     case 2: Q4_LAUNCH_TB(2);
@@ -579,12 +586,13 @@ bool q4_fused_mfma_fits(int M, int N, int K) {
 
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
-                                int M, int N, int K, int bs_log2, void *C, int c_dt,
+                                int M, int N, int K, int bs_log2, void *C, int c_dt, int wl,
                                 hipStream_t s) {
-    if (a_dt != kBf16 || M > 32) return hipErrorInvalidValue;
+    if (a_dt != kBf16 || M > 32 || (wl && (N % 16 != 0 || K % 128 != 0)))
+        return hipErrorInvalidValue;
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
 #define Q4_LAUNCH_SR(R, B) \
-    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, s)
+    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, wl, s)
     if (M <= 1) Q4_LAUNCH_SR(1, 1);
     if (M <= 2) Q4_LAUNCH_SR(2, 1);
     if (M <= 16) Q4_LAUNCH_SR(4, 1);
@@ -600,11 +608,12 @@ hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
 // vector-ALU kernel in passes of 16 rows.
 hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, const void *bias, int M, int N, int K,
-                           int bs_log2, void *C, int c_dt, hipStream_t s) {
+                           int bs_log2, void *C, int c_dt, int wl, hipStream_t s) {
     const bool mfma = a_dt == kBf16 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K);
+    if (wl && !mfma) return hipErrorInvalidValue;  // the vector-ALU kernel reads rows
     if (mfma && (M <= 16 || tiles_per_chunk(N) < 8))
         return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
-                                    C, c_dt, s);
+                                    C, c_dt, wl, s);
     const size_t a_row = (size_t)K * (a_dt == kF32 ? 4 : 2);
     const size_t c_row = (size_t)N * (c_dt == kF32 ? 4 : 2);
     for (int m0 = 0; m0 < M; m0 += 16) {
@@ -613,7 +622,7 @@ hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, cons
         void *Cm = static_cast<char *>(C) + (size_t)m0 * c_row;
         const hipError_t e =
             mfma ? launch_q4_fused_mfma(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
-                                        Cm, c_dt, s)
+                                        Cm, c_dt, wl, s)
                  : launch_q4_fused_simt(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
                                         Cm, c_dt, s);
         if (e != hipSuccess) return e;

@@ -137,7 +137,7 @@ template <int TM>
 __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int m_blocks,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int wl, int m_blocks,
     int n_blocks, int ksplit, int segs_per_part, void *__restrict__ C, int c_dt) {
     // Entry e (a packed byte) fills bytes [256 e, 256 e + 256): 32 copies of
     // its hi pair, then 32 copies of its lo pair; lane l reads copy l % 32.
@@ -175,7 +175,9 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const uint32_t n = (uint32_t)(n0 + 16 * b + j);
-        w_off[b] = n < (uint32_t)N ? n * row_bytes + 16 * (uint32_t)g : kPastEnd;
+        w_off[b] = n >= (uint32_t)N ? kPastEnd
+                   : wl ? (n - (uint32_t)j) * row_bytes + 16 * (uint32_t)lane
+                        : n * row_bytes + 16 * (uint32_t)g;
         s_off[b] = n < (uint32_t)N ? n * nbk * 4 : kPastEnd;
     }
 #pragma unroll
@@ -186,12 +188,13 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
             a_off[t][p] = m < (uint32_t)M ? (m * (uint32_t)K + swapped_k_offset(g, p)) * 2 : kPastEnd;
     }
     const uint32_t w_bytes = (uint32_t)N * row_bytes, s_bytes = (uint32_t)N * nbk * 4;
+    const int seg_sh = wl ? 10 : 6;  // segment -> byte offset (1 KiB units or 64-byte pieces)
     const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2;
 
     auto load_w = [&](int i, SegW &d) {
         const bool live = i < my;
         const uint32_t seg = (uint32_t)(s_begin + wave + kWaves * i);
-        const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg * 64, live);
+        const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg << seg_sh, live);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             d.w[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)w_off[b], 0, 0));
@@ -365,7 +368,7 @@ template <int TM>
 __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int m_blocks,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int wl, int m_blocks,
     int n_blocks, int ksplit, uint32_t per_xcd, int segs_per_part, void *__restrict__ C,
     int c_dt) {
     __shared__ uint32_t table[256 * 64];                 // as in the K-split layout
@@ -391,12 +394,15 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     const uint32_t row_bytes = (uint32_t)K >> 1;
     const uint32_t nbk = (uint32_t)K >> bs_log2;
     const uint32_t w_bytes = (uint32_t)N * row_bytes, s_bytes = (uint32_t)N * nbk * 4;
+    const int seg_sh = wl ? 10 : 6;  // segment -> byte offset (1 KiB units or 64-byte pieces)
     const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2;
     uint32_t w_off[kTN], s_off[kTN];
 #pragma unroll
     for (int b = 0; b < kTN; ++b) {
         const uint32_t n = (uint32_t)(n0 + wave * 16 * kTN + 16 * b + j);
-        w_off[b] = n < (uint32_t)N ? n * row_bytes + 16 * (uint32_t)g : kPastEnd;
+        w_off[b] = n >= (uint32_t)N ? kPastEnd
+                   : wl ? (n - (uint32_t)j) * row_bytes + 16 * (uint32_t)lane
+                        : n * row_bytes + 16 * (uint32_t)g;
         s_off[b] = n < (uint32_t)N ? n * nbk * 4 : kPastEnd;
     }
     // Activation staging: waves 0-3 move the first 64 k of each row of the
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     auto load_w = [&](int i, SegWN &d) {
         const bool live = i < cnt;
         const uint32_t seg = (uint32_t)(s_begin + i);
-        const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg * 64, live);
+        const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg << seg_sh, live);
 #pragma unroll
         for (int b = 0; b < kTN; ++b)
             d.w[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)w_off[b], 0, 0));
@@ -616,11 +622,12 @@ TiledPlan q4_fused_tiled_plan(int M, int N, int K, int max_ks, int layout) {
 
 hipError_t launch_q4_fused_tiled(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
                                  const float *codebook, const void *bias, int M, int N, int K,
-                                 int bs_log2, const TiledPlan &plan, void *C, int c_dt,
+                                 int bs_log2, int wl, const TiledPlan &plan, void *C, int c_dt,
                                  hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int ksplit = plan.ksplit;
-    if (bs_log2 < 6 || ksplit < 1 || (ksplit > 1 && (bias || c_dt != kF32)))
+    if (bs_log2 < 6 || ksplit < 1 || (ksplit > 1 && (bias || c_dt != kF32)) ||
+        (wl && (N % 16 != 0 || K % 128 != 0)))
         return hipErrorInvalidValue;
     const int bm = tile_rows(M);
     const int m_blocks = (M + bm - 1) / bm;
@@ -632,11 +639,11 @@ hipError_t launch_q4_fused_tiled(const uint16_t *A, const uint8_t *Wpacked, cons
         const unsigned grid = 8u * per_xcd;
         if (bm == 64)
             fused_tiled_ns_kernel<4><<<dim3(grid), dim3(64 * kWavesN), 0, s>>>(
-                A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, m_blocks, n_blocks,
+                A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks,
                 ksplit, per_xcd, spp, C, c_dt);
         else
             fused_tiled_ns_kernel<2><<<dim3(grid), dim3(64 * kWavesN), 0, s>>>(
-                A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, m_blocks, n_blocks,
+                A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks,
                 ksplit, per_xcd, spp, C, c_dt);
         return hipGetLastError();
     }
@@ -645,11 +652,11 @@ hipError_t launch_q4_fused_tiled(const uint16_t *A, const uint8_t *Wpacked, cons
     const unsigned grid = (unsigned)(8 * m_blocks * ((n_blocks + 7) / 8) * ksplit);
     if (bm == 64)
         fused_tiled_ks_kernel<4><<<dim3(grid), dim3(64 * kWaves), 0, s>>>(
-            A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, m_blocks, n_blocks, ksplit,
+            A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks, ksplit,
             spp, C, c_dt);
     else
         fused_tiled_ks_kernel<2><<<dim3(grid), dim3(64 * kWaves), 0, s>>>(
-            A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, m_blocks, n_blocks, ksplit,
+            A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks, ksplit,
             spp, C, c_dt);
     return hipGetLastError();
 }

@@ -17,7 +17,11 @@ DeviceInfo device_info();  // the current device, cached per device
 
 // Element types are the Q4_DTYPE_* codes (kBf16, kF32, kF16 in device.h).
 hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
-                          int N, int K, int bs_log2, void *out, int out_dt, hipStream_t s);
+                          int N, int K, int bs_log2, int wl, void *out, int out_dt, hipStream_t s);
+// Weight layouts (wl): 0 = row-major packed rows, 1 = 16-row tiles of 1 KiB
+// units (N % 16 == 0, K % 128 == 0; see launch_repack_tiles).
+hipError_t launch_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
+                               hipStream_t s);
 
 // Fused 4-bit GEMM, C = A * dequant(W)^T (+ bias), A of type a_dt, bias and C
 // of type c_dt.  Dispatches to the matrix-core kernel (bf16 or fp16
@@ -25,10 +29,10 @@ hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const flo
 // activations, offsets beyond 32 bits).
 hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, const void *bias, int M, int N, int K,
-                           int bs_log2, void *C, int c_dt, hipStream_t s);
+                           int bs_log2, void *C, int c_dt, int wl, hipStream_t s);
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
-                                int M, int N, int K, int bs_log2, void *C, int c_dt,
+                                int M, int N, int K, int bs_log2, void *C, int c_dt, int wl,
                                 hipStream_t s);
 hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
@@ -59,7 +63,7 @@ bool q4_fused_tiled_fits(int M, int N, int K);
 TiledPlan q4_fused_tiled_plan(int M, int N, int K, int max_ks, int layout);
 hipError_t launch_q4_fused_tiled(const uint16_t *A, const uint8_t *Wpacked, const float *absmax,
                                  const float *codebook, const void *bias, int M, int N, int K,
-                                 int bs_log2, const TiledPlan &plan, void *C, int c_dt,
+                                 int bs_log2, int wl, const TiledPlan &plan, void *C, int c_dt,
                                  hipStream_t s);
 
 // Tiled bf16 GEMM (bf16 A, 128 x 128 tiles through LDS) for the split path at

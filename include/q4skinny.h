@@ -139,6 +139,62 @@ q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
                             int path);
 
 /*
+ * The tile layout of the packed weights.
+ *
+ * The same bytes as the row-major Wpacked [N, K/2], reordered so that the
+ * 16 rows x 64 bytes a wave's matrix-core lanes decode together for one
+ * 128-wide segment of K are 1 KiB of contiguous memory.  This is the
+ * "packed-weight layout" part that the bitsandbytes pull request "[ROCm]
+ * Optimize kgemm_4bit_inference_naive ..." leaves to the kernel (its kernel
+ * reads whole packed rows with 128-bit loads, section on the kernel's
+ * optimizations); the arrangement below is this library's.
+ *
+ *   Tile t = rows 16t .. 16t+15; segment s = bytes 64s .. 64s+63 of a row
+ *   (k = 128s .. 128s+127).  Unit (t, s) is the 1024 bytes at offset
+ *   (t * K/128 + s) * 1024; its 16-byte piece l (l = 0..63) holds bytes
+ *   64s + 16 * (l / 16) .. +16 of row 16t + l % 16.
+ *
+ * Within a piece the bytes, nibble order and codes are those of the
+ * row-major layout, and absmax keeps its row-major [N, K/blocksize] layout.
+ * Requires N % 16 == 0, K % 128 == 0 and N*K/2 below 4 GiB.  Reading each
+ * tile as one contiguous run gives the DRAM longer bursts than 64-byte
+ * pieces of 16 rows 4 KiB or more apart (a read-only pattern test on MI355X:
+ * 22.2 against 24.4 us for 117 MB).
+ */
+
+/*
+ * q4_repack_tiles: Wtiles = the tile layout of the row-major Wpacked.
+ *
+ *  Wpacked  uint8 [N, K/2] (device), Wtiles uint8 [N*K/2] (device), both
+ *           16-byte aligned and not overlapping.  A pure byte permutation,
+ *           bit-exact.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, N/K < 0, K == 0, N % 16 != 0,
+ *    K % 128 != 0, misalignment, overlapping buffers.
+ *  Q4_ERR_UNSUPPORTED: N*K/2 >= 4 GiB.
+ */
+q4_status q4_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K, void *stream);
+
+/*
+ * q4_gemm_skinny_tiles: q4_gemm_skinny_ex over weights in the tile layout.
+ *
+ * Arguments, dispatch (fused kernels up to the crossover, split path above)
+ * and results are those of q4_gemm_skinny_ex on the row-major weights the
+ * tiles were made from; the outputs are bit-identical to it (every kernel
+ * sees the same bytes in the same registers and sums in the same order).
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: as q4_gemm_skinny_ex, plus N % 16 != 0 or
+ *    K % 128 != 0.
+ *  Q4_ERR_UNSUPPORTED: as q4_gemm_skinny_ex, plus blocksize 32 (whose
+ *    vector-ALU kernel reads rows) and N*K/2 beyond the matrix-core kernels'
+ *    32-bit offsets.
+ */
+q4_status q4_gemm_skinny_tiles(const void *A, int a_dtype, const uint8_t *Wtiles,
+                               const float *absmax, const float *codebook, const void *bias,
+                               int M, int N, int K, int blocksize, void *C, int c_dtype,
+                               void *stream, int path);
+
+/*
  * bf16_gemm_skinny: C = A * W^T (+ bias) for unquantized bf16 weights.
  *
  * Defined by the report on vLLM pull request 40687 "Support N=5 in wvSplitK
@@ -177,6 +233,15 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
  */
 q4_status q4_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,
                      int N, int K, int blocksize, void *out, int out_dtype, void *stream);
+
+/*
+ * q4_dequant_tiles: q4_dequant over weights in the tile layout; `out` is
+ * row-major [N, K] and bit-identical to q4_dequant of the row-major weights.
+ *  Errors: as q4_dequant, plus those of the tile layout in
+ *  q4_gemm_skinny_tiles.
+ */
+q4_status q4_dequant_tiles(const uint8_t *Wtiles, const float *absmax, const float *codebook,
+                           int N, int K, int blocksize, void *out, int out_dtype, void *stream);
 
 /*
  * q4_quantize: blockwise 4-bit quantization, the inverse of q4_dequant.
