@@ -14,9 +14,11 @@
 // absmax[i >> bs_log2].
 //
 // Weights in the tile layout (16-row tiles of 1 KiB units, see
-// repack_tiles_kernel) are gathered: flat word i of row n = i / (K/8) is read
-// from its place in the unit of (n / 16, segment); the output order, the
-// scales and the arithmetic are the row-major ones.
+// repack_tiles_kernel) take dequant_tiles_kernel: the same arithmetic in the
+// order of the tiles, each lane turning one 16-byte piece (32 weights of one
+// row, inside one scale block since bs >= 64) into 32 outputs; 16-bit outputs
+// go through LDS so that the stores run along rows (1 KiB per row and
+// store), fp32 outputs are stored from the lanes (128 bytes each).
 #include "device.h"
 #include "launch.h"
 
@@ -32,7 +34,6 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
                                                            const float *__restrict__ absmax,
                                                            const float *__restrict__ codebook,
                                                            uint64_t words, int bs_log2,
-                                                           int wl, uint32_t kw, uint32_t nseg,
                                                            void *__restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int table = __float_as_int(codebook[lane & 15]);
@@ -47,15 +48,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t i = base + u * 64 + lane;
             const uint64_t ic = i < words ? i : words - 1;
-            uint64_t src = ic;
-            if (wl) {
-                // word c of row n: 16-byte piece c / 4 of segment c / 16, held
-                // by lane (n % 16) + 16 * ((c / 4) % 4) of unit (n / 16, segment)
-                const uint32_t n = (uint32_t)ic / kw, c = (uint32_t)ic - n * kw;
-                const uint32_t l = (n & 15) + 16 * ((c >> 2) & 3);
-                src = ((uint64_t)((n >> 4) * nseg + (c >> 4)) << 8) + 4 * l + (c & 3);
-            }
-            d[u] = packed[src];
+            d[u] = packed[ic];
             am[u] = absmax[(ic * 8) >> bs_log2];
         }
 #pragma unroll
@@ -92,6 +85,85 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t *__res
                     o[1] = make_float4(w[4], w[5], w[6], w[7]);
                 }
             }
+        }
+    }
+}
+
+template <int OT>
+__global__ __launch_bounds__(kThreads) void dequant_tiles_kernel(
+    const uint4 *__restrict__ tiles, const float *__restrict__ absmax,
+    const float *__restrict__ codebook, uint32_t pieces, uint32_t nseg, int K, int bs_log2,
+    void *__restrict__ out) {
+    constexpr int kRowLds = 272, kUnitLds = 16 * kRowLds;
+    __shared__ __attribute__((aligned(16))) char stage[OT == kF32 ? 16 : 4 * kUnitLds];
+    const int lane = threadIdx.x & 63;
+    const int table = __float_as_int(codebook[lane & 15]);
+    const uint32_t nb = (uint32_t)K >> bs_log2;
+    const uint32_t stride = gridDim.x * kThreads;
+    // every thread runs each step (the lookup is cross-lane, the staging
+    // needs the block's barriers); lanes past the end repeat the last piece
+    // and store nothing
+    const uint32_t p_end = (pieces + stride - 1) / stride * stride;
+    for (uint32_t p0 = blockIdx.x * kThreads + threadIdx.x; p0 < p_end; p0 += stride) {
+        const uint32_t p = p0 < pieces ? p0 : pieces - 1;
+        const uint32_t unit = p >> 6, l = p & 63;
+        const uint32_t t = unit / nseg, seg = unit - t * nseg;
+        const uint32_t n = 16 * t + (l & 15);
+        const uint32_t k0 = 128 * seg + 32 * (l >> 4);  // first of the piece's 32 weights
+        const uint4 v = tiles[p];
+        const float am = absmax[n * nb + (k0 >> bs_log2)];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        float w[32];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[8 * u + j] = cb_lookup(table, d[u] >> (4 * j)) * am;
+        const bool live = p0 < pieces;
+        const size_t e0 = (size_t)n * (size_t)K + k0;  // first output element
+        if constexpr (OT == kF32) {
+            float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + e0);
+            if (live)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    o[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+        } else {
+            if constexpr (OT == kF16) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) __asm__ volatile("" : "+v"(w[j]));
+            }
+            // Staged through LDS so that the stores run along rows: wave w
+            // puts its unit's 16 rows x 256 bytes at w * kUnitLds (rows kRowLds
+            // apart, 16 bytes of padding keep the 16 rows of a store in
+            // distinct banks); then store c of the block writes row c / 64,
+            // 16-byte chunk c % 64 of the four units' runs (one 1 KiB run per
+            // row when the four units are consecutive segments of one tile).
+            const int wv = threadIdx.x >> 6;
+            char *mine = stage + wv * kUnitLds + (l & 15) * kRowLds + 64 * (l >> 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t h[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    h[j] = OT == kBf16 ? f32_to_bf16_rne(w[8 * q + j]) : f32_to_f16_rne(w[8 * q + j]);
+                *reinterpret_cast<uint4 *>(mine + 16 * q) =
+                    make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                               h[6] | (h[7] << 16));
+            }
+            __syncthreads();
+            const uint32_t unit0 = (p0 - threadIdx.x) >> 6;  // the block's first unit
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = (int)threadIdx.x + kThreads * i;
+                const int r = c >> 6, uw = (c >> 4) & 3, y = c & 15;
+                const uint32_t u = unit0 + (uint32_t)uw;
+                const uint32_t ut = u / nseg, us = u - ut * nseg;
+                const uint4 v16 = *reinterpret_cast<const uint4 *>(stage + uw * kUnitLds + r * kRowLds + 16 * y);
+                if (u < pieces / 64) {
+                    const size_t e = (size_t)(16 * ut + r) * (size_t)K + 128 * us + 8 * y;
+                    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + e) = v16;
+                }
+            }
+            __syncthreads();
         }
     }
 }
@@ -137,7 +209,26 @@ hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const flo
                           int N, int K, int bs_log2, int wl, void *out, int out_dt, hipStream_t s) {
     if (wl && (N % 16 != 0 || K % 128 != 0 || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32)))
         return hipErrorInvalidValue;
-    const uint32_t kw = (uint32_t)K / 8, nseg = (uint32_t)K / 128;
+    if (wl) {
+        const uint32_t pieces = (uint32_t)((uint64_t)N * (uint64_t)K / 32);
+        const DeviceInfo info = device_info();
+        uint32_t blocks = (pieces + kThreads - 1) / kThreads;
+        const uint32_t cap = (uint32_t)info.num_cus * 8;
+        if (blocks > cap) blocks = cap;
+        if (blocks == 0) return hipSuccess;
+        const uint4 *tiles = reinterpret_cast<const uint4 *>(Wpacked);
+        const uint32_t nseg = (uint32_t)K / 128;
+        if (out_dt == kBf16)
+            dequant_tiles_kernel<kBf16><<<dim3(blocks), dim3(kThreads), 0, s>>>(
+                tiles, absmax, codebook, pieces, nseg, K, bs_log2, out);
+        else if (out_dt == kF16)
+            dequant_tiles_kernel<kF16><<<dim3(blocks), dim3(kThreads), 0, s>>>(
+                tiles, absmax, codebook, pieces, nseg, K, bs_log2, out);
+        else
+            dequant_tiles_kernel<kF32><<<dim3(blocks), dim3(kThreads), 0, s>>>(
+                tiles, absmax, codebook, pieces, nseg, K, bs_log2, out);
+        return hipGetLastError();
+    }
     const uint64_t words = (uint64_t)N * (uint64_t)K / 8;
     const DeviceInfo info = device_info();
     const uint64_t per_block = (uint64_t)kThreads * kUnroll;
@@ -148,13 +239,13 @@ hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const flo
     const uint32_t *packed = reinterpret_cast<const uint32_t *>(Wpacked);
     if (out_dt == kBf16)
         dequant_kernel<kBf16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            packed, absmax, codebook, words, bs_log2, wl, kw, nseg, out);
+            packed, absmax, codebook, words, bs_log2, out);
     else if (out_dt == kF16)
         dequant_kernel<kF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            packed, absmax, codebook, words, bs_log2, wl, kw, nseg, out);
+            packed, absmax, codebook, words, bs_log2, out);
     else
         dequant_kernel<kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            packed, absmax, codebook, words, bs_log2, wl, kw, nseg, out);
+            packed, absmax, codebook, words, bs_log2, out);
     return hipGetLastError();
 }
 
