@@ -1,6 +1,8 @@
 // Fused 4-bit dequantize + GEMM on the matrix cores for tens to hundreds of
 // token rows: C[M,N] = A[M,K] * dequant(W)^T (+ bias), bf16 activations,
-// blocksize >= 64.
+// blocksize >= 64.  The packed weights are row-major or in the tile layout
+// (wl = 1: 16-row tiles of 1 KiB units); a lane loads the same 16 bytes
+// either way, only its offset and the segment stride differ.
 //
 // The bitsandbytes pull request "[ROCm] Optimize kgemm_4bit_inference_naive
 // for ROCm, use it for batch sizes other than 1" finds (section "Fused path
