@@ -14,7 +14,7 @@ Entry points (same names as the C ABI in include/q4skinny.h):
   q4_codebook_preset(name)   "nf4_style" or "int4" -> numpy float32 [16]
   q4_get_crossover_m() / q4_set_crossover_m(m) / q4_release_workspace()
   q4_set_crossover_shape(N, K, m) / q4_get_crossover_shape(N, K) / q4_clear_crossover_shapes()
-  q4_copy_probe(src, dst) / q4_version()
+  q4_copy_probe(src, dst) / q4_read_probe(src, sink, ...) / q4_version()
 ``lib()`` returns the raw ctypes handle for callers that pass pointers.
 """
 from __future__ import annotations
@@ -36,7 +36,7 @@ EXPORTS = (
     "q4_get_crossover_m", "q4_set_crossover_m", "q4_release_workspace", "q4_last_error",
     "q4_copy_probe", "q4_version", "q4_quantize", "q4_codebook_preset",
     "q4_set_crossover_shape", "q4_get_crossover_shape", "q4_clear_crossover_shapes",
-    "q4_repack_tiles", "q4_gemm_skinny_tiles", "q4_dequant_tiles",
+    "q4_repack_tiles", "q4_gemm_skinny_tiles", "q4_dequant_tiles", "q4_read_probe",
 )
 PRESETS = {"nf4_style": 0, "int4": 1}
 
@@ -72,6 +72,7 @@ def lib():
         L.q4_dequant_tiles.argtypes = [P, P, P, I, I, I, P, I, P]
         L.q4_repack_tiles.argtypes = [P, P, I, I, P]
         L.q4_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
+        L.q4_read_probe.argtypes = [P, ctypes.c_size_t, P, I, I, I, I, P]
         L.q4_set_crossover_m.argtypes = [I]
         L.q4_quantize.argtypes = [P, I, P, I, I, I, P, P, P]
         L.q4_codebook_preset.argtypes = [I, P]
@@ -80,7 +81,8 @@ def lib():
         L.q4_get_crossover_shape.restype = ctypes.c_int
         for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
                      "bf16_gemm_skinny", "q4_dequant",
-                     "q4_copy_probe", "q4_set_crossover_m", "q4_release_workspace",
+                     "q4_copy_probe", "q4_read_probe", "q4_set_crossover_m",
+                     "q4_release_workspace",
                      "q4_quantize", "q4_codebook_preset", "q4_set_crossover_shape",
                      "q4_clear_crossover_shapes"):
             getattr(L, name).restype = ctypes.c_int
@@ -252,6 +254,23 @@ def q4_copy_probe(src, dst):
                                _stream(src)))
     del torch
     return dst
+
+
+PROBE_NONTEMPORAL, PROBE_INTERLEAVE = 1, 2
+
+
+def q4_read_probe(src, sink, threads: int = 0, unroll: int = 0, wgs_per_cu: int = 0,
+                  nontemporal: bool = True, interleave: bool = False):
+    """Reads all of src (a contiguous GPU tensor) once; sink is a GPU tensor of
+    at least 4 bytes (written only when the folded data hits a fixed value)."""
+    torch = _torch()
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold 4 bytes")
+    flags = (PROBE_NONTEMPORAL if nontemporal else 0) | (PROBE_INTERLEAVE if interleave else 0)
+    _check(lib().q4_read_probe(_dev(src, "src", src.dtype), nbytes, _dev(sink, "sink", sink.dtype),
+                               int(threads), int(unroll), int(wgs_per_cu), flags, _stream(src)))
+    del torch
 
 
 def q4_get_crossover_m() -> int:

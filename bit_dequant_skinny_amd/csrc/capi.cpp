@@ -70,7 +70,7 @@ q4_status ok() {
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---- test hook: Q4_TEST_FAIL_LAUNCH=<kernel>[:count] --------------------------
-// kernel: fused, dequant, gemm, planes, plane sum, quantize or copy.  Makes the
+// kernel: fused, dequant, gemm, planes, plane sum, quantize, copy or read.  Makes the
 // next `count` launches of that kernel report a launch failure without
 // launching, so tests can check the error path and the recovery.
 std::once_flag g_hook_once;
@@ -165,7 +165,15 @@ int crossover_for(int N, int K) {
     return it != g_shape_crossover.end() ? it->second : crossover();
 }
 
-// ---- split-path workspace: one buffer per (device, stream) ------------------
+// ---- workspace: one buffer per (device, stream) -------------------------------
+// The split path's bf16 weights, the activation planes of fp16 / fp32 inputs
+// and the fp32 partial outputs of K splits.  One buffer per stream, so that
+// calls on different streams never share scratch; grown on demand.  Growing
+// frees the old buffer: HIP graphs captured earlier with calls that used it
+// must not be replayed after a call that grows it.  Growing during a stream
+// capture is refused (an allocation cannot be captured): the first call of a
+// shape runs eagerly, later calls of the same or a smaller size reuse the
+// buffer and can be captured.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
@@ -177,19 +185,32 @@ q4_status workspace(int device, hipStream_t s, size_t bytes, void **out) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[{device, s}];
     if (w.bytes < bytes) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(s, &cap);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(Q4_ERR_HIP, "workspace: hipStreamIsCapturing: %s", hipGetErrorString(e));
+        }
+        if (cap != hipStreamCaptureStatusNone)
+            return fail(Q4_ERR_HIP,
+                        "workspace of %zu bytes needed while the stream is being captured "
+                        "(have %zu): run the call once outside the capture first",
+                        bytes, w.bytes);
         if (w.ptr) {
-            // The old buffer may still be read by work queued on `s`.
-            hipError_t e = hipStreamSynchronize(s);
-            if (e == hipSuccess) e = hipFree(w.ptr);
+            // The old buffer may still be read by work queued on `s`; it is
+            // freed even if that wait fails.
+            hipError_t se = hipStreamSynchronize(s);
+            hipError_t fe = hipFree(w.ptr);
             w.ptr = nullptr;
             w.bytes = 0;
-            if (e != hipSuccess) {
+            if (se != hipSuccess || fe != hipSuccess) {
                 (void)hipGetLastError();
-                return fail(Q4_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+                return fail(Q4_ERR_HIP, "workspace release: %s",
+                            hipGetErrorString(se != hipSuccess ? se : fe));
             }
         }
         void *p = nullptr;
-        hipError_t e = hipMalloc(&p, bytes);
+        e = hipMalloc(&p, bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(Q4_ERR_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
@@ -731,20 +752,28 @@ q4_status q4_clear_crossover_shapes(void) {
 q4_status q4_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     q4_status st = Q4_OK;
+    int prev = 0;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    // Each device that owns a buffer is synchronised once (the streams the
+    // buffers were used on may no longer exist), then its buffers are freed.
+    std::map<int, bool> synced;
     for (auto &kv : g_ws) {
         if (!kv.second.ptr) continue;
-        int prev = 0;
-        (void)hipGetDevice(&prev);
-        hipError_t e = hipSetDevice(kv.first.first);
-        if (e == hipSuccess) e = hipStreamSynchronize(kv.first.second);
-        if (e == hipSuccess) e = hipFree(kv.second.ptr);
-        (void)hipSetDevice(prev);
+        const int device = kv.first.first;
+        hipError_t e = hipSetDevice(device);
+        if (e == hipSuccess && !synced[device]) {
+            e = hipDeviceSynchronize();
+            synced[device] = true;
+        }
+        const hipError_t fe = hipFree(kv.second.ptr);
+        if (e == hipSuccess) e = fe;
         if (e != hipSuccess && st == Q4_OK) {
             (void)hipGetLastError();
             st = fail(Q4_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
         }
     }
     g_ws.clear();
+    if (have_prev) (void)hipSetDevice(prev);
     return st == Q4_OK ? ok() : st;
 }
 
@@ -762,6 +791,34 @@ q4_status q4_copy_probe(const void *src, void *dst, size_t bytes, void *stream) 
     return st == Q4_OK ? ok() : st;
 }
 
-const char *q4_version(void) { return "q4skinny 0.1.0 (gfx950)"; }
+q4_status q4_read_probe(const void *src, size_t bytes, uint32_t *sink, int threads, int unroll,
+                        int wgs_per_cu, int flags, void *stream) {
+    if (threads == 0) threads = Q4_READ_PROBE_THREADS;
+    if (unroll == 0) unroll = Q4_READ_PROBE_UNROLL;
+    if (wgs_per_cu == 0) wgs_per_cu = Q4_READ_PROBE_WGS_PER_CU;
+    if (!q4::read_probe_shape_ok(threads, unroll) || wgs_per_cu < 1 || wgs_per_cu > 32 ||
+        (flags & ~(Q4_PROBE_NONTEMPORAL | Q4_PROBE_INTERLEAVE)) != 0)
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "read probe shape: threads %d (256, 512, 1024), unroll %d (2, 4, 8), "
+                    "workgroups per CU %d (1..32), flags 0x%x",
+                    threads, unroll, wgs_per_cu, flags);
+    if (bytes >= (size_t(1) << 32))
+        return fail(Q4_ERR_UNSUPPORTED, "read probe over %zu bytes (below 4 GiB)", bytes);
+    if (bytes == 0) return ok();
+    if (!src || !sink) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (bytes % 16 || !aligned(src, 16) || !aligned(sink, 4))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "bytes and src must be multiples of 16, sink 4-byte aligned");
+    drain_prior_error();
+    q4_status st = launch_checked("read", [&] {
+        return q4::launch_read_probe(src, bytes, sink, threads, unroll, wgs_per_cu,
+                                     (flags & Q4_PROBE_NONTEMPORAL) != 0,
+                                     (flags & Q4_PROBE_INTERLEAVE) != 0,
+                                     static_cast<hipStream_t>(stream));
+    });
+    return st == Q4_OK ? ok() : st;
+}
+
+const char *q4_version(void) { return "q4skinny 0.2.0 (gfx950)"; }
 
 }  // extern "C"

@@ -75,9 +75,10 @@ __device__ __forceinline__ void store_elem(void *p, size_t i, float v, int dt) {
 // Packed-byte decode table of the matrix-core kernels.  Entry e (a packed
 // byte, low nibble = even k) holds x = (hi(cb[e & 15]), hi(cb[e >> 4])) and
 // y = (lo(cb[e & 15]), lo(cb[e >> 4])) in bf16, where hi = bf16(cb) and
-// lo = bf16(cb - hi): hi + lo equals the fp32 codebook value to within 2^-18
-// relative.  Two entries back to back, [x0 y0 x1 y1], form the operand
-// [hi(c0) hi(c1) lo(c0) lo(c1) hi(c2) hi(c3) lo(c2) lo(c3)] of
+// lo = bf16(cb - hi): hi + lo equals the fp32 codebook value to within 2^-16
+// relative (two roundings to 8 significant bits), and exactly when the value
+// has at most 16 significant bits.  Two entries back to back, [x0 y0 x1 y1],
+// form the operand [hi(c0) hi(c1) lo(c0) lo(c1) hi(c2) hi(c3) lo(c2) lo(c3)] of
 // v_mfma_f32_16x16x32_bf16, which against the activations [a0 a1 a0 a1 a2 a3
 // a2 a3] forms a*hi + a*lo exactly in the fp32 accumulator.
 __device__ __forceinline__ uint2 pair_table_entry(float c0, float c1) {

@@ -9,7 +9,8 @@
 // Decode.  A 256-entry LDS table maps one packed byte (two codes c0, c1) to
 // two dwords: (hi(c0), hi(c1)) and (lo(c0), lo(c1)) in bf16, where
 // hi = bf16(cb) and lo = bf16(cb - hi), so hi + lo equals the fp32 codebook
-// value to within 2^-18 relative.  One ds_read_b64 decodes two weights.  Two
+// value to within 2^-16 relative (exactly for values of at most 16
+// significant bits).  One ds_read_b64 decodes two weights.  Two
 // such reads form one B operand of v_mfma_f32_16x16x32_bf16 laid out
 // [hi(c0) hi(c1) lo(c0) lo(c1) hi(c2) hi(c3) lo(c2) lo(c3)] against the A
 // operand [a0 a1 a0 a1 a2 a3 a2 a3], so the matrix core forms a*hi + a*lo
@@ -191,9 +192,16 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint32_t s_piece = (uint32_t)(tid % (4 * P)) * 16;
     const uint32_t s_win = (uint32_t)(P * KW * 128 * 4) >> bs_log2;  // bytes per row per period
     int sc = 0, sq = 0;  // scale cursor: the first slot of the period loaded next
+    // Bytes of this thread's piece that lie inside the row (a piece may run
+    // past the row's last block when K / bs is not a multiple of 4: those
+    // scales belong to the next row and are zeroed at staging, so that a
+    // non-finite scale there cannot turn the 0 * scale of the padded blocks
+    // into NaN).
+    int s_rem = 16;
     auto load_scales = [&](floatx4 (&out)[SP]) {
         const uint32_t w0 = ((uint32_t)((sq + rot) % spw) * KW * 128 >> bs_log2) * 4;  // window start
         const bool live = sc < my_chunks && s_piece < s_win && w0 + s_piece < nb * 4;
+        s_rem = (int)(nb * 4) - (int)(w0 + s_piece);
 #pragma unroll
         for (int i = 0; i < SP; ++i) {
             const int row = s_row + i * (128 / P);
@@ -215,8 +223,10 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < SP; ++i) {
             float *row = &scl[buf][(s_row + i * (128 / P)) * kScaleStride + (s_piece >> 2)];
-            *reinterpret_cast<floatx2 *>(row) = floatx2{v[i][0], v[i][1]};
-            *reinterpret_cast<floatx2 *>(row + 2) = floatx2{v[i][2], v[i][3]};
+            const float x0 = s_rem > 0 ? v[i][0] : 0.f, x1 = s_rem > 4 ? v[i][1] : 0.f;
+            const float x2 = s_rem > 8 ? v[i][2] : 0.f, x3 = s_rem > 12 ? v[i][3] : 0.f;
+            *reinterpret_cast<floatx2 *>(row) = floatx2{x0, x1};
+            *reinterpret_cast<floatx2 *>(row + 2) = floatx2{x2, x3};
         }
     };
     // In slot u of a period, wave w applies the scales of the 64-wide blocks
@@ -390,12 +400,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                 }
             };
             if constexpr (DB == 2) {
-                // The next unit's decode in two halves around this unit's
-                // MFMAs, so its table reads fly while the MFMAs run.  Halves
-                // of 8 reads keep the reads in flight at any wait within the
-                // 4-bit LDS counter (at most 15 outstanding): with all 17
-                // reads issued at once, waiting for an older read also waited
-                // for the first of them.
+                // The next unit's decode interleaved with this unit's MFMAs,
+                // so its table reads fly while the MFMAs run.
                 uint32_t xn[4];
                 if (tr + 1 < TB) {
                     swap_w(wbuf[r_cur][tr + 1], xn);
@@ -405,19 +411,24 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                     w_advance();
                     swap_w(wbuf[r_next][0], xn);
                 }
-                lookups(xn, e[enext], 0, 8);
-                __builtin_amdgcn_sched_barrier(0);
-                mfma_steps(0, 2);
-                __builtin_amdgcn_sched_barrier(0);
-                lookups(xn, e[enext], 8, 16);
+                lookups(xn, e[enext], 0, 16);
                 if (tr + 1 < TB) {
                     am[cur ^ 1] = read_scales(scs + (tr + 1) * 16 * kScaleStride);
                     issue(wbuf[r_cur][tr + 1], tr + 1);
                 } else {
                     issue(wbuf[r_next][0], 0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                mfma_steps(2, 4);
+                mfma_steps(0, 4);
+                // Each MFMA followed by four VALU instructions and two table
+                // reads of the next unit, so one wave keeps the matrix core,
+                // the VALU and the LDS busy together (the compiler otherwise
+                // clusters the dependent MFMAs of a chain).
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+                }
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 // One decode buffer: the next unit's table reads follow this

@@ -16,7 +16,7 @@
 //
 // Decode.  A 256-entry LDS table maps one packed byte to the bf16 hi and lo
 // parts of its two codebook values (hi = bf16(cb), lo = bf16(cb - hi), so
-// hi + lo is the fp32 value to within 2^-18 relative), 32 copies of each so
+// hi + lo is the fp32 value to within 2^-16 relative), 32 copies of each so
 // that the lookups of a half-wave never share a bank.  Four lookups give the
 // hi parts of a dword's 8 codes and four more the lo parts: two B operands of
 // v_mfma_f32_16x16x32_bf16 against the same 8 activations as loaded, so the

@@ -91,5 +91,13 @@ hipError_t launch_quantize(const void *W, int w_dt, int N, int K, int bs_log2,
                            hipStream_t s);
 
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
+// Read-only stream over `bytes` (< 4 GiB) by num_cus * wgs_per_cu workgroups
+// of `threads` (256, 512, 1024) lanes, `unroll` (2, 4, 8) 16-byte loads per
+// lane per batch; nt = non-temporal loads, interleave = batches dealt round
+// robin instead of contiguous shares.  `sink` (4 bytes) is written only if
+// the folded data equals a fixed value.
+bool read_probe_shape_ok(int threads, int unroll);
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int threads,
+                             int unroll, int wgs_per_cu, int nt, int interleave, hipStream_t s);
 
 }  // namespace q4

@@ -99,8 +99,15 @@ q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *abs
 
 /*
  * q4_gemm_skinny_path: q4_gemm_skinny with the path forced (Q4_PATH_AUTO,
- * Q4_PATH_FUSED or Q4_PATH_SPLIT).  Used by the crossover measurement and
- * the tests.  An unknown path value is Q4_ERR_INVALID_ARGUMENT.
+ * Q4_PATH_FUSED or Q4_PATH_SPLIT).
+ *
+ * The two paths are those the bitsandbytes pull request "[ROCm] Optimize
+ * kgemm_4bit_inference_naive for ROCm, use it for batch sizes other than 1"
+ * times against each other (section "Fused path support for M > 1" and its
+ * split-versus-fused table): the fused dequantize + GEMM kernel, and the split
+ * dequantize-to-bf16 then GEMM.  Forcing one is how the crossover is measured
+ * and how the tests reach both.  Arguments, outputs and errors are those of
+ * q4_gemm_skinny; an unknown path value is Q4_ERR_INVALID_ARGUMENT.
  */
 q4_status q4_gemm_skinny_path(const void *A, const uint8_t *Wpacked, const float *absmax,
                               const float *codebook, int M, int N, int K, int blocksize,
@@ -289,9 +296,16 @@ q4_status q4_codebook_preset(int which, float *codebook);
 
 /*
  * Crossover control.  The fused-versus-split threshold (fused when
- * M <= crossover) starts at the value measured on MI355X and compiled in,
- * unless the environment variable Q4_CROSSOVER_M holds an integer at the
- * first call.  q4_set_crossover_m accepts 0..Q4_CROSSOVER_MAX (0 = always split).
+ * M <= crossover) of the bitsandbytes pull request "[ROCm] Optimize
+ * kgemm_4bit_inference_naive ..." (section "Fused path support for M > 1":
+ * the crossover M differs per GPU, and one threshold is chosen so that the
+ * fused path is kept wherever it wins on the slowest-crossing GPU).  Here
+ * it starts at the value measured on MI355X and compiled in, unless the
+ * environment variable Q4_CROSSOVER_M holds an integer at the first call.
+ *  q4_get_crossover_m  the process-wide value (shapes without an entry of
+ *                      their own use it).
+ *  q4_set_crossover_m  sets it; 0..Q4_CROSSOVER_MAX (0 = always split), else
+ *                      Q4_ERR_INVALID_ARGUMENT and the value is unchanged.
  */
 int q4_get_crossover_m(void);
 q4_status q4_set_crossover_m(int m);
@@ -320,11 +334,32 @@ q4_status q4_set_crossover_shape(int N, int K, int m);
 int q4_get_crossover_shape(int N, int K);
 q4_status q4_clear_crossover_shapes(void);
 
-/* Frees the split-path workspaces of every device and stream (synchronises
- * the devices that own them).  Safe to call at any time between calls. */
+/*
+ * q4_release_workspace: frees the library-owned scratch of every device and
+ * stream.  The split path of the bitsandbytes pull request "[ROCm] Optimize
+ * kgemm_4bit_inference_naive ..." (section "Fused path support for M > 1")
+ * dequantizes W to bf16 before the GEMM, so that path needs an N*K*2-byte
+ * buffer; it also holds the activation planes of fp16 / fp32 inputs and the
+ * fp32 partial outputs of K splits.  The library keeps one buffer per
+ * (device, stream), grown on demand: a growth frees the previous buffer, so
+ * HIP graphs captured with calls that used it must not be replayed after a
+ * call that grows it, or after this call.  A growth is refused while its
+ * stream is being captured (Q4_ERR_HIP; run the call once eagerly first).
+ * Each device that owns a buffer is synchronised before its buffers are
+ * freed.  Returns Q4_ERR_HIP (and still forgets every buffer) if a
+ * synchronisation or free fails.
+ */
 q4_status q4_release_workspace(void);
 
-/* Message for the last failing call on this thread ("" if none). */
+/*
+ * q4_last_error: the message of the last failing call on the calling thread
+ * ("" after a successful call); valid until the thread's next call into the
+ * library.  Every entry point returns a status the caller acts on and drains
+ * the HIP runtime's last-error flag after a failed launch, the convention of
+ * the bitsandbytes pull request "Cache the hipBLASLt int8 matmul algo per
+ * problem on ROCm" (its csrc/ops.cu change); this accessor carries the
+ * runtime's or the validator's message to the caller.
+ */
 const char *q4_last_error(void);
 
 /*
@@ -334,6 +369,38 @@ const char *q4_last_error(void);
  * and scales hardware byte counters against a transfer of known size.
  */
 q4_status q4_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
+
+/*
+ * q4_read_probe: reads `bytes` bytes at `src` once with 128-bit buffer loads
+ * and writes (almost) nothing.  A measurement aid: the achievable HBM read
+ * rate of one launch over a buffer of that size, the ceiling of kernels that
+ * stream their weights once, against which the bitsandbytes pull request
+ * "[ROCm] Optimize kgemm_4bit_inference_naive for ROCm, use it for batch
+ * sizes other than 1" also quotes a measured peak (table
+ * "kgemm_4bit_inference_naive benchmark").
+ *
+ *  src         device buffer, 16-byte aligned; bytes a multiple of 16, below
+ *              4 GiB.
+ *  sink        device buffer of one uint32, written only when the folded
+ *              data equals a fixed value (it keeps every load live).
+ *  threads     lanes per workgroup: 256, 512 or 1024 (0 = the default below).
+ *  unroll      16-byte loads per lane per batch: 2, 4 or 8 (0 = default);
+ *              about twice that many are in flight per lane.
+ *  wgs_per_cu  workgroups per compute unit, 1..32 (0 = default).
+ *  flags       Q4_PROBE_NONTEMPORAL: the loads carry the non-temporal hint
+ *              of the fused kernels' weight loads; Q4_PROBE_INTERLEAVE:
+ *              batches are dealt round robin to the workgroups instead of
+ *              one contiguous share each.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, misalignment, a launch shape or
+ *    flag outside the sets above.  Q4_ERR_UNSUPPORTED: bytes >= 4 GiB.
+ */
+#define Q4_READ_PROBE_THREADS 512
+#define Q4_READ_PROBE_UNROLL 8
+#define Q4_READ_PROBE_WGS_PER_CU 1
+enum { Q4_PROBE_NONTEMPORAL = 1, Q4_PROBE_INTERLEAVE = 2 };
+q4_status q4_read_probe(const void *src, size_t bytes, uint32_t *sink, int threads, int unroll,
+                        int wgs_per_cu, int flags, void *stream);
 
 /* Library version string. */
 const char *q4_version(void);

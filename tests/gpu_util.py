@@ -116,3 +116,43 @@ def q4_weights(N: int, K: int, bs: int, config: int, shape: int):
 def bf16_weights(N: int, K: int, config: int, shape: int):
     return (synth.bf16_weights(N, K, synth.seed(config, shape, 2)),
             synth.bias_bf16(N, synth.seed(config, shape, 3)))
+
+
+def _rne_bf16(x) -> np.ndarray:
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+
+
+def _widen_bf16(b) -> np.ndarray:
+    return (np.asarray(b).astype(np.uint32) << 16).view(np.float32)
+
+
+def hilo_codebook(cb) -> np.ndarray:
+    """The codebook as the matrix-core kernels hold it: bf16 hi = RNE(cb) plus
+    bf16 lo = RNE(cb - hi), summed in fp32 (hi + lo is exact in fp32).  It
+    equals cb exactly when cb has at most 16 significant bits, and is within
+    2^-16 relative otherwise."""
+    cb = np.asarray(cb, np.float32)
+    hi = _widen_bf16(_rne_bf16(cb))
+    lo = _widen_bf16(_rne_bf16((cb - hi).astype(np.float32)))
+    return (hi + lo).astype(np.float32)
+
+
+def hilo_products(cb):
+    """The bf16 bits a one-hot activation row yields through the matrix-core
+    kernels: fl32(absmax * (hi + lo)) rounded once to bf16."""
+    v = hilo_codebook(cb)
+    return lambda code, am: _rne_bf16(v[code] * np.asarray(am, np.float32)).astype(np.uint16)
+
+
+def codebook_16bit(seed: int) -> np.ndarray:
+    """A sorted random codebook in [-1, 1] holding -1, 0 and 1 whose entries
+    have at most 16 significant bits (the low 8 bits of each fp32 significand
+    cleared), so the matrix-core kernels' hi + lo pair holds it exactly."""
+    while True:
+        cb = synth.random_codebook(seed)
+        cb16 = (cb.view(np.uint32) & np.uint32(0xFFFFFF00)).view(np.float32)
+        if len(np.unique(cb16)) == 16:
+            assert np.array_equal(hilo_codebook(cb16), cb16)
+            return cb16
+        seed += 1000

@@ -103,3 +103,64 @@ def test_injected_launch_failure_and_recovery(case):
                        capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert ("ok " + case) in r.stdout
+
+
+WS_CHILD = r'''
+import sys
+import numpy as np
+import torch
+import bit_dequant_skinny_amd as q4
+import oracle, synth
+sys.path.insert(0, "tests")
+from gpu_util import assert_within_tolerance, bf16_host, q4_to_dev
+
+side = torch.cuda.Stream()
+bs = 64
+small = synth.q4_problem(4, 64, 512, bs, config=71)
+big = synth.q4_problem(4, 512, 2048, bs, config=72)
+As, Wps, ams, cbs = q4_to_dev(small)
+Ab, Wpb, amb, cbb = q4_to_dev(big)
+with torch.cuda.stream(side):
+    q4.q4_gemm_skinny(As, Wps, ams, cbs, bs, path="split")  # workspace sized for the small shape
+torch.cuda.synchronize()
+out = torch.zeros((4, 512), dtype=torch.bfloat16, device="cuda:0")
+g = torch.cuda.CUDAGraph()
+err = None
+with torch.cuda.graph(g, stream=side):
+    try:
+        q4.q4_gemm_skinny(Ab, Wpb, amb, cbb, bs, path="split", out=out)
+    except q4.Q4Error as e:
+        err = e
+assert err is not None and err.status == q4.Q4_ERR_HIP, err
+assert "captured" in str(err), str(err)
+torch.cuda.synchronize()
+assert torch.count_nonzero(out).item() == 0, "output written by a refused call"
+with torch.cuda.stream(side):
+    q4.q4_gemm_skinny(Ab, Wpb, amb, cbb, bs, path="split", out=out)
+torch.cuda.synchronize()
+Cr, S = oracle.q4_gemm_w16(big["A"], big["Wpacked"], big["absmax"], big["codebook"], 4, 512, 2048, bs)
+assert_within_tolerance(bf16_host(out), Cr, S, "split after a refused capture")
+# now the workspace is large enough: the same call can be captured and replayed
+g2 = torch.cuda.CUDAGraph()
+out2 = torch.zeros_like(out)
+with torch.cuda.graph(g2, stream=side):
+    q4.q4_gemm_skinny(Ab, Wpb, amb, cbb, bs, path="split", out=out2)
+for _ in range(3):
+    out2.zero_()
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+q4.q4_release_workspace()
+print("OK")
+'''
+
+
+def test_workspace_growth_during_capture_is_refused():
+    """A call that would grow its stream's workspace while the stream is
+    being captured returns Q4_ERR_HIP (no allocation can be captured) and
+    launches nothing; the same call run eagerly afterwards is correct, and
+    once the workspace is large enough the call captures and replays."""
+    r = subprocess.run([sys.executable, "-c", WS_CHILD], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout + r.stderr

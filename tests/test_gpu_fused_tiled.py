@@ -25,8 +25,8 @@ import pytest
 import bit_dequant_skinny_amd as q4
 import oracle
 import synth
-from gpu_util import (assert_within_tolerance, bf16_host, host_f64, q4_to_dev, q4_weights,
-                      sample_cols, to_dev, to_dev_dtype, torch)
+from gpu_util import (assert_within_tolerance, bf16_host, hilo_products, host_f64, q4_to_dev,
+                      q4_weights, sample_cols, to_dev, to_dev_dtype, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,27 +63,9 @@ def test_fused_tiled_scaling_and_determinism(M):
     assert torch().equal(C2, C1 * 2)
 
 
-def _hilo_products(cb, absmax_blocks):
-    """The value a one-hot row yields through the matrix cores: the codebook
-    held as bf16 hi + lo (hi = RNE(cb), lo = RNE(cb - hi)) times the block's
-    absmax in fp32, rounded to bf16 bits."""
-    def rne(x):
-        u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
-        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
-
-    def widen(b):
-        return (b.astype(np.uint32) << 16).view(np.float32)
-
-    cb = np.asarray(cb, np.float32)
-    hi = widen(rne(cb))
-    lo = widen(rne((cb - hi).astype(np.float32)))
-    v = (hi + lo).astype(np.float32)
-    return lambda code, am: rne(np.float32(v[code]) * np.float32(am)).astype(np.uint16)
-
-
 def test_fused_tiled_one_hot_rows_return_dequantized_rows():
     """Row m = e_j gives C[m, n] = the dequantized weight w(n, j).  The tiled
-    kernel holds each codebook value as hi + lo (within 2^-18 relative), so
+    kernel holds each codebook value as hi + lo (within 2^-16 relative), so
     where the fp32 product cb * absmax lies that close to a bf16 rounding
     midpoint the result may be the neighbouring bf16 value; everywhere else it
     must be the oracle's dequantized bf16 weight exactly."""
@@ -97,7 +79,7 @@ def test_fused_tiled_one_hot_rows_return_dequantized_rows():
     C = bf16_host(q4.q4_gemm_skinny(to_dev(A, "bf16"), Wp, am, cb, bs, path="fused"))
     _sync()
     w16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)[:, js].T
-    hilo = _hilo_products(p["codebook"], p["absmax"])
+    hilo = hilo_products(p["codebook"])
     codes = oracle.unpack(p["Wpacked"], N, K)[:, js].T
     scales = p["absmax"].reshape(N, K // bs)[:, np.array(js) // bs].T
     alt = hilo(codes, scales)

@@ -12,8 +12,8 @@ import pytest
 import bit_dequant_skinny_amd as q4
 import oracle
 import synth
-from gpu_util import (as_f64, assert_within_tolerance, bf16_host, dev, q4_to_dev, to_dev,
-                      torch)
+from gpu_util import (as_f64, assert_within_tolerance, bf16_host, codebook_16bit, dev,
+                      hilo_products, host_f64, q4_to_dev, to_dev, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,20 +77,105 @@ def test_fused_parity(M, N, K, bs):
     assert_within_tolerance(bf16_host(C), Cr, S, "fused M=%d N=%d K=%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("path", ["fused", "split"])
-def test_one_hot_rows_return_dequantized_rows(path):
-    """A one-hot row of A selects one dequantized weight per output exactly."""
-    N, K, bs = 48, 1024, 64
-    p = synth.q4_problem(1, N, K, bs, config=52, codebook=CODEBOOKS["nf4style"])
-    js = [0, 1, 31, 32, 63, 64, 511, 1023]
-    A = np.zeros((len(js), K), np.uint16)
+def _one_hot_case(N, K, bs, config, codebook, js, path, M_pad=0):
+    """C for activation rows e_j (j in js), the oracle's dequantized bf16
+    weights w16[:, js].T, and the bf16 value the matrix-core kernels give
+    for each of those weights (codebook held as hi + lo)."""
+    p = synth.q4_problem(1, N, K, bs, config=config, codebook=codebook)
+    A = np.zeros((len(js) + M_pad, K), np.uint16)
     for m, j in enumerate(js):
         A[m, j] = 0x3F80
     _, Wp, am, cb = q4_to_dev(p)
-    C = q4.q4_gemm_skinny(to_dev(A, "bf16"), Wp, am, cb, bs, path=path)
+    C = bf16_host(q4.q4_gemm_skinny(to_dev(A, "bf16"), Wp, am, cb, bs, path=path))[:len(js)]
     _sync()
-    w16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
-    assert np.array_equal(bf16_host(C), w16[:, js].T)
+    w16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)[:, js].T
+    codes = oracle.unpack(p["Wpacked"], N, K)[:, js].T
+    scales = p["absmax"].reshape(N, K // bs)[:, np.array(js) // bs].T
+    return C, w16, hilo_products(p["codebook"])(codes, scales)
+
+
+ONE_HOT_JS = [0, 1, 31, 32, 63, 64, 511, 1023]
+
+
+@pytest.mark.parametrize("path,cbname", [("split", "nf4style"), ("split", "random"),
+                                         ("fused", "int4"), ("fused", "random16")])
+def test_one_hot_rows_return_dequantized_rows(path, cbname):
+    """A one-hot row of A selects one dequantized weight per output exactly:
+    on the split path for any codebook (the GEMM multiplies the bf16 weights
+    by 1 and adds zeros), on the fused path for codebooks whose entries have
+    at most 16 significant bits (the kernel's bf16 hi + lo pair is then the
+    codebook value itself)."""
+    cb = {"int4": q4.q4_codebook_preset("int4"), "random16": codebook_16bit(52)}.get(
+        cbname, CODEBOOKS.get(cbname))
+    C, w16, _ = _one_hot_case(48, 1024, 64, 52, cb, ONE_HOT_JS, path)
+    assert np.array_equal(C, w16)
+
+
+@pytest.mark.parametrize("cbname", ["nf4style", "random"])
+def test_one_hot_rows_fused_two_value_form(cbname):
+    """With a full 24-bit codebook the fused kernel gives fl32(absmax (hi + lo))
+    rounded to bf16; where that differs from the dequantized weight (the fp32
+    product lies within 2^-16 of a bf16 rounding midpoint) either value is
+    accepted, everywhere else the dequantized weight exactly."""
+    js = list(range(0, 1024, 7))
+    C, w16, alt = _one_hot_case(200, 1024, 64, 152, CODEBOOKS[cbname], js, "fused")
+    same = w16 == alt
+    assert np.array_equal(C[same], w16[same])
+    assert np.all((C[~same] == w16[~same]) | (C[~same] == alt[~same]))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_skinny_special_block_scales(M):
+    """Blocks scaled by zero, by subnormals and by large finite values on the
+    skinny kernel (one and two token blocks), fp32 output."""
+    N, K, bs = 96, 1024, 64
+    p = synth.q4_problem(M, N, K, bs, config=57 + M)
+    am = p["absmax"].copy().reshape(N, K // bs)
+    am[3, :] = 0.0
+    am[10, 2] = np.float32(1e-40)
+    am[11, 5] = np.float32(3e-39)
+    am[12, :] = np.float32(2e-39)
+    am[20, 7] = np.float32(1e30)
+    am[:, 9] = 0.0
+    A, Wp, _, cb = q4_to_dev(p)
+    C = q4.q4_gemm_skinny(A, Wp, to_dev(am, "f32"), cb, bs, path="fused",
+                          out_dtype=torch().float32)
+    _sync()
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], am, p["codebook"], M, N, K, bs)
+    got = host_f64(C)
+    assert np.all(got[:, 3] == 0.0)
+    assert_within_tolerance(None, Cr, S, "special scales M=%d" % M, out="fp32", values=got)
+
+
+@pytest.mark.parametrize("layout,N,K", [("rows", 48, 1088), ("rows", 33, 576),
+                                        ("tiles", 48, 384), ("rows", 40, 1088)])
+@pytest.mark.parametrize("M", [1, 8])
+def test_ragged_blocks_ignore_the_next_rows_scales(layout, N, K, M):
+    """K / 64 not a multiple of 4: the last 16-byte piece of a row's scales
+    runs into the next row.  A non-finite scale at the start of a row must
+    not reach the row before it: that row stays finite and within tolerance,
+    and the row with the infinite scale is non-finite wherever its weight is."""
+    bs = 64
+    p = synth.q4_problem(M, N, K, bs, config=58)
+    am = p["absmax"].copy().reshape(N, K // bs)
+    bad_rows = [5, 16, 17, N - 1]
+    for r in bad_rows:
+        am[r, 0] = np.inf
+    am[9, 0] = np.nan
+    bad_rows.append(9)
+    A, Wp, _, cb = q4_to_dev(p)
+    if layout == "tiles":
+        Wp = q4.q4_repack_tiles(Wp)
+    C = q4.q4_gemm_skinny(A, Wp, to_dev(am, "f32"), cb, bs, path="fused", layout=layout,
+                          out_dtype=torch().float32)
+    _sync()
+    good = np.array([n for n in range(N) if n not in bad_rows])
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], am, p["codebook"], M, N, K, bs, cols=good)
+    got = host_f64(C)
+    assert np.all(np.isfinite(got[:, good]))
+    assert_within_tolerance(None, Cr, S, "ragged K=%d %s" % (K, layout), out="fp32",
+                            values=got[:, good])
+    assert not np.any(np.isfinite(got[:, bad_rows]))
 
 
 @pytest.mark.parametrize("path", ["fused", "split"])

@@ -15,8 +15,8 @@ import pytest
 import bit_dequant_skinny_amd as q4
 import oracle
 import synth
-from gpu_util import (assert_within_tolerance, bf16_host, q4_to_dev, q4_weights, sample_cols,
-                      to_dev, torch)
+from gpu_util import (assert_within_tolerance, bf16_host, codebook_16bit, hilo_products,
+                      q4_to_dev, q4_weights, sample_cols, to_dev, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,19 +64,36 @@ def test_eight_tile_shapes_take_the_tiled_kernel(M):
     assert_within_tolerance(bf16_host(C)[:, cols], Cr, S, "8-tile shape M=%d" % M)
 
 
-def test_two_block_one_hot_rows_return_dequantized_rows():
+@pytest.mark.parametrize("cbname", ["int4", "random16", "nf4style"])
+def test_two_block_one_hot_rows_return_dequantized_rows(cbname):
+    """Row m = e_j gives the dequantized weight w(n, j) bit for bit when every
+    codebook entry has at most 16 significant bits (the kernel's bf16 hi + lo
+    pair is then the entry itself).  With the 24-bit NF4-style table the
+    kernel gives fl32(absmax (hi + lo)) rounded to bf16, which may be the
+    neighbouring bf16 value where the fp32 product lies within 2^-16 of a
+    rounding midpoint: there either value is accepted."""
     N, K, bs = 300, 1024, 64
-    p = synth.q4_problem(1, N, K, bs, config=63)
+    cb = {"int4": q4.q4_codebook_preset("int4"), "random16": codebook_16bit(63),
+          "nf4style": synth.nf4_style_codebook()}[cbname]
+    p = synth.q4_problem(1, N, K, bs, config=63, codebook=cb)
     js = [0, 1, 7, 31, 32, 63, 64, 100, 127, 128, 255, 256, 511, 512, 700, 767,
           768, 800, 900, 1000, 1010, 1015, 1020, 1021, 1022, 1023, 2, 3, 4, 5, 6, 8]
     A = np.zeros((len(js), K), np.uint16)
     for m, j in enumerate(js):
         A[m, j] = 0x3F80
-    _, Wp, am, cb = q4_to_dev(p)
-    C = q4.q4_gemm_skinny(to_dev(A, "bf16"), Wp, am, cb, bs, path="fused")
+    _, Wp, am, cbd = q4_to_dev(p)
+    C = bf16_host(q4.q4_gemm_skinny(to_dev(A, "bf16"), Wp, am, cbd, bs, path="fused"))
     _sync()
-    w16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)
-    assert np.array_equal(bf16_host(C), w16[:, js].T)
+    w16 = oracle.dequant_bf16(p["Wpacked"], p["absmax"], p["codebook"], N, K, bs)[:, js].T
+    if cbname != "nf4style":
+        assert np.array_equal(C, w16)
+        return
+    codes = oracle.unpack(p["Wpacked"], N, K)[:, js].T
+    scales = p["absmax"].reshape(N, K // bs)[:, np.array(js) // bs].T
+    alt = hilo_products(p["codebook"])(codes, scales)
+    same = w16 == alt
+    assert np.array_equal(C[same], w16[same])
+    assert np.all((C[~same] == w16[~same]) | (C[~same] == alt[~same]))
 
 
 @pytest.mark.parametrize("M", [24, 32])

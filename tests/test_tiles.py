@@ -211,6 +211,15 @@ def test_gpu_dequant_tiles_bit_exact(bs, dt):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M", [1, 8, 64])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 64])
 def test_gpu_gemm_tiles_ffn_full_size_equal_rows(M):
-    _tiles_case(M, 28672, 8192, 64, config=2)
+    """The 28672 x 8192 FFN over tiles, in the instantiations the benchmark
+    times (M = 1, 2, 4, 8): equal to the row-major call bit for bit, and
+    within tolerance of the oracle on sampled columns."""
+    tol, bf16_host = _gpu()[:2]
+    p, C = _tiles_case(M, 28672, 8192, 64, config=2)
+    from gpu_util import sample_cols
+    cols = sample_cols(28672, 96, 31 * M)
+    Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, 28672, 8192, 64,
+                           cols=cols)
+    tol(bf16_host(C)[:, cols], Cr, S, "FFN tiles M=%d" % M)
