@@ -83,7 +83,7 @@ constexpr int KW = 8;  // waves per workgroup
 // every unit compile-time constants.  P: slots per scale-staging period (a
 // divisor of UF).  MB: blocks of 16 token rows per pass (1, or 2 for up to 32
 // tokens): the decoded weights of a unit feed the MFMAs of every block.
-template <int SR, int TB, int RS, int UF, int P, int MB>
+template <int SR, int TB, int RS, int UF, int P, int MB, bool BS64>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
@@ -162,12 +162,14 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     int ic = 0, iq = 0;
     uint32_t w_row0 = group_of(0) * 16 * row_bytes + w_lane;
     bool w_live = true;
+    int iqr = rot;  // (iq + rot) % spw, kept incrementally (no division per slot)
     auto w_seek = [&]() {
-        const int seg = wave + ((iq + rot) % spw) * KW;
+        const int seg = wave + iqr * KW;
         w_live = ic < my_chunks && seg < nseg;
         w_row0 = group_of(ic) * 16 * row_bytes + ((uint32_t)seg << seg_sh) + w_lane;
     };
     auto w_advance = [&]() {
+        if (++iqr == spw) iqr = 0;
         if (++iq == spw) {
             iq = 0;
             ++ic;
@@ -192,6 +194,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint32_t s_piece = (uint32_t)(tid % (4 * P)) * 16;
     const uint32_t s_win = (uint32_t)(P * KW * 128 * 4) >> bs_log2;  // bytes per row per period
     int sc = 0, sq = 0;  // scale cursor: the first slot of the period loaded next
+    int sqr = rot;       // (sq + rot) % spw
     // Bytes of this thread's piece that lie inside the row (a piece may run
     // past the row's last block when K / bs is not a multiple of 4: those
     // scales belong to the next row and are zeroed at staging, so that a
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // into NaN).
     int s_rem = 16;
     auto load_scales = [&](floatx4 (&out)[SP]) {
-        const uint32_t w0 = ((uint32_t)((sq + rot) % spw) * KW * 128 >> bs_log2) * 4;  // window start
+        const uint32_t w0 = ((uint32_t)sqr * KW * 128 >> bs_log2) * 4;  // window start
         const bool live = sc < my_chunks && s_piece < s_win && w0 + s_piece < nb * 4;
         s_rem = (int)(nb * 4) - (int)(w0 + s_piece);
 #pragma unroll
@@ -211,8 +214,11 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             out[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sres, (int)so, 0, 0));
         }
         sq += P;
+        sqr += P;
+        if (sqr >= spw) sqr -= spw;
         if (sq >= spw) {
             sq = 0;
+            sqr = rot;
             ++sc;
         }
     };
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // e = 16u + 2w and e + 1 of the period window, which lie in bs-wide blocks
     // e >> sh and (e + 1) >> sh: one 8-byte read at the even block below, then
     // a select (both halves for bs = 64, one half twice for bs = 128 and 256).
-    const int sh = bs_log2 - 6;
+    const int sh = BS64 ? 0 : bs_log2 - 6;
     auto read_scales = [&](const float *p) { return *reinterpret_cast<const floatx2 *>(p); };
     auto pick_scales = [&](const floatx2 &a2, int pick, float (&out)[2]) {
         out[0] = pick == 1 ? a2[1] : a2[0];
@@ -247,8 +253,8 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // memory, which cancels whatever codes sit there.
     const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;  // past the end of A for j >= M
     uint4 anext[MB][4];
-    auto load_a = [&](int q) {
-        const uint32_t kk = ((uint32_t)wave + (uint32_t)((q + rot) % spw) * KW) * 128;
+    auto load_a = [&](int qr) {  // qr: the slot's index along the row, (q + rot) % spw
+        const uint32_t kk = ((uint32_t)wave + (uint32_t)qr * KW) * 128;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t k = kk + swapped_k_offset(g, t);
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     {
         floatx4 s0[SP];
         load_scales(s0);
-        load_a(0);
+        load_a(rot);
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
 #pragma unroll
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         for (int b = 0; b < MB; ++b)
 #pragma unroll
             for (int r = 0; r < SR; ++r) acc[tr][b][r] = 0.f;
-    int pq = 0;   // the slot being computed
+    int pqr = rot;  // the slot being computed, as its index along the row
     int qp = 0;   // periods done, for the staging buffer parity
     floatx4 snext[SP];  // the next period's scale pieces
 
@@ -367,10 +373,10 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             for (int s = 0; s < 8; ++s)
                 __asm__ volatile("" : "+v"(adup[b][s].x), "+v"(adup[b][s].y), "+v"(adup[b][s].z),
                                  "+v"(adup[b][s].w));
-        load_a(pq + 1 == spw ? 0 : pq + 1);  // the activations of the next slot
+        load_a(pqr + 1 == spw ? 0 : pqr + 1);  // the activations of the next slot
         if constexpr (us % P == 0) load_scales(snext);  // and the next period's scales
         const int s_blk = (16 * (us % P) + 2 * wave) >> sh;
-        const int s_pick = sh == 0 ? -1 : (s_blk & 1);
+        const int s_pick = BS64 || sh == 0 ? -1 : (s_blk & 1);
         auto picked = [&](const floatx2 &a2) {
             float o[2];
             pick_scales(a2, s_pick, o);
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             lds_barrier();
             ++qp;
         }
-        if (++pq == spw) pq = 0;
+        if (++pqr == spw) pqr = 0;
     };
 
     // Chunk end: combine the KW partials of the chunk's tiles.  Output (tile,
@@ -548,8 +554,12 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // loop iterations.
     const int spw = ((K + 127) / 128 + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
-    fused_mfma_kernel<SR, TB, RS, UF, P, MB><<<dim3(G), dim3(64 * KW), 0, s>>>(
-        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, wl, C, c_dt);
+    if (bs_log2 == 6)
+        fused_mfma_kernel<SR, TB, RS, UF, P, MB, true><<<dim3(G), dim3(64 * KW), 0, s>>>(
+            A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, wl, C, c_dt);
+    else
+        fused_mfma_kernel<SR, TB, RS, UF, P, MB, false><<<dim3(G), dim3(64 * KW), 0, s>>>(
+            A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, wl, C, c_dt);
     return hipGetLastError();
 }
 
