@@ -29,6 +29,7 @@ Q4_DTYPE_BF16, Q4_DTYPE_FP32, Q4_DTYPE_FP16 = 0, 1, 2
 PATHS = {"auto": 0, "fused": 1, "split": 2}
 FUSED_PASS_M = 32
 CROSSOVER_MAX = 65536
+Q4_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/q4skinny.h declares.
 EXPORTS = (
@@ -37,6 +38,7 @@ EXPORTS = (
     "q4_copy_probe", "q4_version", "q4_quantize", "q4_codebook_preset",
     "q4_set_crossover_shape", "q4_get_crossover_shape", "q4_clear_crossover_shapes",
     "q4_repack_tiles", "q4_gemm_skinny_tiles", "q4_dequant_tiles", "q4_read_probe",
+    "q4_gemm_skinny_ex_noalloc",
 )
 PRESETS = {"nf4_style": 0, "int4": 1}
 
@@ -69,6 +71,7 @@ def lib():
         L.bf16_gemm_skinny.argtypes = [P, P, P, I, I, I, P, P]
         L.q4_dequant.argtypes = [P, P, P, I, I, I, P, I, P]
         L.q4_gemm_skinny_tiles.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
+        L.q4_gemm_skinny_ex_noalloc.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
         L.q4_dequant_tiles.argtypes = [P, P, P, I, I, I, P, I, P]
         L.q4_repack_tiles.argtypes = [P, P, I, I, P]
         L.q4_copy_probe.argtypes = [P, P, ctypes.c_size_t, P]
@@ -80,6 +83,8 @@ def lib():
         L.q4_get_crossover_shape.argtypes = [I, I]
         L.q4_get_crossover_shape.restype = ctypes.c_int
         for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
+                     "q4_gemm_skinny_ex_noalloc", "q4_gemm_skinny_tiles", "q4_dequant_tiles",
+                     "q4_repack_tiles",
                      "bf16_gemm_skinny", "q4_dequant",
                      "q4_copy_probe", "q4_read_probe", "q4_set_crossover_m",
                      "q4_release_workspace",

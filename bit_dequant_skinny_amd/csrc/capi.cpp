@@ -181,7 +181,22 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+// A call made through q4_gemm_skinny_ex_noalloc brings its own scratch (the
+// device's fixed array) for the duration of the call on this thread; every
+// workspace request of that call is served from it or refused.
+thread_local void *tl_fixed_scratch = nullptr;
+thread_local size_t tl_fixed_bytes = 0;
+
 q4_status workspace(int device, hipStream_t s, size_t bytes, void **out) {
+    if (tl_fixed_scratch) {
+        if (bytes > tl_fixed_bytes)
+            return fail(Q4_ERR_UNSUPPORTED,
+                        "this call needs %zu bytes of scratch, above the %zu bytes of the "
+                        "allocation-free entry point",
+                        bytes, tl_fixed_bytes);
+        *out = tl_fixed_scratch;
+        return Q4_OK;
+    }
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[{device, s}];
     if (w.bytes < bytes) {
@@ -537,6 +552,24 @@ q4_status dequant_impl(const uint8_t *Wpacked, int wl, const float *absmax,
 }  // namespace
 
 namespace q4 {
+
+q4_status report(q4_status st, const char *what, hipError_t e) {
+    (void)hipGetLastError();
+    return fail(st, "%s: %s", what, hipGetErrorString(e));
+}
+
+q4_status gemm_ex_fixed_scratch(const void *A, int a_dtype, const uint8_t *Wpacked,
+                                const float *absmax, const float *codebook, const void *bias,
+                                int M, int N, int K, int blocksize, void *C, int c_dtype,
+                                void *stream, int path, void *scratch, size_t scratch_bytes) {
+    tl_fixed_scratch = scratch;
+    tl_fixed_bytes = scratch_bytes;
+    const q4_status st = gemm_impl(A, a_dtype, Wpacked, 0, absmax, codebook, bias, M, N, K,
+                                   blocksize, C, c_dtype, stream, path);
+    tl_fixed_scratch = nullptr;
+    tl_fixed_bytes = 0;
+    return st;
+}
 
 DeviceInfo device_info() {
     static std::atomic<int> cus[256];  // 0 = not yet queried

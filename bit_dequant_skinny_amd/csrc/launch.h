@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "q4skinny.h"
+
 namespace q4 {
 
 struct DeviceInfo {
@@ -91,6 +93,18 @@ hipError_t launch_quantize(const void *W, int w_dt, int N, int K, int bs_log2,
                            hipStream_t s);
 
 hipError_t launch_copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+// q4_gemm_skinny_ex with every workspace request served from `scratch`
+// (scratch_bytes long) instead of the per-stream workspace: a request that
+// does not fit returns Q4_ERR_UNSUPPORTED before anything is launched.
+// Defined in capi.cpp.
+q4_status gemm_ex_fixed_scratch(const void *A, int a_dtype, const uint8_t *Wpacked,
+                                const float *absmax, const float *codebook, const void *bias,
+                                int M, int N, int K, int blocksize, void *C, int c_dtype,
+                                void *stream, int path, void *scratch, size_t scratch_bytes);
+// Drains the HIP error flag and records "what: <HIP message>" for
+// q4_last_error; returns st.  Defined in capi.cpp.
+q4_status report(q4_status st, const char *what, hipError_t e);
 // Read-only stream over `bytes` (< 4 GiB) by num_cus * wgs_per_cu workgroups
 // of `threads` (256, 512, 1024) lanes, `unroll` (2, 4, 8) 16-byte loads per
 // lane per batch; nt = non-temporal loads, interleave = batches dealt round

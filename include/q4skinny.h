@@ -146,6 +146,33 @@ q4_status q4_gemm_skinny_ex(const void *A, int a_dtype, const uint8_t *Wpacked,
                             int path);
 
 /*
+ * q4_gemm_skinny_ex_noalloc: q4_gemm_skinny_ex that allocates nothing.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments,
+ * results (bit for bit), dispatch and errors are those of q4_gemm_skinny_ex,
+ * except that the scratch some paths need (the bf16 weights of the split
+ * path, the activation planes of fp16 / fp32 inputs, the fp32 partial
+ * outputs of K splits) comes from a fixed device array of
+ * Q4_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends, instead of the per-stream workspace.
+ *  - A call whose path needs more scratch than that returns
+ *    Q4_ERR_UNSUPPORTED (nothing launched); q4_gemm_skinny_ex has no limit.
+ *  - No hipMalloc / hipFree / allocating library call is made, so the call
+ *    can be captured into a HIP graph from its first use.
+ *  - Every call on a device shares that device's array: calls that overlap
+ *    on one device (different streams or threads) race; serialise them.
+ *    Each call writes the scratch it reads, so nothing carries over.
+ *  - The array's device address is looked up once per device, at the
+ *    device's first call (Q4_ERR_HIP if that lookup fails).
+ */
+#define Q4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+q4_status q4_gemm_skinny_ex_noalloc(const void *A, int a_dtype, const uint8_t *Wpacked,
+                                    const float *absmax, const float *codebook, const void *bias,
+                                    int M, int N, int K, int blocksize, void *C, int c_dtype,
+                                    void *stream, int path);
+
+/*
  * The tile layout of the packed weights.
  *
  * The same bytes as the row-major Wpacked [N, K/2], reordered so that the
