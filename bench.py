@@ -109,7 +109,12 @@ class Dev:
 
     def _time_graph(self, f, reps):
         t = self.t
-        side = t.cuda.Stream()
+        # one capture stream for the whole run: the library keeps one
+        # workspace per stream, so a fresh stream per timing would hold a new
+        # buffer (up to N*K*2 bytes for the split path) each time
+        if not hasattr(self, "side"):
+            self.side = t.cuda.Stream()
+        side = self.side
         # warm up on the capture stream: the library keeps its scratch per
         # stream and must not allocate while the stream is captured
         with t.cuda.stream(side):
@@ -168,16 +173,23 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(p, M_list, target_s=12.0):
-    """The oracle as it stands, on a bounded sample of the workload: a random
-    subset of output columns, grown until one pass takes a quarter of the
-    target time; once the whole output fits, whole passes are repeated until
-    the target time is reached."""
-    import oracle
-    orc = oracle.default()
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_rate(orc, p, M_list, target_s):
+    """Algorithmic GB/s of the oracle on a random subset of output columns,
+    grown until one pass takes a quarter of the target time; once the whole
+    output fits, whole passes are repeated until the target time is reached."""
     N, K = p["N"], p["K"]
     g = synth.rng(123)
-    ncols = 64
+    ncols = 16
     while True:
         cols = np.sort(g.choice(N, size=ncols, replace=False))
         t0 = time.perf_counter()
@@ -195,15 +207,53 @@ def cpu_baseline(p, M_list, target_s=12.0):
         t_used += time.perf_counter() - t0
         passes += 1
     total_bytes = passes * sum(q4_bytes(M, N, K) * ncols / N for M in M_list)
+    return total_bytes / t_used / 1e9, "%d pass(es) over %d of %d output columns, %.1f s" % (
+        passes, ncols, N, t_used)
+
+
+def cpu_baseline(p, M_list, target_s=10.0):
+    """The oracle as it stands, on a bounded sample of the workload, on all
+    host cores (the reported value) and on one core."""
+    import oracle
+    orc = oracle.default()
+    cores = os.cpu_count() or 1
+    affinity = getattr(os, "sched_getaffinity", None)
+    if affinity is not None:
+        cores = len(affinity(0))
+    orc.set_threads(cores)
+    used = orc.max_threads()
+    rate_all, sample_all = _oracle_rate(orc, p, M_list, target_s)
+    orc.set_threads(1)
+    rate_one, sample_one = _oracle_rate(orc, p, M_list, target_s / 2)
+    orc.set_threads(used)
     return {
-        "value": total_bytes / t_used / 1e9,
+        "value": rate_all,
         "unit": "GB/s",
-        "cores": orc.max_threads(),
+        "cores": used,
         "kind": "oracle",
-        "sample": "%d pass(es) over %d of %d output columns at M=%s, K=%d (algorithmic bytes "
-                  "scaled by the column fraction), %.1f s" % (
-                      passes, ncols, N, "/".join(map(str, M_list)), K, t_used),
+        "sample": "fused GEMM M=%s, K=%d, N=%d: %s (algorithmic bytes scaled by the column "
+                  "fraction)" % ("/".join(map(str, M_list)), p["K"], p["N"], sample_all),
+        "single_thread": {"value": rate_one, "unit": "GB/s", "cores": 1, "sample": sample_one},
+        "cpu_model": cpu_model(),
     }
+
+
+def read_ceiling(d, nbytes, R):
+    """Achievable HBM read rate of one launch over nbytes: q4_read_probe (a
+    read-only 128-bit stream, default launch shape) over R rotating buffers,
+    timed like the per-M kernels."""
+    import bit_dequant_skinny_amd as q4
+    t = d.t
+    nbytes = nbytes // 16 * 16
+    bufs = [t.empty(nbytes, dtype=t.uint8, device=d.dev) for _ in range(R)]
+    for b in bufs:
+        b.fill_(0x5a)
+    sink = t.zeros(4, dtype=t.int32, device=d.dev)
+    us = d.time_launches([lambda i: q4.q4_read_probe(bufs[i % R], sink)], reps=12 * R)[0]
+    del bufs
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bytes": nbytes, "buffers": R, "us": round(us, 2), "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_GBS, 4)}
 
 
 def headline(d, args):
@@ -304,8 +354,11 @@ def headline(d, args):
     m1_us = per_m_us[1]
     ach = q4_bytes(1, N, K) / (m1_us * 1e-6) / 1e9
     traffic = traffic_from_profile()
+    ceiling = read_ceiling(d, q4_bytes(1, N, K), R)
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_GBS, 4),
+            "achievable_read": ceiling,
+            "frac_of_achievable_read": round(ach / ceiling["GB/s"], 4),
             "traffic": None if traffic is None else round(traffic / (m1_us * 1e-6) / 1e9, 1),
             "traffic_bytes_per_launch": traffic,
             "kernel": "fused q4 M=1, K=8192, N=28672, %s layout" % args.layout,
@@ -340,20 +393,81 @@ def headline(d, args):
     return out, p, M_list
 
 
+SWEEP_SHAPES = [  # (K, N, workload index, shape index)
+    (5120, 8192, 2, 0), (5120, 5120, 2, 1), (17408, 5120, 2, 2), (8192, 8192, 2, 3),
+    (8192, 28672, 1, 0), (2560, 248320, 4, 0)]
+SWEEP_M = list(range(1, 17)) + [32, 64, 96, 128, 192, 256, 384, 512]
+
+
+def crossover_sweep(d, weights):
+    """Fused against split (dequantize to bf16 + GEMM) at every M = 1..16 and
+    at 32..512 on each shape, weights in the tile layout, rotating copies: the
+    measured crossover (the last M up to which the fused path wins) beside the
+    library's routing for the shape."""
+    import bit_dequant_skinny_amd as q4
+    t = d.t
+    out = {}
+    for K, N, config, shape in SWEEP_SHAPES:
+        sets, cb = weights(N, K, config, shape)
+        R = len(sets)
+        rows = {}
+        last_fused_win = 0
+        for M in SWEEP_M:
+            A = d.bf16(synth.activations_bf16(M, K, synth.seed(config, shape, 10 * M + 1)))
+            C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+            fns = []
+            for path in ("fused", "split"):
+                def f(i, path=path):
+                    Wp, am = sets[i % R]
+                    q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path=path, layout="tiles")
+                fns.append(f)
+            uf, us = d.time_launches(fns, reps=max(4, min(24, 2 * R)), warmup=2)
+            rows[str(M)] = {"fused_us": round(uf, 2), "split_us": round(us, 2),
+                            "fused_GB/s": round(q4_bytes(M, N, K) / (uf * 1e-6) / 1e9, 1)}
+            if uf <= us:
+                last_fused_win = M
+        first_split = next((M for M in SWEEP_M if rows[str(M)]["split_us"] < rows[str(M)]["fused_us"]),
+                           None)
+        out["K=%d N=%d" % (K, N)] = {
+            "us": rows,
+            "first M where split beats fused": first_split,
+            "last M where fused wins": last_fused_win,
+            "library: fused when M <=": q4.q4_get_crossover_shape(N, K),
+        }
+        log("  K=%d N=%d: split first wins at M=%s (library %d)" % (
+            K, N, first_split, q4.q4_get_crossover_shape(N, K)))
+    return out
+
+
 def other_configs(d):
     """Kernel times of the other decode workloads (HIP events, rotated weights)."""
     import bit_dequant_skinny_amd as q4
     t = d.t
     res = {}
 
+    cache = {}
+
+    def q4_weights(N, K, config, shape):
+        """Seeded packed weights (row-major and tile layout) rotated over
+        >= 1 GiB; one shape is kept at a time."""
+        key = (N, K, config, shape)
+        if key not in cache:
+            cache.clear()
+            p = synth.q4_problem(1, N, K, BS, config=config, shape=shape)
+            sets = d.copies((d.raw(p["Wpacked"]), d.raw(p["absmax"])), q4_bytes(1, N, K))
+            cache[key] = {"rows": sets, "tiles": [(q4.q4_repack_tiles(Wp), am) for Wp, am in sets],
+                          "cb": d.raw(p["codebook"])}
+        return cache[key]
+
+    def q4_cfg_weights(N, K, config, shape):
+        w = q4_weights(N, K, config, shape)
+        return w["tiles"], w["cb"]
+
     def q4_cfg(name, M_list, N, K, config, shape, paths=("auto",), layouts=("rows",)):
-        p = synth.q4_problem(1, N, K, BS, config=config, shape=shape)
-        sets = d.copies((d.raw(p["Wpacked"]), d.raw(p["absmax"])), q4_bytes(1, N, K))
-        by_layout = {"rows": sets}
-        if "tiles" in layouts:
-            by_layout["tiles"] = [(q4.q4_repack_tiles(Wp), am) for Wp, am in sets]
+        w = q4_weights(N, K, config, shape)
+        R = len(w["rows"])
         cases = [(path, lay) for lay in layouts for path in paths]
-        cb = d.raw(p["codebook"])
+        cb = w["cb"]
         rows = {}
         for M in M_list:
             A = d.bf16(synth.activations_bf16(M, K, synth.seed(config, shape, 10 * M + 1)))
@@ -361,10 +475,10 @@ def other_configs(d):
             fns = []
             for path, lay in cases:
                 def f(i, path=path, lay=lay):
-                    Wp, am = by_layout[lay][i % len(sets)]
+                    Wp, am = w[lay][i % R]
                     q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path=path, layout=lay)
                 fns.append(f)
-            us = d.time_launches(fns, reps=max(60, min(200, len(sets) * 2)))
+            us = d.time_launches(fns, reps=max(60, min(200, R * 2)))
             for (path, lay), u in zip(cases, us):
                 gbs = q4_bytes(M, N, K) / (u * 1e-6) / 1e9
                 key = "M=%d %s" % (M, path) + ("" if lay == "rows" else " tiles")
@@ -375,30 +489,11 @@ def other_configs(d):
 
     log("C1 GEMV 4096x4096")
     q4_cfg("q4 M=1 K=4096 N=4096", [1], 4096, 4096, 0, 0, layouts=("rows", "tiles"))
-    log("C3 decode layers")
-    cross = {}
-    for shape, (K, N) in enumerate([(5120, 8192), (5120, 5120), (17408, 5120), (8192, 8192)]):
-        rows = q4_cfg("q4 K=%d N=%d" % (K, N), [1, 4, 8, 16], N, K, 2, shape,
-                      paths=("fused", "split"), layouts=("rows", "tiles"))
-        mstar = None
-        for M in [1, 4, 8, 16]:
-            if rows["M=%d split" % M]["us"] < rows["M=%d fused" % M]["us"]:
-                mstar = M
-                break
-        cross["K=%d N=%d" % (K, N)] = mstar
-    res["crossover (first M of 1,4,8,16 where split beats fused)"] = cross
-    log("fused vs split at 32..256 token rows")
-    big = {}
-    for shape, (K, N) in enumerate([(5120, 8192), (5120, 5120), (17408, 5120), (8192, 8192),
-                                    (8192, 28672)]):
-        Ms = [32, 64, 128, 256]
-        rows = q4_cfg("q4 K=%d N=%d M=32..256" % (K, N), Ms, N, K, 2, shape,
-                      paths=("fused", "split"))
-        first = next((M for M in Ms if rows["M=%d split" % M]["us"] < rows["M=%d fused" % M]["us"]),
-                     None)
-        big["K=%d N=%d" % (K, N)] = {"first M of 32..256 where split beats fused": first,
-                                     "library: fused when M <=": q4.q4_get_crossover_shape(N, K)}
-    res["crossover at 32..256 rows"] = big
+    log("fused vs split sweep (crossover): decode layers, FFN, output projection")
+    res["crossover sweep"] = crossover_sweep(d, q4_cfg_weights)
+    log("C5 large-vocabulary projection, 4-bit (weights of the sweep's last shape)")
+    q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0, layouts=("rows", "tiles"))
+    cache.clear()
     log("C4 bf16 skinny")
     for shape, N in enumerate([96, 2048, 16384, 31040]):
         K = 2560
@@ -455,8 +550,7 @@ def other_configs(d):
                               "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
         del Wq, outs
     res["q4_quantize N=28672 K=8192 bs=64"] = rows
-    log("C5 large-vocabulary projection")
-    q4_cfg("q4 K=2560 N=248320", [1, 8], 248320, 2560, 4, 0, layouts=("rows", "tiles"))
+    log("C5 large-vocabulary projection, bf16")
     K, N = 2560, 248320
     W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
     rows = {}
@@ -470,6 +564,7 @@ def other_configs(d):
     res["bf16 K=2560 N=248320"] = rows
     del W
     res["copy probe 1 GiB (read+write)"] = copy_probe(d)
+    res["read probe 1 GiB"] = read_ceiling(d, 1 << 30, 1)
     return res
 
 

@@ -158,11 +158,34 @@ void load_shape_table_locked() {
     }
 }
 
+// Shapes without an entry of their own take the entry of a shape in the same
+// bucket, the convention of the bitsandbytes pull request "Cache the
+// hipBLASLt int8 matmul algo per problem on ROCm" (an exact key first, then a
+// bucket key).  A bucket groups shapes on which the fused kernel runs the
+// same schedule and the split path does about as much work per weight: the
+// same K rounded up to a power of two, and the same class of 16-row tiles per
+// compute unit (1, 2, 3-4 or 5 and more; the skinny kernel's ring and scale
+// period change at those points).  Several entries in one bucket: the
+// smallest crossover, which prefers a missed win to a regression.
+int bucket_of(int N, int K) {
+    int kb = 0;
+    while (kb < 31 && (1 << kb) < K) ++kb;
+    const int tb = q4::q4_fused_tiles_per_chunk(N);
+    const int tc = tb <= 1 ? 0 : tb == 2 ? 1 : tb <= 4 ? 2 : 3;
+    return kb * 4 + tc;
+}
+
 int crossover_for(int N, int K) {
     std::lock_guard<std::mutex> lock(g_shape_mutex);
     load_shape_table_locked();
     const auto it = g_shape_crossover.find({N, K});
-    return it != g_shape_crossover.end() ? it->second : crossover();
+    if (it != g_shape_crossover.end()) return it->second;
+    const int b = bucket_of(N, K);
+    int best = -1;
+    for (const auto &kv : g_shape_crossover)
+        if (bucket_of(kv.first.first, kv.first.second) == b && (best < 0 || kv.second < best))
+            best = kv.second;
+    return best >= 0 ? best : crossover();
 }
 
 // ---- workspace: one buffer per (device, stream) -------------------------------

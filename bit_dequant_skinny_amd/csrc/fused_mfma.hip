@@ -602,6 +602,8 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
 // registers for the second (then 17..32 rows run as two 16-row launches).
 bool q4_fused_mfma_two_blocks(int N) { return tiles_per_chunk(N) < 8; }
 
+int q4_fused_tiles_per_chunk(int N) { return tiles_per_chunk(N); }
+
 bool q4_fused_mfma_fits(int M, int N, int K) {
     (void)M;
     return ((uint64_t)N + 256) * (uint64_t)K / 2 < (1ull << 32) &&

@@ -49,6 +49,8 @@ hipError_t launch_split_planes(const void *A, int a_dt, size_t n, uint16_t *plan
 hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *bias, void *C,
                              int c_dt, hipStream_t s);
 bool q4_fused_mfma_fits(int M, int N, int K);
+// 16-row tiles each workgroup of the skinny kernel covers per chunk (1..8).
+int q4_fused_tiles_per_chunk(int N);
 bool q4_fused_mfma_two_blocks(int N);
 
 // Fused 4-bit GEMM with output tiles of 64 (32 for M <= 32) tokens (bf16 A,

@@ -351,7 +351,13 @@ q4_status q4_set_crossover_m(int m);
  *                           removes it; Q4_ERR_INVALID_ARGUMENT for N <= 0,
  *                           K <= 0 or m > Q4_CROSSOVER_MAX.
  *  q4_get_crossover_shape   the crossover calls of shape (N, K) use: the
- *                           entry if present, else q4_get_crossover_m().
+ *                           entry if present; else the smallest entry of
+ *                           the shapes in the same bucket (K rounded up to
+ *                           a power of two, and 16-row tiles per compute
+ *                           unit in the class 1, 2, 3-4 or 5+), the exact-
+ *                           then-bucket lookup of the bitsandbytes pull
+ *                           request "Cache the hipBLASLt int8 matmul algo per
+ *                           problem on ROCm"; else q4_get_crossover_m().
  *  q4_clear_crossover_shapes removes every entry, the measured ones
  *                           included (neither they nor the environment's
  *                           table are read again).

@@ -97,11 +97,16 @@ class Oracle:
                                           P, I, P, P]
         lib.oracle_quantize.argtypes = [P, ctypes.c_int, P, I, I, I, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_tile_offset.argtypes = [I, I, I, I]
         lib.oracle_tile_offset.restype = I
         lib.oracle_repack_tiles.argtypes = [P, I, I, P]
         self.lib = lib
         self.path = lib_path
+
+    def set_threads(self, n: int) -> None:
+        """Threads the OpenMP loops use from now on (n >= 1)."""
+        self.lib.oracle_set_threads(int(n))
 
     def max_threads(self) -> int:
         """Threads the OpenMP loops use (OMP_NUM_THREADS)."""

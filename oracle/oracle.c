@@ -418,6 +418,18 @@ void oracle_repack_tiles(const uint8_t *Wpacked, int64_t N, int64_t K, uint8_t *
             out[oracle_tile_offset(N, K, n, j)] = Wpacked[n * (K / 2) + j];
 }
 
+/* Thread count of the OpenMP loops from here on (the benchmark's CPU baseline
+ * times the oracle single-threaded and on all cores); n < 1 leaves it as is. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

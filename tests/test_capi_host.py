@@ -152,7 +152,7 @@ def test_crossover_shape_table():
         q4.q4_set_crossover_shape(5120, 8192, 0)
         assert q4.q4_get_crossover_shape(4096, 4096) == 8
         assert q4.q4_get_crossover_shape(5120, 8192) == 0
-        assert q4.q4_get_crossover_shape(8192, 5120) == base  # (N, K) is ordered
+        assert q4.q4_get_crossover_shape(8192, 4096) == base  # (N, K) is ordered
         q4.q4_set_crossover_m(3)
         assert q4.q4_get_crossover_shape(4096, 4096) == 8     # the entry wins
         assert q4.q4_get_crossover_shape(100, 100) == 3       # no entry: global
@@ -162,6 +162,26 @@ def test_crossover_shape_table():
         q4.q4_set_crossover_m(base)
         q4.q4_clear_crossover_shapes()
     assert q4.q4_get_crossover_shape(5120, 8192) == base
+
+
+def test_crossover_bucket_of_unmeasured_shapes():
+    """A shape without an entry takes the smallest entry of its bucket (K
+    rounded up to a power of two, tiles per compute unit in the classes 1, 2,
+    3-4, 5+; 256 compute units assumed without a GPU); exact entries win."""
+    base = q4.q4_get_crossover_m()
+    q4.q4_clear_crossover_shapes()
+    try:
+        q4.q4_set_crossover_shape(28672, 8192, 300)  # 7 tiles per CU, K bucket 8192
+        q4.q4_set_crossover_shape(24576, 8192, 280)  # 6 tiles per CU, same bucket
+        q4.q4_set_crossover_shape(5120, 5120, 90)    # 2 tiles per CU, K bucket 8192
+        assert q4.q4_get_crossover_shape(20480, 7000) == 280   # 5 tiles, K -> 8192
+        assert q4.q4_get_crossover_shape(28672, 8192) == 300   # exact entry
+        assert q4.q4_get_crossover_shape(8192, 6144) == 90     # 2 tiles, K -> 8192
+        assert q4.q4_get_crossover_shape(8192, 16384) == base  # K bucket 16384: none
+        assert q4.q4_get_crossover_shape(16384, 8192) == base  # 4 tiles: no entry
+        assert q4.q4_get_crossover_shape(100, 8192) == base    # 1 tile: no entry
+    finally:
+        q4.q4_clear_crossover_shapes()
 
 
 def test_crossover_shape_table_from_environment():

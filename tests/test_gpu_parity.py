@@ -276,11 +276,11 @@ def test_auto_path_follows_crossover():
 
 
 def test_auto_path_follows_per_shape_crossover():
-    """A per-shape entry routes that shape alone; other shapes keep the
-    process-wide crossover."""
+    """A per-shape entry routes that shape (and the shapes of its bucket);
+    shapes of other buckets keep the process-wide crossover."""
     M, bs = 8, 64
     pa = synth.q4_problem(M, 64, 512, bs, config=59, shape=0)
-    pb = synth.q4_problem(M, 48, 512, bs, config=59, shape=1)
+    pb = synth.q4_problem(M, 48, 1024, bs, config=59, shape=1)
     da, db = q4_to_dev(pa), q4_to_dev(pb)
     q4.q4_clear_crossover_shapes()
     try:
@@ -358,3 +358,24 @@ def test_copy_probe_copies():
     q4.q4_copy_probe(src, dst)
     _sync()
     assert t.equal(src, dst)
+
+
+def test_auto_path_follows_bucket_of_unmeasured_shape():
+    """A shape with no entry of its own routes by the entry of a shape in its
+    bucket (same K power-of-two bucket and tiles-per-CU class)."""
+    bs = 64
+    q4.q4_clear_crossover_shapes()
+    try:
+        q4.q4_set_crossover_shape(4096, 1024, 5)  # 1 tile per CU, K bucket 1024
+        assert q4.q4_get_crossover_shape(96, 1000 // 64 * 64) == 5
+        res = {}
+        for M in (5, 6):
+            p = synth.q4_problem(M, 96, 960, bs, config=60)
+            A, Wp, am, cb = q4_to_dev(p)
+            res[M] = [bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path=path))
+                      for path in ("auto", "fused", "split")]
+    finally:
+        q4.q4_clear_crossover_shapes()
+    _sync()
+    assert np.array_equal(res[5][0], res[5][1])  # M = 5 <= 5: fused
+    assert np.array_equal(res[6][0], res[6][2])  # M = 6 > 5: split
