@@ -579,6 +579,37 @@ def copy_probe(d, nbytes=1 << 30):
             "GB/s": round(2 * nbytes / (u * 1e-6) / 1e9, 1)}
 
 
+def profile_case(d, which, launches=12):
+    """A few launches of one call for counter and trace runs: the split path
+    (dequantize + bf16 GEMM) on the FFN at M = 16 and 256, or the bf16 skinny
+    GEMM on the 248320 x 2560 projection at M = 1; weights rotate as in the
+    timed runs."""
+    import bit_dequant_skinny_amd as q4
+    t = d.t
+    if which in ("split16", "split256"):
+        M = 16 if which == "split16" else 256
+        N, K = 28672, 8192
+        p = synth.q4_problem(1, N, K, BS, config=1, shape=0)
+        sets = d.copies((d.raw(p["Wpacked"]), d.raw(p["absmax"])), q4_bytes(1, N, K))
+        cb = d.raw(p["codebook"])
+        A = d.bf16(synth.activations_bf16(M, K, synth.seed(1, 0, 10 * M + 1)))
+        C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+        for i in range(launches):
+            Wp, am = sets[i % len(sets)]
+            q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path="split")
+    elif which == "bf16c5":
+        N, K, M = 248320, 2560, 1
+        W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
+        A = d.bf16(synth.activations_bf16(M, K, synth.seed(4, 1, 10 * M + 1)))
+        C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+        for _ in range(launches):
+            q4.bf16_gemm_skinny(A, W, None, out=C)
+    else:
+        raise ValueError(which)
+    t.cuda.synchronize()
+    print(json.dumps({"profile_case": which, "launches": launches}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -592,6 +623,8 @@ def main():
                     help="packed-weight layout of the timed step (q4_repack_tiles or row-major)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel (counter calibration)")
+    ap.add_argument("--profile-case", choices=("split16", "split256", "bf16c5"),
+                    help="only run a few launches of one call (for rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -601,6 +634,9 @@ def main():
     assert d.t.cuda.is_available(), "bench.py needs an MI355X"
     if args.copy_probe:
         print(json.dumps({"copy probe 1 GiB (read+write)": copy_probe(d)}), flush=True)
+        return
+    if args.profile_case:
+        profile_case(d, args.profile_case)
         return
     out, p, M_list = headline(d, args)
     log("headline: %.1f GB/s" % out["value"])

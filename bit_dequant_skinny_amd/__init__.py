@@ -265,7 +265,7 @@ PROBE_NONTEMPORAL, PROBE_INTERLEAVE = 1, 2
 
 
 def q4_read_probe(src, sink, threads: int = 0, unroll: int = 0, wgs_per_cu: int = 0,
-                  nontemporal: bool = True, interleave: bool = False):
+                  nontemporal: bool = True, interleave: bool = True):
     """Reads all of src (a contiguous GPU tensor) once; sink is a GPU tensor of
     at least 4 bytes (written only when the folded data hits a fixed value)."""
     torch = _torch()

@@ -39,20 +39,48 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *sources(),
-           "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the device feature flag; that warning is harmless.
     out = "\n".join(l for l in res.stdout.splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
-    if res.returncode != 0:
+    return res.returncode, out
+
+
+def build(verbose: bool = False, extra_flags=None, jobs: int = 0) -> str:
+    """Compiles every source to an object in parallel (one hipcc per file),
+    then links the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    srcs = sources()
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(objdir, os.path.basename(src) + "." + tag + ".o") for src in srcs]
+    cmds = [[hipcc, *compile_flags, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-c", src,
+             "-o", obj] for src, obj in zip(srcs, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    n = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)), 16)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        results = list(ex.map(_run, cmds))
+    failed = [(c, out) for c, (rc, out) in zip(cmds, results) if rc != 0]
+    if failed:
+        for c, out in failed:
+            sys.stderr.write(" ".join(c) + "\n" + out + "\n")
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+        raise RuntimeError("hipcc failed on %d source(s)" % len(failed))
+    tmp = LIB + ".tmp" + tag
+    rc, out = _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    for o in objs:
+        os.remove(o)
+    if rc != 0:
         sys.stderr.write(out + "\n")
-        raise RuntimeError("hipcc failed with status %d" % res.returncode)
+        raise RuntimeError("hipcc link failed with status %d" % rc)
     if out.strip() and verbose:
         print(out)
     os.replace(tmp, LIB)

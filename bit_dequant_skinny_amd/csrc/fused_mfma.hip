@@ -29,9 +29,11 @@
 // 16 bytes (32 codes) of its feature's row at byte 16*g of the segment, so a
 // feature row is read 64 contiguous bytes per segment and one load
 // instruction brings 1 KiB.  Groups 0,1 hold the segment's first 64-wide
-// block and groups 2,3 the second; one v_permlane32_swap exchanges half of
-// each lane's dwords with the lane 32 away so that every MFMA step draws from
-// a single 64-wide block, which keeps the absmax scaling exact per block.
+// block and groups 2,3 the second; half of each lane's dwords are exchanged
+// with the lane 32 away (over rows by one v_permlane32_swap pair, over tiles
+// by loading the two 8-byte halves in place) so that every MFMA step draws
+// from a single 64-wide block, which keeps the absmax scaling exact per
+// block.
 // Tokens feed the A operand (lane % 16 = token; lanes of tokens >= M are
 // computed and discarded).
 //
@@ -83,11 +85,11 @@ constexpr int KW = 8;  // waves per workgroup
 // every unit compile-time constants.  P: slots per scale-staging period (a
 // divisor of UF).  MB: blocks of 16 token rows per pass (1, or 2 for up to 32
 // tokens): the decoded weights of a unit feed the MFMAs of every block.
-template <int SR, int TB, int RS, int UF, int P, int MB, bool BS64>
+template <int SR, int TB, int RS, int UF, int P, int MB, bool BS64, int WL>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups, int wl,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups,
     void *__restrict__ C, int c_dt) {
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
     static_assert(64 * KW == 512, "two threads per table entry");
@@ -152,8 +154,21 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // the 16 rows x 64 bytes of (tile, segment) are one 1 KiB unit at
     // (tile*nseg + s) * 1024 that holds lane l's 16 bytes at 16*l.  A tile
     // spans 16*row_bytes bytes in both.
-    const uint32_t w_lane = wl ? 16u * (uint32_t)lane : (uint32_t)j * row_bytes + 16u * (uint32_t)g;
-    const int seg_sh = wl ? 10 : 6;
+    //
+    // Over tiles a lane loads its 16 bytes as two 8-byte halves already in the
+    // order the MFMA steps use (see swapped_k_offset): lanes 0-31 the first
+    // half of their own piece and the first half of the piece of the lane 32
+    // above, lanes 32-63 the second half of the piece of the lane 32 below and
+    // the second half of their own.  The halves are 512 bytes apart, so each
+    // load instruction still reads 512 contiguous bytes and no lane exchange
+    // follows (measured 2-4 % faster at M = 1..4).  Over rows the same halves
+    // would be 32-byte pieces of 16 rows per instruction, which the memory
+    // serves far worse (40 against 28 us at M = 1 on the FFN): there each lane
+    // loads its own 16 bytes and one v_permlane32_swap pair regroups them.
+    const uint32_t w_lane =
+        WL ? (lane < 32 ? 16u * (uint32_t)lane : 16u * (uint32_t)(lane - 32) + 8u)
+           : (uint32_t)j * row_bytes + 16u * (uint32_t)g;
+    const int seg_sh = WL ? 10 : 6;
 
     // Weight issue cursor: the (chunk, slot) whose loads are issued next.
     // Slots past this workgroup's last chunk and segments past the end of a
@@ -182,7 +197,13 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // at M = 1..8 (neutral over rows).
     auto issue = [&](uint4 &dst, int tr) {
         const uint32_t wo = w_live ? w_row0 + (uint32_t)tr * w_tile_step : kPastEnd;
-        dst = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 2));
+        if constexpr (WL == 1) {
+            const auto h0 = __builtin_amdgcn_raw_buffer_load_b64(wres, (int)wo, 0, 2);
+            const auto h1 = __builtin_amdgcn_raw_buffer_load_b64(wres, (int)(wo + 512u), 0, 2);
+            dst = make_uint4(h0[0], h0[1], h1[0], h1[1]);
+        } else {
+            dst = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 2));
+        }
     };
 
     // Scales are staged through LDS one period (P slots) ahead: per period
@@ -201,16 +222,27 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // non-finite scale there cannot turn the 0 * scale of the padded blocks
     // into NaN).
     int s_rem = 16;
-    auto load_scales = [&](floatx4 (&out)[SP]) {
-        const uint32_t w0 = ((uint32_t)sqr * KW * 128 >> bs_log2) * 4;  // window start
-        const bool live = sc < my_chunks && s_piece < s_win && w0 + s_piece < nb * 4;
-        s_rem = (int)(nb * 4) - (int)(w0 + s_piece);
+    // Byte offset of this thread's pieces in their rows' scales for the chunk
+    // being loaded (kPastEnd for the spare rows past the chunk's tiles); set
+    // once per chunk, so a period adds only its window start.
+    uint32_t s_rowoff[SP];
+    auto scale_rows = [&]() {
 #pragma unroll
         for (int i = 0; i < SP; ++i) {
             const int row = s_row + i * (128 / P);
             const uint32_t ns = (group_of(sc) + (uint32_t)(row >> 4) * (uint32_t)groups) * 16 +
                                 (uint32_t)(row & 15);
-            const uint32_t so = live && row < TB * 16 ? ns * nb * 4 + w0 + s_piece : kPastEnd;
+            s_rowoff[i] = row < TB * 16 && s_piece < s_win ? ns * nb * 4 + s_piece : kPastEnd;
+        }
+    };
+    scale_rows();
+    auto load_scales = [&](floatx4 (&out)[SP]) {
+        const uint32_t w0 = ((uint32_t)sqr * KW * 128 >> bs_log2) * 4;  // window start
+        const bool live = sc < my_chunks && w0 + s_piece < nb * 4;
+        s_rem = (int)(nb * 4) - (int)(w0 + s_piece);
+#pragma unroll
+        for (int i = 0; i < SP; ++i) {
+            const uint32_t so = live ? s_rowoff[i] + w0 : kPastEnd;
             out[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sres, (int)so, 0, 0));
         }
         sq += P;
@@ -220,6 +252,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             sq = 0;
             sqr = rot;
             ++sc;
+            scale_rows();
         }
     };
     // Writes the pieces into the staging buffer; every thread writes, so the
@@ -251,31 +284,45 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // and k >= K (a ragged last segment, or a slot past the last segment)
     // takes an offset past every buffer: both read zeros without touching
     // memory, which cancels whatever codes sit there.
-    const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;  // past the end of A for j >= M
+    //
+    // Lane (j, g) reads at k = kk + L + T(t) with L = 32 (g & 1) + 16 (g >> 1)
+    // its own part and T(t) = 8 (t & 1) + 64 (t >> 1) (swapped_k_offset), so
+    // one per-lane base per slot and immediate offsets 0, 16, 128, 144 give
+    // the four loads.  K is a multiple of 64 here: dwords 0, 1 (k < kk + 64)
+    // are live when kk + 64 <= K and dwords 2, 3 when kk + 128 <= K, the same
+    // for every lane.
+    const uint32_t a_lane = (uint32_t)j * (uint32_t)K * 2 +  // past the end of A for j >= M
+                            2u * (32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1));
     uint4 anext[MB][4];
     auto load_a = [&](int qr) {  // qr: the slot's index along the row, (q + rot) % spw
         const uint32_t kk = ((uint32_t)wave + (uint32_t)qr * KW) * 128;
+        const uint32_t base = a_lane + 2u * kk;
+        const uint32_t lo = kk + 64 <= (uint32_t)K ? base : kPastEnd;
+        const uint32_t hi = kk + 128 <= (uint32_t)K ? base : kPastEnd;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t k = kk + swapped_k_offset(g, t);
-#pragma unroll
-            for (int b = 0; b < MB; ++b) {
-                const uint32_t off = k < (uint32_t)K ? a_row + (uint32_t)(16 * b) * (uint32_t)K * 2 + k * 2
-                                                     : kPastEnd;
-                anext[b][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)off, 0, 0));
-            }
+        for (int b = 0; b < MB; ++b) {
+            const uint32_t bo = (uint32_t)(16 * b) * (uint32_t)K * 2;
+            anext[b][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)(lo + bo), 0, 0));
+            anext[b][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)(lo + bo + 16), 0, 0));
+            anext[b][2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)(hi + bo + 128), 0, 0));
+            anext[b][3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)(hi + bo + 144), 0, 0));
         }
     };
 
-    // Table lookups of one tile: 16 packed bytes -> 32 bf16 hi/lo pairs.
+    // Table lookups of one tile: 16 packed bytes -> 32 bf16 hi/lo pairs,
+    // with the codes of the segment's first 64-wide block in dwords 0, 1 and
+    // those of the second in dwords 2, 3 (as loaded over tiles; over rows
+    // after the exchange).
     auto swap_w = [&](const uint4 &wv, uint32_t (&x)[4]) {
         x[0] = wv.x; x[1] = wv.y; x[2] = wv.z; x[3] = wv.w;
-        // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
-        // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
-        const auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-        x[0] = s02[0]; x[2] = s02[1];
-        x[1] = s13[0]; x[3] = s13[1];
+        if constexpr (WL == 0) {
+            // lanes 0-31 keep dwords 0,1 and take dwords 0,1 of lane+32;
+            // lanes 32-63 take dwords 2,3 of lane-32 and keep dwords 2,3
+            const auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+            x[0] = s02[0]; x[2] = s02[1];
+            x[1] = s13[0]; x[3] = s13[1];
+        }
     };
     auto lookups = [&](const uint32_t (&x)[4], uint2 (&ev)[16], int i0, int i1) {
 #pragma unroll
@@ -554,12 +601,17 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // loop iterations.
     const int spw = ((K + 127) / 128 + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
-    if (bs_log2 == 6)
-        fused_mfma_kernel<SR, TB, RS, UF, P, MB, true><<<dim3(G), dim3(64 * KW), 0, s>>>(
-            A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, wl, C, c_dt);
-    else
-        fused_mfma_kernel<SR, TB, RS, UF, P, MB, false><<<dim3(G), dim3(64 * KW), 0, s>>>(
-            A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, wl, C, c_dt);
+#define Q4_LAUNCH_KERNEL(B, L)                                                          \
+    fused_mfma_kernel<SR, TB, RS, UF, P, MB, B, L><<<dim3(G), dim3(64 * KW), 0, s>>>( \
+        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt)
+    if (bs_log2 == 6) {
+        if (wl) Q4_LAUNCH_KERNEL(true, 1);
+        else Q4_LAUNCH_KERNEL(true, 0);
+    } else {
+        if (wl) Q4_LAUNCH_KERNEL(false, 1);
+        else Q4_LAUNCH_KERNEL(false, 0);
+    }
+#undef Q4_LAUNCH_KERNEL
     return hipGetLastError();
 }
 

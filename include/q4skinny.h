@@ -428,9 +428,12 @@ q4_status q4_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
  *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, misalignment, a launch shape or
  *    flag outside the sets above.  Q4_ERR_UNSUPPORTED: bytes >= 4 GiB.
  */
-#define Q4_READ_PROBE_THREADS 512
-#define Q4_READ_PROBE_UNROLL 8
-#define Q4_READ_PROBE_WGS_PER_CU 1
+/* The fastest shape of a sweep over 132 MB (9 rotating buffers) on MI355X:
+ * 256 lanes, 4 loads per batch, 2 workgroups per CU (with both flags set,
+ * 19.6 us = 6.7 TB/s; 512 lanes x 8 loads x 1 workgroup took 21.7 us). */
+#define Q4_READ_PROBE_THREADS 256
+#define Q4_READ_PROBE_UNROLL 4
+#define Q4_READ_PROBE_WGS_PER_CU 2
 enum { Q4_PROBE_NONTEMPORAL = 1, Q4_PROBE_INTERLEAVE = 2 };
 q4_status q4_read_probe(const void *src, size_t bytes, uint32_t *sink, int threads, int unroll,
                         int wgs_per_cu, int flags, void *stream);
