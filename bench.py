@@ -280,29 +280,45 @@ def headline(d, args):
         Wp, am = by_layout[layout][i % R]
         q4.q4_gemm_skinny(A[M], Wp, am, cb, BS, out=C[M], layout=layout)
 
+    # The timed steps call the C ABI with their arguments prepared once, as a
+    # decode loop that holds its buffers does; the binding's argument checks
+    # cost several microseconds of host time per call, which left the GPU
+    # idle between these ~27 us kernels (reported beside as binding_GB/s).
+    L = q4.lib()
+    cfn = L.q4_gemm_skinny_tiles if args.layout == "tiles" else L.q4_gemm_skinny_ex
+    stream = t.cuda.current_stream().cuda_stream
+    prepared = {M: [(A[M].data_ptr(), q4.Q4_DTYPE_BF16, Wp.data_ptr(), am.data_ptr(), cb.data_ptr(),
+                     None, M, N, K, BS, C[M].data_ptr(), q4.Q4_DTYPE_BF16, stream, 0)
+                    for Wp, am in by_layout[args.layout]] for M in M_list}
+
+    def launch_c(M, i):
+        st = cfn(*prepared[M][i % R])
+        if st != q4.Q4_OK:
+            raise RuntimeError(L.q4_last_error().decode())
+
     n = 0
     for _ in range(args.warmup):
         for M in M_list:
             launch(M, n)
             n += 1
     t.cuda.synchronize()
-    # The headline: the K steps issued one call at a time, as a decode loop
-    # calls the library, timed by the host clock between synchronisations
-    # (and by HIP events on the stream the calls launch on).
-    e_start, e_end = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e_start.record()
-    for _ in range(args.steps):
-        for M in M_list:
-            launch(M, n)
-            n += 1
-    e_end.record()
+    # Per-M kernel times first (back-to-back launches of one M over the
+    # rotating weight copies, graph replays between HIP events): besides
+    # their own figures they bring the part to its sustained clock before the
+    # headline's timed steps (the first milliseconds of load after start-up
+    # or idle run well below it: 3.8-4.0 TB/s against 4.7-4.8 TB/s for the
+    # same 20 steps once warm).
+    for i in range(24 * R):  # a few milliseconds of load before the first timing
+        launch_c(M_list[i % len(M_list)], i)
     t.cuda.synchronize()
-    eager_wall = time.perf_counter() - t0
-    eager_events_s = e_start.elapsed_time(e_end) * 1e-3
-    # The same K steps captured once into a HIP graph and replayed (reported
-    # beside the headline: on this stack a replay of the mixed-M graph runs
-    # slower than the calls issued one by one).
+    per_m_us = dict(zip(M_list, d.time_launches(
+        [lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)))
+    # (not with --quick: profiling runs launch one layout only)
+    other = "rows" if args.layout == "tiles" else "tiles"
+    other_us = {} if args.quick else dict(zip(M_list, d.time_launches(
+        [lambda i, M=M: launch(M, i, other) for M in M_list], reps=12 * R)))
+    # The K steps captured once into a HIP graph and replayed (reported
+    # beside the headline).
     side = t.cuda.Stream()
     with t.cuda.stream(side):
         for M in M_list:
@@ -334,14 +350,30 @@ def headline(d, args):
     t.cuda.synchronize()
     sustained_ms = ev[1].elapsed_time(ev[4]) / 3
     del g
-    # Per-M kernel times: back-to-back launches of one M over the rotating
-    # weight copies between one event pair.
-    per_m_us = dict(zip(M_list, d.time_launches(
-        [lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)))
-    # (not with --quick: profiling runs launch one layout only)
-    other = "rows" if args.layout == "tiles" else "tiles"
-    other_us = {} if args.quick else dict(zip(M_list, d.time_launches(
-        [lambda i, M=M: launch(M, i, other) for M in M_list], reps=12 * R)))
+    # The headline: the K steps issued one call at a time, as a decode loop
+    # calls the library, timed by the host clock between synchronisations
+    # (and by HIP events on the stream the calls launch on).
+    t.cuda.synchronize()
+    e_start, e_end = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e_start.record()
+    for _ in range(args.steps):
+        for M in M_list:
+            launch_c(M, n)
+            n += 1
+    e_end.record()
+    t.cuda.synchronize()
+    eager_wall = time.perf_counter() - t0
+    eager_events_s = e_start.elapsed_time(e_end) * 1e-3
+    # the same steps through the Python binding
+    t.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for M in M_list:
+            launch(M, n)
+            n += 1
+    t.cuda.synchronize()
+    binding_wall = time.perf_counter() - t0
     total = args.steps * sum(q4_bytes(M, N, K) for M in M_list)
     per_m = {}
     for M in M_list:
@@ -382,7 +414,9 @@ def headline(d, args):
                    "M": M_list, "K": K, "N": N, "blocksize": BS, "weight_copies": R,
                    "weight_layout": args.layout},
         "pct_of_peak": round(100 * total / eager_wall / 1e9 / PEAK_GBS, 1),
-        "timed_as": "the K steps issued call by call, host wall clock between synchronisations",
+        "timed_as": "the K steps issued call by call through the C ABI, host wall clock between "
+                    "synchronisations",
+        "binding_GB/s": round(total / binding_wall / 1e9, 1),
         "events_GB/s": round(total / eager_events_s / 1e9, 1),
         "graph_replay_GB/s": round(total / wall / 1e9, 1),
         "graph_sustained_GB/s": round(total / (sustained_ms * 1e-3) / 1e9, 1),
