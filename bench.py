@@ -305,12 +305,17 @@ def headline(d, args):
     # Per-M kernel times first (back-to-back launches of one M over the
     # rotating weight copies, graph replays between HIP events): besides
     # their own figures they bring the part to its sustained clock before the
-    # headline's timed steps (the first milliseconds of load after start-up
-    # or idle run well below it: 3.8-4.0 TB/s against 4.7-4.8 TB/s for the
-    # same 20 steps once warm).
-    for i in range(24 * R):  # a few milliseconds of load before the first timing
-        launch_c(M_list[i % len(M_list)], i)
-    t.cuda.synchronize()
+    # headline's timed steps (the first tens of milliseconds of load after
+    # start-up or idle run well below it: 3.8-4.0 TB/s against 4.7-4.8 TB/s
+    # for the same 20 steps once warm).  0.2 s of untimed launches come
+    # before the first timing.
+    i = 0
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        for _ in range(8 * R):
+            launch_c(M_list[i % len(M_list)], i)
+            i += 1
+        t.cuda.synchronize()
     per_m_us = dict(zip(M_list, d.time_launches(
         [lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)))
     # (not with --quick: profiling runs launch one layout only)
@@ -533,18 +538,21 @@ def other_configs(d):
         K = 2560
         W = d.bf16(synth.bf16_weights(N, K, synth.seed(3, shape, 2)))
         b = d.bf16(synth.bias_bf16(N, synth.seed(3, shape, 3)))
-        sets = d.copies((W,), bf16_bytes(1, N, K, True))
+        sets = {"rows": d.copies((W,), bf16_bytes(1, N, K, True))}
+        if N % 16 == 0:
+            sets["tiles"] = d.copies((q4.bf16_repack_tiles(W),), bf16_bytes(1, N, K, True))
         rows = {}
         for M in range(1, 6):
             A = d.bf16(synth.activations_bf16(M, K, synth.seed(3, shape, 10 * M + 1)))
             C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
-
-            def f(i):
-                q4.bf16_gemm_skinny(A, sets[i % len(sets)][0], b, out=C)
-            u = d.time_launches([f], reps=max(60, min(200, len(sets) * 2)))[0]
-            gbs = bf16_bytes(M, N, K, True) / (u * 1e-6) / 1e9
-            rows["M=%d" % M] = {"us": round(u, 2), "GB/s": round(gbs, 1),
-                                "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+            for lay, ws in sets.items():
+                def f(i, ws=ws, lay=lay):
+                    q4.bf16_gemm_skinny(A, ws[i % len(ws)][0], b, out=C, layout=lay)
+                u = d.time_launches([f], reps=max(60, min(200, len(ws) * 2)))[0]
+                gbs = bf16_bytes(M, N, K, True) / (u * 1e-6) / 1e9
+                rows["M=%d" % M + ("" if lay == "rows" else " tiles")] = {
+                    "us": round(u, 2), "GB/s": round(gbs, 1),
+                    "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
         res["bf16+bias K=2560 N=%d" % N] = rows
         del sets, W
     log("4-bit path: bias epilogue and other element types, K=8192 N=28672")
@@ -587,16 +595,20 @@ def other_configs(d):
     log("C5 large-vocabulary projection, bf16")
     K, N = 2560, 248320
     W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
+    Ws = {"rows": W, "tiles": q4.bf16_repack_tiles(W)}
     rows = {}
     for M in range(1, 6):
         A = d.bf16(synth.activations_bf16(M, K, synth.seed(4, 1, 10 * M + 1)))
         C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
-        u = d.time_launches([lambda i: q4.bf16_gemm_skinny(A, W, None, out=C)], reps=20)[0]
-        gbs = bf16_bytes(M, N, K, False) / (u * 1e-6) / 1e9
-        rows["M=%d" % M] = {"us": round(u, 2), "GB/s": round(gbs, 1),
-                            "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
+        for lay, Wl in Ws.items():
+            u = d.time_launches([lambda i, Wl=Wl, lay=lay: q4.bf16_gemm_skinny(
+                A, Wl, None, out=C, layout=lay)], reps=20)[0]
+            gbs = bf16_bytes(M, N, K, False) / (u * 1e-6) / 1e9
+            rows["M=%d" % M + ("" if lay == "rows" else " tiles")] = {
+                "us": round(u, 2), "GB/s": round(gbs, 1),
+                "pct_peak": round(100 * gbs / PEAK_GBS, 1)}
     res["bf16 K=2560 N=248320"] = rows
-    del W
+    del W, Ws
     res["copy probe 1 GiB (read+write)"] = copy_probe(d)
     res["read probe 1 GiB"] = read_ceiling(d, 1 << 30, 1)
     return res
@@ -616,8 +628,8 @@ def copy_probe(d, nbytes=1 << 30):
 def profile_case(d, which, launches=12):
     """A few launches of one call for counter and trace runs: the split path
     (dequantize + bf16 GEMM) on the FFN at M = 16 and 256, or the bf16 skinny
-    GEMM on the 248320 x 2560 projection at M = 1; weights rotate as in the
-    timed runs."""
+    GEMM on the 248320 x 2560 projection at M = 1 (row-major or tile layout);
+    weights rotate as in the timed runs."""
     import bit_dequant_skinny_amd as q4
     t = d.t
     if which in ("split16", "split256"):
@@ -631,13 +643,16 @@ def profile_case(d, which, launches=12):
         for i in range(launches):
             Wp, am = sets[i % len(sets)]
             q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path="split")
-    elif which == "bf16c5":
+    elif which in ("bf16c5", "bf16c5tiles"):
         N, K, M = 248320, 2560, 1
         W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
+        lay = "tiles" if which == "bf16c5tiles" else "rows"
+        if lay == "tiles":
+            W = q4.bf16_repack_tiles(W)
         A = d.bf16(synth.activations_bf16(M, K, synth.seed(4, 1, 10 * M + 1)))
         C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
         for _ in range(launches):
-            q4.bf16_gemm_skinny(A, W, None, out=C)
+            q4.bf16_gemm_skinny(A, W, None, out=C, layout=lay)
     else:
         raise ValueError(which)
     t.cuda.synchronize()
@@ -657,7 +672,7 @@ def main():
                     help="packed-weight layout of the timed step (q4_repack_tiles or row-major)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel (counter calibration)")
-    ap.add_argument("--profile-case", choices=("split16", "split256", "bf16c5"),
+    ap.add_argument("--profile-case", choices=("split16", "split256", "bf16c5", "bf16c5tiles"),
                     help="only run a few launches of one call (for rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -8,7 +8,8 @@ functions below raises.
 Entry points (same names as the C ABI in include/q4skinny.h):
   q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize=64, out=None, path="auto",
                  bias=None, out_dtype=None)   (q4_gemm_skinny_path / q4_gemm_skinny_ex)
-  bf16_gemm_skinny(A, W, bias=None, out=None)
+  bf16_gemm_skinny(A, W, bias=None, out=None, layout="rows")   (bf16_gemm_skinny_tiles)
+  bf16_repack_tiles(W, out=None)
   q4_dequant(Wpacked, absmax, codebook, blocksize=64, out_dtype=torch.bfloat16, out=None)
   q4_quantize(W, codebook, blocksize=64, out=None)   codebook: host sequence of 16 floats
   q4_codebook_preset(name)   "nf4_style" or "int4" -> numpy float32 [16]
@@ -38,7 +39,7 @@ EXPORTS = (
     "q4_copy_probe", "q4_version", "q4_quantize", "q4_codebook_preset",
     "q4_set_crossover_shape", "q4_get_crossover_shape", "q4_clear_crossover_shapes",
     "q4_repack_tiles", "q4_gemm_skinny_tiles", "q4_dequant_tiles", "q4_read_probe",
-    "q4_gemm_skinny_ex_noalloc",
+    "q4_gemm_skinny_ex_noalloc", "bf16_repack_tiles", "bf16_gemm_skinny_tiles",
 )
 PRESETS = {"nf4_style": 0, "int4": 1}
 
@@ -69,6 +70,8 @@ def lib():
         L.q4_gemm_skinny_path.argtypes = [P, P, P, P, I, I, I, I, P, P, I]
         L.q4_gemm_skinny_ex.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
         L.bf16_gemm_skinny.argtypes = [P, P, P, I, I, I, P, P]
+        L.bf16_gemm_skinny_tiles.argtypes = [P, P, P, I, I, I, P, P]
+        L.bf16_repack_tiles.argtypes = [P, P, I, I, P]
         L.q4_dequant.argtypes = [P, P, P, I, I, I, P, I, P]
         L.q4_gemm_skinny_tiles.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
         L.q4_gemm_skinny_ex_noalloc.argtypes = [P, I, P, P, P, P, I, I, I, I, P, I, P, I]
@@ -85,7 +88,8 @@ def lib():
         for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
                      "q4_gemm_skinny_ex_noalloc", "q4_gemm_skinny_tiles", "q4_dequant_tiles",
                      "q4_repack_tiles",
-                     "bf16_gemm_skinny", "q4_dequant",
+                     "bf16_gemm_skinny", "bf16_gemm_skinny_tiles", "bf16_repack_tiles",
+                     "q4_dequant",
                      "q4_copy_probe", "q4_read_probe", "q4_set_crossover_m",
                      "q4_release_workspace",
                      "q4_quantize", "q4_codebook_preset", "q4_set_crossover_shape",
@@ -189,8 +193,12 @@ def q4_gemm_skinny(A, Wpacked, absmax, codebook, blocksize: int = 64, out=None, 
     return out
 
 
-def bf16_gemm_skinny(A, W, bias=None, out=None):
-    """C[M,N] = A[M,K] * W[N,K]^T (+ bias) in bf16, M <= 5."""
+def bf16_gemm_skinny(A, W, bias=None, out=None, layout: str = "rows"):
+    """C[M,N] = A[M,K] * W[N,K]^T (+ bias) in bf16, M <= 5.
+
+    layout "tiles" reads weights made by bf16_repack_tiles (same shape)."""
+    if layout not in ("rows", "tiles"):
+        raise ValueError("layout must be 'rows' or 'tiles'")
     torch = _torch()
     if A.dim() != 2 or W.dim() != 2 or A.shape[1] != W.shape[1]:
         raise ValueError("A must be [M, K] and W [N, K]")
@@ -203,9 +211,26 @@ def bf16_gemm_skinny(A, W, bias=None, out=None):
     elif tuple(out.shape) != (M, N):
         raise ValueError("out must be [M, N]")
     bptr = None if bias is None else _dev(bias, "bias", torch.bfloat16)
-    _check(lib().bf16_gemm_skinny(
+    fn = lib().bf16_gemm_skinny if layout == "rows" else lib().bf16_gemm_skinny_tiles
+    _check(fn(
         _dev(A, "A", torch.bfloat16), _dev(W, "W", torch.bfloat16), bptr, M, N, K,
         _dev(out, "out", torch.bfloat16), _stream(A)))
+    return out
+
+
+def bf16_repack_tiles(W, out=None):
+    """The tile layout of row-major bf16 weights [N, K] (same shape: 16-row
+    tiles of 1 KiB units of 32 k; N % 16 == 0, K % 32 == 0)."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    N, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    elif tuple(out.shape) != (N, K):
+        raise ValueError("out must be [N, K]")
+    _check(lib().bf16_repack_tiles(
+        _dev(W, "W", torch.bfloat16), _dev(out, "out", torch.bfloat16), N, K, _stream(W)))
     return out
 
 

@@ -572,6 +572,34 @@ q4_status dequant_impl(const uint8_t *Wpacked, int wl, const float *absmax,
     return st == Q4_OK ? ok() : st;
 }
 
+// bf16_gemm_skinny over row-major (wl = 0) or tile-layout (wl = 1) weights.
+q4_status bf16_impl(const void *A, const void *W, int wl, const void *bias, int M, int N, int K,
+                    void *C, void *stream) {
+    if (M < 0 || N < 0 || K < 0)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d, N=%d, K=%d)", M, N, K);
+    if (K == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "K must be positive");
+    if (K % 8) return fail(Q4_ERR_INVALID_ARGUMENT, "K=%d must be a multiple of 8", K);
+    if (wl && (N % 16 != 0 || K % 32 != 0))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "the bf16 tile layout needs N %% 16 == 0 and K %% 32 == 0 (N=%d, K=%d)", N, K);
+    if (M > 5) return fail(Q4_ERR_UNSUPPORTED, "bf16 skinny GEMM supports M <= 5 (M=%d)", M);
+    if ((int64_t)N * (int64_t)K > (int64_t(1) << 40))
+        return fail(Q4_ERR_UNSUPPORTED, "N*K too large");
+    if (wl && !q4::bf16_tiles_fit(N, K))
+        return fail(Q4_ERR_UNSUPPORTED, "bf16 tile-layout matrix too large (N=%d, K=%d)", N, K);
+    if (M == 0 || N == 0) return ok();
+    if (!A || !W || !C) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 2) || (bias && !aligned(bias, 2)))
+        return fail(Q4_ERR_INVALID_ARGUMENT,
+                    "A and W must be 16-byte aligned, C and bias 2-byte aligned");
+    drain_prior_error();
+    q4_status st = launch_checked("gemm", [&] {
+        return q4::launch_bf16_gemm(A, Q4_DTYPE_BF16, static_cast<const uint16_t *>(W), bias, M,
+                                    N, K, C, Q4_DTYPE_BF16, static_cast<hipStream_t>(stream), wl);
+    });
+    return st == Q4_OK ? ok() : st;
+}
+
 }  // namespace
 
 namespace q4 {
@@ -649,22 +677,35 @@ q4_status q4_gemm_skinny(const void *A, const uint8_t *Wpacked, const float *abs
 
 q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M, int N, int K,
                            void *C, void *stream) {
-    if (M < 0 || N < 0 || K < 0)
-        return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (M=%d, N=%d, K=%d)", M, N, K);
+    return bf16_impl(A, W, 0, bias, M, N, K, C, stream);
+}
+
+q4_status bf16_gemm_skinny_tiles(const void *A, const void *Wtiles, const void *bias, int M,
+                                 int N, int K, void *C, void *stream) {
+    return bf16_impl(A, Wtiles, 1, bias, M, N, K, C, stream);
+}
+
+q4_status bf16_repack_tiles(const void *W, void *Wtiles, int N, int K, void *stream) {
+    if (N < 0 || K < 0) return fail(Q4_ERR_INVALID_ARGUMENT, "negative size (N=%d, K=%d)", N, K);
     if (K == 0) return fail(Q4_ERR_INVALID_ARGUMENT, "K must be positive");
-    if (K % 8) return fail(Q4_ERR_INVALID_ARGUMENT, "K=%d must be a multiple of 8", K);
-    if (M > 5) return fail(Q4_ERR_UNSUPPORTED, "bf16 skinny GEMM supports M <= 5 (M=%d)", M);
-    if ((int64_t)N * (int64_t)K > (int64_t(1) << 40))
-        return fail(Q4_ERR_UNSUPPORTED, "N*K too large");
-    if (M == 0 || N == 0) return ok();
-    if (!A || !W || !C) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 2) || (bias && !aligned(bias, 2)))
+    if (N % 16 != 0 || K % 32 != 0)
         return fail(Q4_ERR_INVALID_ARGUMENT,
-                    "A and W must be 16-byte aligned, C and bias 2-byte aligned");
+                    "the bf16 tile layout needs N %% 16 == 0 and K %% 32 == 0 (N=%d, K=%d)", N, K);
+    if (!q4::bf16_tiles_fit(N, K))
+        return fail(Q4_ERR_UNSUPPORTED, "bf16 tile-layout matrix too large (N=%d, K=%d)", N, K);
+    if (N == 0) return ok();
+    if (!W || !Wtiles) return fail(Q4_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned(W, 16) || !aligned(Wtiles, 16))
+        return fail(Q4_ERR_INVALID_ARGUMENT, "W and Wtiles must be 16-byte aligned");
+    const size_t bytes = (size_t)N * (size_t)K * 2;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(W), b = reinterpret_cast<uintptr_t>(Wtiles);
+    if (a < b + bytes && b < a + bytes)
+        return fail(Q4_ERR_INVALID_ARGUMENT, "Wtiles must not overlap W");
     drain_prior_error();
-    q4_status st = launch_checked("gemm", [&] {
-        return q4::launch_bf16_gemm(A, Q4_DTYPE_BF16, static_cast<const uint16_t *>(W), bias, M,
-                                    N, K, C, Q4_DTYPE_BF16, static_cast<hipStream_t>(stream));
+    q4_status st = launch_checked("repack", [&] {
+        return q4::launch_bf16_repack_tiles(static_cast<const uint16_t *>(W),
+                                            static_cast<uint16_t *>(Wtiles), N, K,
+                                            static_cast<hipStream_t>(stream));
     });
     return st == Q4_OK ? ok() : st;
 }

@@ -189,20 +189,39 @@ __global__ __launch_bounds__(kThreads) void repack_tiles_kernel(const uint4 *__r
 
 }  // namespace
 
-hipError_t launch_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
-                               hipStream_t s) {
-    if (N % 16 != 0 || K % 128 != 0 || (uint64_t)N * (uint64_t)K / 2 >= (1ull << 32))
+namespace {
+
+// The 16-row tiling of both weight types: rows of row_bytes bytes (a
+// multiple of 64) cut into 64-byte columns; (tile, column) is one 1 KiB unit.
+hipError_t repack_rows16(const void *src, void *dst, int N, uint64_t row_bytes, hipStream_t s) {
+    if (N % 16 != 0 || row_bytes % 64 != 0 || (uint64_t)N * row_bytes >= (1ull << 32))
         return hipErrorInvalidValue;
-    const uint32_t pieces = (uint32_t)((uint64_t)N * (uint64_t)K / 32);
+    const uint32_t pieces = (uint32_t)((uint64_t)N * row_bytes / 16);
     const DeviceInfo info = device_info();
     uint32_t blocks = (pieces + kThreads - 1) / kThreads;
     const uint32_t cap = (uint32_t)info.num_cus * 8;
     if (blocks > cap) blocks = cap;
     if (blocks == 0) return hipSuccess;
     repack_tiles_kernel<<<dim3(blocks), dim3(kThreads), 0, s>>>(
-        reinterpret_cast<const uint4 *>(Wpacked), reinterpret_cast<uint4 *>(Wtiles), pieces,
-        (uint32_t)K / 128, (uint32_t)K / 32);
+        reinterpret_cast<const uint4 *>(src), reinterpret_cast<uint4 *>(dst), pieces,
+        (uint32_t)(row_bytes / 64), (uint32_t)(row_bytes / 16));
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
+                               hipStream_t s) {
+    if (K % 128 != 0) return hipErrorInvalidValue;
+    return repack_rows16(Wpacked, Wtiles, N, (uint64_t)K / 2, s);
+}
+
+// bf16 weights: a unit is 16 rows x 32 k (the 64 bytes of a row one
+// matrix-core step consumes), piece l = row l % 16, k 8(l / 16) .. +8.
+hipError_t launch_bf16_repack_tiles(const uint16_t *W, uint16_t *Wtiles, int N, int K,
+                                    hipStream_t s) {
+    if (K % 32 != 0) return hipErrorInvalidValue;
+    return repack_rows16(W, Wtiles, N, (uint64_t)K * 2, s);
 }
 
 hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const float *codebook,

@@ -29,6 +29,13 @@
 // rows, weight rows past N and steps past the wave's share of K cost no memory
 // traffic and need no branches.  Wider slabs take the plain kernel below.
 //
+// The streaming kernel also reads weights in this library's tile layout
+// (bf16_repack_tiles): the 16 rows x 32 k one instruction consumes stored as
+// one contiguous 1 KiB unit in lane order, so each load instruction reads
+// 1 KiB of contiguous memory instead of 64-byte pieces of 16 rows.  Lanes
+// receive the same values in the same registers, so the results are
+// bit-identical to the row-major call.
+//
 // fp16 activations (split path of the 4-bit GEMM) are split exactly into
 // bf16 hi + lo and take two MFMAs per step.  The bias (optional) has the
 // output's type; the output is bf16, fp16 or fp32, rounded once from the fp32
@@ -65,8 +72,10 @@ __device__ __forceinline__ floatx4 mfma_step(uint4 av, uint4 wv, floatx4 acc) {
 
 // Streaming kernel for M <= 16: wave (tile, k part) as in bf16_gemm_kernel,
 // every step one 16-byte weight load and one 16-byte activation load per
-// lane, kRing steps ahead of the MFMA that consumes them.
-template <int AT>
+// lane, kRing steps ahead of the MFMA that consumes them.  WL = 1: weights in
+// the tile layout (unit (tile, step) at (tile * K/32 + step) * 1 KiB, lane l's
+// 16 bytes at 16 l; needs N % 16 == 0 and K % 32 == 0).
+template <int AT, int WL>
 __global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
     const void *__restrict__ bias, int M, int N, int K, int ksplit,
@@ -94,10 +103,18 @@ __global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
         const uint32_t k = (uint32_t)(st << 5) + (uint32_t)(g << 3);
         return (st < s_end && k < (uint32_t)K) ? row + 2 * k : kPastEnd;
     };
+    // tiles past the last one lie beyond the buffer as well
+    const uint32_t w_tile = (uint32_t)tile * (uint32_t)K * 32u + (uint32_t)lane * 16u;
+    auto woffs = [&](int st) -> uint32_t {
+        if constexpr (WL == 1)
+            return st < s_end ? w_tile + ((uint32_t)st << 10) : kPastEnd;
+        else
+            return offs(st, w_row);
+    };
     uint4 wv[kRing], av[kRing];
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
-        wv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)offs(s_begin + r, w_row), 0, 0));
+        wv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woffs(s_begin + r), 0, 0));
         av[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)offs(s_begin + r, a_row), 0, 0));
         __builtin_amdgcn_sched_barrier(0);  // issue in ring order
     }
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
         for (int r = 0; r < kRing; ++r) {
             acc = mfma_step<AT>(av[r], wv[r], acc);
             const int nx = s + r + kRing;
-            wv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)offs(nx, w_row), 0, 0));
+            wv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woffs(nx), 0, 0));
             av[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)offs(nx, a_row), 0, 0));
             // keep each refill right after the MFMA that frees its registers,
             // so every step waits only for loads issued kRing steps earlier
@@ -206,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void bf16_gemm_kernel(
 
 template <int AT, int MT>
 hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const void *bias, int M, int N,
-                     int K, void *C, int c_dt, hipStream_t s) {
+                     int K, void *C, int c_dt, int wl, hipStream_t s) {
     const int tiles = (N + 15) / 16;
     const DeviceInfo info = device_info();
     // Split K across the waves of a workgroup when there are too few feature
@@ -220,9 +237,14 @@ hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const void *bias, int
     // rows past N) and 16 rows of activations must stay below 4 GiB.
     const bool stream = MT == 1 && ((uint64_t)N + 16) * (uint64_t)K * 2 < (1ull << 31) &&
                         16ull * (uint64_t)K * 2 < (1ull << 31);
-    if (stream)
-        bf16_stream_kernel<AT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
-                                                                       ksplit, C, c_dt);
+    if (wl) {
+        // the tile layout is read by the streaming kernel only
+        if (AT != kBf16 || !stream || N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
+        bf16_stream_kernel<kBf16, 1><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
+                                                                             ksplit, C, c_dt);
+    } else if (stream)
+        bf16_stream_kernel<AT, 0><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
+                                                                          ksplit, C, c_dt);
     else
         bf16_gemm_kernel<AT, MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
                                                                          ksplit, C, c_dt);
@@ -231,7 +253,7 @@ hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const void *bias, int
 
 template <int AT>
 hipError_t launch_slabs(const uint16_t *A, const uint16_t *W, const void *bias, int M, int N,
-                        int K, void *C, int c_dt, hipStream_t s) {
+                        int K, void *C, int c_dt, int wl, hipStream_t s) {
     // Token tiles of 16; above 64 tokens the weight is streamed once per
     // 64-token slab.
     const size_t c_size = c_dt == kF32 ? 4 : 2;
@@ -240,9 +262,10 @@ hipError_t launch_slabs(const uint16_t *A, const uint16_t *W, const void *bias, 
         const uint16_t *Am = A + (size_t)m0 * K;
         void *Cm = static_cast<char *>(C) + (size_t)m0 * N * c_size;
         hipError_t e;
-        if (mm <= 16) e = launch_mt<AT, 1>(Am, W, bias, mm, N, K, Cm, c_dt, s);
-        else if (mm <= 32) e = launch_mt<AT, 2>(Am, W, bias, mm, N, K, Cm, c_dt, s);
-        else e = launch_mt<AT, 4>(Am, W, bias, mm, N, K, Cm, c_dt, s);
+        if (mm <= 16) e = launch_mt<AT, 1>(Am, W, bias, mm, N, K, Cm, c_dt, wl, s);
+        else if (wl) e = hipErrorInvalidValue;
+        else if (mm <= 32) e = launch_mt<AT, 2>(Am, W, bias, mm, N, K, Cm, c_dt, 0, s);
+        else e = launch_mt<AT, 4>(Am, W, bias, mm, N, K, Cm, c_dt, 0, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -251,10 +274,17 @@ hipError_t launch_slabs(const uint16_t *A, const uint16_t *W, const void *bias, 
 }  // namespace
 
 hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,
-                            int N, int K, void *C, int c_dt, hipStream_t s) {
+                            int N, int K, void *C, int c_dt, hipStream_t s, int wl) {
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
-    if (a_dt == kF16) return launch_slabs<kF16>(A16, W, bias, M, N, K, C, c_dt, s);
-    return launch_slabs<kBf16>(A16, W, bias, M, N, K, C, c_dt, s);
+    if (a_dt == kF16) return launch_slabs<kF16>(A16, W, bias, M, N, K, C, c_dt, wl, s);
+    return launch_slabs<kBf16>(A16, W, bias, M, N, K, C, c_dt, wl, s);
+}
+
+bool bf16_tiles_fit(int N, int K) {
+    // the streaming kernel's offsets: every tile of the grid (up to 3 past
+    // the last) and 16 activation rows below 2 GiB
+    return ((uint64_t)N + 64) * (uint64_t)K * 2 < (1ull << 31) &&
+           16ull * (uint64_t)K * 2 < (1ull << 31);
 }
 
 }  // namespace q4

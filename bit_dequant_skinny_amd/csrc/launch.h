@@ -24,6 +24,10 @@ hipError_t launch_dequant(const uint8_t *Wpacked, const float *absmax, const flo
 // units (N % 16 == 0, K % 128 == 0; see launch_repack_tiles).
 hipError_t launch_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
                                hipStream_t s);
+// bf16 weights [N, K] -> 16-row tiles of 1 KiB units of 32 k (N % 16 == 0,
+// K % 32 == 0, N*K*2 below 4 GiB).
+hipError_t launch_bf16_repack_tiles(const uint16_t *W, uint16_t *Wtiles, int N, int K,
+                                    hipStream_t s);
 
 // Fused 4-bit GEMM, C = A * dequant(W)^T (+ bias), A of type a_dt, bias and C
 // of type c_dt.  Dispatches to the matrix-core kernel (bf16 or fp16
@@ -80,8 +84,11 @@ hipError_t launch_gemm_tiled(const uint16_t *A, const uint16_t *W, const void *b
                              int N, int K, int ksplit, void *C, int c_dt, hipStream_t s);
 
 // bf16-weight GEMM on the matrix cores, C = A * W^T (+ bias); A bf16 or fp16.
+// wl = 1: W in the tile layout of launch_bf16_repack_tiles (bf16 A, M <= 16,
+// bf16_tiles_fit(N, K)).
 hipError_t launch_bf16_gemm(const void *A, int a_dt, const uint16_t *W, const void *bias, int M,
-                            int N, int K, void *C, int c_dt, hipStream_t s);
+                            int N, int K, void *C, int c_dt, hipStream_t s, int wl = 0);
+bool bf16_tiles_fit(int N, int K);
 
 // Quantizer thresholds derived on the host from a strictly increasing table:
 // mid[i] = (c[i] + c[i+1]) / 2 in fp64 (exact), zero_code = the entry nearest

@@ -250,6 +250,46 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
                            int K, void *C, void *stream);
 
 /*
+ * Tile layout of bf16 weights (a layout of this library; the GEMM of the
+ * report on vLLM pull request 40687, section "关键源码片段", reads W [N, K]
+ * row-major, which bf16_gemm_skinny keeps).  Rows form tiles of 16 (tile t =
+ * rows 16t..16t+15) and a row's elements form steps of 32 (step s = k
+ * 32s..32s+31: the k one matrix-core instruction consumes).  The 16 x 32
+ * elements of (t, s) are one 1 KiB unit at element (t * K/32 + s) * 512;
+ * piece l = 0..63 of a unit (8 elements) holds k = 32s + 8*(l/16) .. +7 of
+ * row 16t + l % 16, the 16 bytes matrix-core lane l takes for that step.
+ * Each load instruction then reads 1 KiB of contiguous memory instead of
+ * 64-byte pieces of 16 rows 2*K bytes apart (on MI355X 8-16 % faster on the
+ * K = 2560 shapes).  Requires N % 16 == 0, K % 32 == 0 and (N + 64)*K*2
+ * below 2 GiB.
+ */
+
+/*
+ * bf16_repack_tiles: Wtiles = the tile layout of the row-major bf16 W.
+ *
+ *  W bf16 [N, K] (device), Wtiles bf16 [N*K] (device), both 16-byte aligned
+ *  and not overlapping.  A pure permutation of 16-byte pieces, bit-exact.
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: NULL pointer, N/K < 0, K == 0, N % 16 != 0,
+ *    K % 32 != 0, misalignment, overlapping buffers.
+ *  Q4_ERR_UNSUPPORTED: (N + 64)*K*2 >= 2 GiB.
+ */
+q4_status bf16_repack_tiles(const void *W, void *Wtiles, int N, int K, void *stream);
+
+/*
+ * bf16_gemm_skinny_tiles: bf16_gemm_skinny over weights in the tile layout.
+ * Arguments and results are those of bf16_gemm_skinny on the row-major
+ * weights the tiles were made from; the outputs are bit-identical to it
+ * (each lane receives the same values and the sums run in the same order).
+ *
+ *  Q4_ERR_INVALID_ARGUMENT: as bf16_gemm_skinny, plus N % 16 != 0 or
+ *    K % 32 != 0.
+ *  Q4_ERR_UNSUPPORTED: as bf16_gemm_skinny, plus (N + 64)*K*2 >= 2 GiB.
+ */
+q4_status bf16_gemm_skinny_tiles(const void *A, const void *Wtiles, const void *bias, int M,
+                                 int N, int K, void *C, void *stream);
+
+/*
  * q4_dequant: out[n, k] = codebook[code(n, k)] * absmax[n, k / blocksize].
  *
  * The dequantize step of the split path in the bitsandbytes pull request

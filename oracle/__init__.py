@@ -23,6 +23,8 @@ Function map (steps as numbered in the C file):
   quantize        O11 blockwise absmax + nearest-entry codes (inverse of O3)
   tile_offset     O12 where byte j of packed row n sits in the tile layout
   repack_tiles    O12 the row-major packed bytes moved to the tile layout
+  bf16_tile_index O13 where element k of bf16 weight row n sits in its tile layout
+  bf16_repack_tiles O13 the row-major bf16 weights moved to that layout
 
 Element types are named "bf16", "fp16", "fp32" (uint16 bit patterns for the
 two 16-bit types, float32 arrays for fp32).
@@ -101,6 +103,9 @@ class Oracle:
         lib.oracle_tile_offset.argtypes = [I, I, I, I]
         lib.oracle_tile_offset.restype = I
         lib.oracle_repack_tiles.argtypes = [P, I, I, P]
+        lib.oracle_bf16_tile_index.argtypes = [I, I, I, I]
+        lib.oracle_bf16_tile_index.restype = I
+        lib.oracle_bf16_repack_tiles.argtypes = [P, I, I, P]
         self.lib = lib
         self.path = lib_path
 
@@ -243,6 +248,16 @@ class Oracle:
         Wp = _c(Wpacked, np.uint8)
         out = np.empty((N, K // 2), dtype=np.uint8)
         self.lib.oracle_repack_tiles(_ptr(Wp), N, K, _ptr(out))
+        return out
+
+    def bf16_tile_index(self, N, K, n, k) -> int:
+        return int(self.lib.oracle_bf16_tile_index(N, K, n, k))
+
+    def bf16_repack_tiles(self, W_bf16, N, K) -> np.ndarray:
+        """uint16 [N, K] holding the tile layout of row-major bf16 W."""
+        W = _c(W_bf16, np.uint16)
+        out = np.empty((N, K), dtype=np.uint16)
+        self.lib.oracle_bf16_repack_tiles(_ptr(W), N, K, _ptr(out))
         return out
 
     def gemm_f32w(self, A_bf16, W_f32, M, N, K):

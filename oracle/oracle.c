@@ -418,6 +418,33 @@ void oracle_repack_tiles(const uint8_t *Wpacked, int64_t N, int64_t K, uint8_t *
             out[oracle_tile_offset(N, K, n, j)] = Wpacked[n * (K / 2) + j];
 }
 
+/* O13  The tile layout of unquantized bf16 weights (again a layout of this
+ * library; the bf16 skinny GEMM of the pages reads W [N, K] row-major).
+ * Rows form tiles of 16 as in O12; a row's elements form steps of 32
+ * (step s = k 32s..32s+31, the k one matrix-core instruction consumes);
+ * the 16 rows x 32 elements of (t, s) become one unit of 512 elements,
+ * stored unit after unit in the order (t, s) with s fastest; inside a unit,
+ * piece p = 0..63 of 8 elements holds k = 32s + 8*(p / 16) .. +7 of row
+ * 16t + p % 16.  Requires N % 16 == 0 and K % 32 == 0.
+ * oracle_bf16_tile_index gives the element index that W[n][k] moves to;
+ * oracle_bf16_repack_tiles moves every element there. */
+int64_t oracle_bf16_tile_index(int64_t N, int64_t K, int64_t n, int64_t k)
+{
+    (void)N;
+    int64_t steps = K / 32;     /* steps per row */
+    int64_t t = n / 16, r = n % 16;
+    int64_t s = k / 32, q = k % 32;
+    int64_t piece = r + 16 * (q / 8);
+    return (t * steps + s) * 512 + piece * 8 + q % 8;
+}
+
+void oracle_bf16_repack_tiles(const uint16_t *W, int64_t N, int64_t K, uint16_t *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            out[oracle_bf16_tile_index(N, K, n, k)] = W[n * K + k];
+}
+
 /* Thread count of the OpenMP loops from here on (the benchmark's CPU baseline
  * times the oracle single-threaded and on all cores); n < 1 leaves it as is. */
 void oracle_set_threads(int n)

@@ -531,4 +531,28 @@ def pin_quantize_matches_numpy_searchsorted(orc):
         assert np.array_equal(a1, a2) and np.array_equal(c1, c2)
 
 
+def pin_tile_layout_golden(orc):
+    """O12: byte offsets worked by hand (tests/golden/tile_layout.txt)."""
+    for line in golden_lines("tile_layout.txt"):
+        n, j, off = (int(v) for v in line.split())
+        assert orc.tile_offset(32, 256, n, j) == off, ("tile", n, j)
+
+
+def pin_bf16_tile_layout(orc):
+    """O13: element indices worked by hand (tests/golden/bf16_tile_layout.txt),
+    a bijection of whole units, and the byte tiling of O12 on 2*K-byte rows."""
+    for line in golden_lines("bf16_tile_layout.txt"):
+        n, k, idx = (int(v) for v in line.split())
+        assert orc.bf16_tile_index(32, 64, n, k) == idx, ("bf16 tile", n, k)
+    N, K = 32, 96
+    idx = np.array([[orc.bf16_tile_index(N, K, n, k) for k in range(K)] for n in range(N)])
+    assert sorted(idx.ravel().tolist()) == list(range(N * K))
+    for n in range(N):
+        for k in range(K):
+            assert orc.tile_offset(N, 4 * K, n, 2 * k) == 2 * idx[n, k]
+    W = np.arange(N * K, dtype=np.uint16).reshape(N, K)
+    T = orc.bf16_repack_tiles(W, N, K).ravel()
+    assert np.array_equal(T[idx.ravel()], W.ravel())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
