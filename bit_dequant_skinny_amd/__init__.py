@@ -15,6 +15,7 @@ Entry points (same names as the C ABI in include/q4skinny.h):
   q4_codebook_preset(name)   "nf4_style" or "int4" -> numpy float32 [16]
   q4_get_crossover_m() / q4_set_crossover_m(m) / q4_release_workspace()
   q4_set_crossover_shape(N, K, m) / q4_get_crossover_shape(N, K) / q4_clear_crossover_shapes()
+  q4_skinny_kparts(M, N, K)
   q4_copy_probe(src, dst) / q4_read_probe(src, sink, ...) / q4_version()
 ``lib()`` returns the raw ctypes handle for callers that pass pointers.
 """
@@ -40,6 +41,7 @@ EXPORTS = (
     "q4_set_crossover_shape", "q4_get_crossover_shape", "q4_clear_crossover_shapes",
     "q4_repack_tiles", "q4_gemm_skinny_tiles", "q4_dequant_tiles", "q4_read_probe",
     "q4_gemm_skinny_ex_noalloc", "bf16_repack_tiles", "bf16_gemm_skinny_tiles",
+    "q4_skinny_kparts",
 )
 PRESETS = {"nf4_style": 0, "int4": 1}
 
@@ -85,6 +87,8 @@ def lib():
         L.q4_set_crossover_shape.argtypes = [I, I, I]
         L.q4_get_crossover_shape.argtypes = [I, I]
         L.q4_get_crossover_shape.restype = ctypes.c_int
+        L.q4_skinny_kparts.argtypes = [I, I, I]
+        L.q4_skinny_kparts.restype = ctypes.c_int
         for name in ("q4_gemm_skinny", "q4_gemm_skinny_path", "q4_gemm_skinny_ex",
                      "q4_gemm_skinny_ex_noalloc", "q4_gemm_skinny_tiles", "q4_dequant_tiles",
                      "q4_repack_tiles",
@@ -256,6 +260,11 @@ def q4_dequant(Wpacked, absmax, codebook, blocksize: int = 64, out_dtype=None, o
         _dev(codebook, "codebook", torch.float32), N, K, blocksize, _dev(out, "out", out_dtype),
         code, _stream(Wpacked)))
     return out
+
+
+def q4_skinny_kparts(M: int, N: int, K: int) -> int:
+    """Parts the fused skinny kernel splits K into for this shape (1 = none)."""
+    return int(lib().q4_skinny_kparts(M, N, K))
 
 
 def q4_repack_tiles(Wpacked, out=None):

@@ -210,6 +210,21 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 thread_local void *tl_fixed_scratch = nullptr;
 thread_local size_t tl_fixed_bytes = 0;
 
+q4_status refuse_under_capture(hipStream_t s, const char *what, size_t bytes) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(Q4_ERR_HIP, "%s: hipStreamIsCapturing: %s", what, hipGetErrorString(e));
+    }
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(Q4_ERR_HIP,
+                    "%s of %zu bytes needed while the stream is being captured: run the call "
+                    "once outside the capture first",
+                    what, bytes);
+    return Q4_OK;
+}
+
 q4_status workspace(int device, hipStream_t s, size_t bytes, void **out) {
     if (tl_fixed_scratch) {
         if (bytes > tl_fixed_bytes)
@@ -223,17 +238,9 @@ q4_status workspace(int device, hipStream_t s, size_t bytes, void **out) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[{device, s}];
     if (w.bytes < bytes) {
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        hipError_t e = hipStreamIsCapturing(s, &cap);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(Q4_ERR_HIP, "workspace: hipStreamIsCapturing: %s", hipGetErrorString(e));
-        }
-        if (cap != hipStreamCaptureStatusNone)
-            return fail(Q4_ERR_HIP,
-                        "workspace of %zu bytes needed while the stream is being captured "
-                        "(have %zu): run the call once outside the capture first",
-                        bytes, w.bytes);
+        q4_status st = refuse_under_capture(s, "workspace", bytes);
+        if (st != Q4_OK) return st;
+        hipError_t e = hipSuccess;
         if (w.ptr) {
             // The old buffer may still be read by work queued on `s`; it is
             // freed even if that wait fails.
@@ -356,10 +363,12 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
 // bf16 activations: the tiled kernel above fused_tiled_min_m rows, else the
 // skinny kernels in passes of up to Q4_FUSED_PASS_M token rows over
 // consecutive row slabs, each streaming the packed weights once more (more
-// than one pass only where the tiled kernel cannot run).
+// than one pass only where the tiled kernel cannot run).  Up to 16 rows the
+// skinny kernel may split K over workgroups (kparts_ok: the workspace is
+// free for its partial sums, i.e. not holding activation planes).
 q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
                     const void *bias, int M, int N, int K, int bs_log2, int wl, void *C, int c_dt,
-                    hipStream_t s) {
+                    hipStream_t s, bool kparts_ok = true) {
     if (a_dt != Q4_DTYPE_BF16 && bs_log2 >= 6 && q4::q4_fused_mfma_fits(M, N, K))
         return run_fused_planes(A, a_dt, Wp, am, cb, bias, M, N, K, bs_log2, wl, C, c_dt, s);
     if (a_dt == Q4_DTYPE_BF16 && fused_tiled(M, N, K, bs_log2)) {
@@ -382,13 +391,28 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
             return q4::launch_sum_planes(parts, ks, M, N, bias, C, c_dt, s);
         });
     }
+    float *kpart = nullptr;
+    if (kparts_ok && a_dt == Q4_DTYPE_BF16 && bs_log2 >= 6 && M <= 16 &&
+        q4::q4_fused_mfma_fits(M, N, K)) {
+        const int ks = q4::q4_fused_kparts(M, N, K);
+        if (ks > 1) {
+            int device = 0;
+            q4_status st = current_device(&device);
+            if (st != Q4_OK) return st;
+            void *ws = nullptr;
+            st = workspace(device, s, (size_t)ks * (size_t)M * (size_t)N * 4, &ws);
+            if (st != Q4_OK) return st;
+            kpart = static_cast<float *>(ws);
+        }
+    }
     const size_t a_row = (size_t)K * dtype_size(a_dt), c_row = (size_t)N * dtype_size(c_dt);
     for (int m0 = 0; m0 < M; m0 += Q4_FUSED_PASS_M) {
         const int mm = M - m0 < Q4_FUSED_PASS_M ? M - m0 : Q4_FUSED_PASS_M;
         q4_status st = launch_checked("fused", [&] {
             return q4::launch_q4_fused(static_cast<const char *>(A) + (size_t)m0 * a_row, a_dt,
                                        Wp, am, cb, bias, mm, N, K, bs_log2,
-                                       static_cast<char *>(C) + (size_t)m0 * c_row, c_dt, wl, s);
+                                       static_cast<char *>(C) + (size_t)m0 * c_row, c_dt, wl, s,
+                                       kpart);
         });
         if (st != Q4_OK) return st;
     }
@@ -428,7 +452,7 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
     st = tiled ? run_fused_tiled(planes, Wp, am, cb, nullptr, rows, N, K, bs_log2, wl, plan,
                                  parts, parts, Q4_DTYPE_FP32, s)
                : run_fused(planes, Q4_DTYPE_BF16, Wp, am, cb, nullptr, rows, N, K, bs_log2, wl,
-                           parts, Q4_DTYPE_FP32, s);
+                           parts, Q4_DTYPE_FP32, s, false);
     if (st != Q4_OK) return st;
     return launch_checked("plane sum", [&] {
         return q4::launch_sum_planes(parts, ks * np, M, N, bias, C, c_dt, s);
@@ -838,6 +862,11 @@ q4_status q4_set_crossover_shape(int N, int K, int m) {
 }
 
 int q4_get_crossover_shape(int N, int K) { return crossover_for(N, K); }
+
+int q4_skinny_kparts(int M, int N, int K) {
+    if (M < 1 || M > 16 || N < 1 || K < 1) return 1;
+    return q4::q4_fused_kparts(M, N, K);
+}
 
 q4_status q4_clear_crossover_shapes(void) {
     std::lock_guard<std::mutex> lock(g_shape_mutex);

@@ -54,6 +54,16 @@
 // after a barrier that leaves global loads in flight, each output is summed
 // over the waves in wave order (deterministic, no atomics) and stored as
 // bf16.
+//
+// K parts.  When the tile groups would leave compute units idle (320 tiles
+// of a 5120-row matrix on 256 CUs give 160 groups of two), K is cut into KS
+// parts of SPP segments and workgroup b computes part b / groups of group
+// b % groups, one chunk per workgroup.  Each part's fp32 sums go to its own
+// slab of a buffer, and a second kernel adds the slabs in part order, adds
+// the bias and rounds once (deterministic).  Combining inside this kernel
+// (the last workgroup of a group to arrive adds the parts) needs an
+// agent-scope release per workgroup, an L2 write-back, which measured far
+// slower than the second launch.
 #include "device.h"
 #include "launch.h"
 
@@ -89,8 +99,8 @@ template <int SR, int TB, int RS, int UF, int P, int MB, bool BS64, int WL>
 __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups,
-    void *__restrict__ C, int c_dt) {
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups, int ks,
+    int spp, float *__restrict__ kpart, void *__restrict__ C, int c_dt) {
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
     static_assert(64 * KW == 512, "two threads per table entry");
     static_assert(MB == 1 || (MB == 2 && SR == 4), "two blocks of full rows");
@@ -111,8 +121,11 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     constexpr int kScaleStride = P * 16 + 2;
     __shared__ float scl[2][kScaleRows * kScaleStride];
     const int G = gridDim.x;
-    const int my_chunks = (groups - (int)blockIdx.x + G - 1) / G;
+    // With K parts the grid is exactly groups * ks workgroups of one chunk.
+    const int my_chunks = ks > 1 ? 1 : (groups - (int)blockIdx.x + G - 1) / G;
     if (my_chunks <= 0) return;  // uniform over the workgroup
+    const int kpart_ix = ks > 1 ? (int)blockIdx.x / groups : 0;
+    const uint32_t grp0 = (uint32_t)blockIdx.x - (uint32_t)(kpart_ix * groups);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -126,7 +139,12 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const int j = lane & 15;
     const int g = lane >> 4;
     const int nseg = (K + 127) >> 7;
-    const int spw = (nseg + KW - 1) / KW;  // segment slots per wave per chunk
+    // This workgroup's part: segments seg0 .. seg0 + seg_lim - 1 of each row
+    // (all of them without K parts, spp == nseg).  Slots index segments of
+    // the part; slots at or past seg_lim read zeros.
+    const int seg0 = kpart_ix * spp;
+    const int seg_lim = nseg - seg0 < spp ? nseg - seg0 : spp;
+    const int spw = (spp + KW - 1) / KW;  // segment slots per wave per chunk
     const uint32_t row_bytes = (uint32_t)K >> 1;
     // Workgroups start their walk along K at different slots (whole scale
     // periods), chosen by b / 8 so that the workgroups on one XCD do too:
@@ -146,7 +164,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // group q is q + tr*groups, so at any time neighbouring workgroups read
     // neighbouring 16-row tiles.  Slot q of wave w is segment w + q*KW (the
     // waves of a workgroup read 64*KW contiguous bytes of each row at a time).
-    auto group_of = [&](int c) { return (uint32_t)blockIdx.x + (uint32_t)c * (uint32_t)G; };
+    auto group_of = [&](int c) { return grp0 + (uint32_t)c * (uint32_t)G; };
     const uint32_t w_tile_step = 16u * (uint32_t)groups * row_bytes;
     // The lane's part of a weight offset, and the shift from a segment to its
     // offset.  Row-major: segment s of row n is the 64 bytes at
@@ -166,8 +184,9 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // serves far worse (40 against 28 us at M = 1 on the FFN): there each lane
     // loads its own 16 bytes and one v_permlane32_swap pair regroups them.
     const uint32_t w_lane =
-        WL ? (lane < 32 ? 16u * (uint32_t)lane : 16u * (uint32_t)(lane - 32) + 8u)
-           : (uint32_t)j * row_bytes + 16u * (uint32_t)g;
+        (WL ? (lane < 32 ? 16u * (uint32_t)lane : 16u * (uint32_t)(lane - 32) + 8u)
+            : (uint32_t)j * row_bytes + 16u * (uint32_t)g) +
+        ((uint32_t)seg0 << (WL ? 10 : 6));
     const int seg_sh = WL ? 10 : 6;
 
     // Weight issue cursor: the (chunk, slot) whose loads are issued next.
@@ -180,7 +199,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     int iqr = rot;  // (iq + rot) % spw, kept incrementally (no division per slot)
     auto w_seek = [&]() {
         const int seg = wave + iqr * KW;
-        w_live = ic < my_chunks && seg < nseg;
+        w_live = ic < my_chunks && seg < seg_lim;
         w_row0 = group_of(ic) * 16 * row_bytes + ((uint32_t)seg << seg_sh) + w_lane;
     };
     auto w_advance = [&]() {
@@ -214,6 +233,10 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const int s_row = tid / (4 * P);
     const uint32_t s_piece = (uint32_t)(tid % (4 * P)) * 16;
     const uint32_t s_win = (uint32_t)(P * KW * 128 * 4) >> bs_log2;  // bytes per row per period
+    // The part's scales: from its first block to the end of its last one.
+    const uint32_t s_first = ((uint32_t)seg0 * 128 >> bs_log2) * 4;
+    const uint32_t s_blocks_end = ((uint32_t)(seg0 + seg_lim) * 128 + (1u << bs_log2) - 1) >> bs_log2;
+    const uint32_t s_end = (s_blocks_end < nb ? s_blocks_end : nb) * 4;
     int sc = 0, sq = 0;  // scale cursor: the first slot of the period loaded next
     int sqr = rot;       // (sq + rot) % spw
     // Bytes of this thread's piece that lie inside the row (a piece may run
@@ -237,9 +260,9 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     };
     scale_rows();
     auto load_scales = [&](floatx4 (&out)[SP]) {
-        const uint32_t w0 = ((uint32_t)sqr * KW * 128 >> bs_log2) * 4;  // window start
-        const bool live = sc < my_chunks && w0 + s_piece < nb * 4;
-        s_rem = (int)(nb * 4) - (int)(w0 + s_piece);
+        const uint32_t w0 = s_first + ((uint32_t)sqr * KW * 128 >> bs_log2) * 4;  // window start
+        const bool live = sc < my_chunks && w0 + s_piece < s_end;
+        s_rem = (int)s_end - (int)(w0 + s_piece);
 #pragma unroll
         for (int i = 0; i < SP; ++i) {
             const uint32_t so = live ? s_rowoff[i] + w0 : kPastEnd;
@@ -294,11 +317,13 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint32_t a_lane = (uint32_t)j * (uint32_t)K * 2 +  // past the end of A for j >= M
                             2u * (32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1));
     uint4 anext[MB][4];
-    auto load_a = [&](int qr) {  // qr: the slot's index along the row, (q + rot) % spw
-        const uint32_t kk = ((uint32_t)wave + (uint32_t)qr * KW) * 128;
+    auto load_a = [&](int qr) {  // qr: the slot's index along the part, (q + rot) % spw
+        const int ls = wave + qr * KW;  // segment of the part
+        const uint32_t kk = (uint32_t)(seg0 + ls) * 128;
         const uint32_t base = a_lane + 2u * kk;
-        const uint32_t lo = kk + 64 <= (uint32_t)K ? base : kPastEnd;
-        const uint32_t hi = kk + 128 <= (uint32_t)K ? base : kPastEnd;
+        const bool in = ls < seg_lim;
+        const uint32_t lo = in && kk + 64 <= (uint32_t)K ? base : kPastEnd;
+        const uint32_t hi = in && kk + 128 <= (uint32_t)K ? base : kPastEnd;
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
             const uint32_t bo = (uint32_t)(16 * b) * (uint32_t)K * 2;
@@ -566,8 +591,12 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                     const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
                     const int tok = 16 * b + 4 * g + r;
                     if (n < N && tok < M) {
-                        if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
-                        store_elem(C, (size_t)tok * N + n, v, c_dt);
+                        if (MB == 1 && ks > 1) {
+                            kpart[((size_t)kpart_ix * M + tok) * N + n] = v;  // this part's sum
+                        } else {
+                            if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
+                            store_elem(C, (size_t)tok * N + n, v, c_dt);
+                        }
                     }
                 }
             }
@@ -584,10 +613,51 @@ int tiles_per_chunk(int N) {
     return tb > 8 ? 8 : tb;
 }
 
+// Work plan: tiles per chunk (tb), K parts (ks) of spp segments each.
+struct SkinnyPlan {
+    int tb, ks, spp;
+};
+
+// Without K parts a workgroup walks ceil(groups / CUs) chunks of tb tiles
+// times ceil(segments / 8) slots.  With up to 16 token rows, K parts are
+// used when some (tb, ks) with groups * ks <= CUs (one chunk per workgroup)
+// saves at least 8 units per wave and 20 % of them: the second launch that
+// adds the parts costs about as much as 4 units (a unit is ~0.42 us at
+// 17408 x 5120), so 17408 x 5120 goes from 34 to 24 units per wave while
+// 5120 x 5120 (10 to 7) keeps one part.  Parts are whole slots of the 8
+// waves (spp a multiple of 8 segments), so every part starts on a scale
+// block boundary for blocksizes up to 1024.
+SkinnyPlan skinny_plan(int M, int N, int K) {
+    const int tb0 = tiles_per_chunk(N);
+    const int nseg = (K + 127) / 128;
+    SkinnyPlan plan{tb0, 1, nseg};
+    if (M > 16) return plan;  // two token blocks: one part
+    const int tiles = (N + 15) / 16;
+    const int cus = device_info().num_cus;
+    const long groups0 = (tiles + tb0 - 1) / tb0;
+    const long base = (groups0 + cus - 1) / cus * tb0 * ((nseg + KW - 1) / KW);
+    long best = base;
+    for (int tb = 1; tb <= 8; ++tb)
+        for (int ks = 2; ks <= 8; ++ks) {
+            const int per = (nseg + ks - 1) / ks;
+            const int spp = (per + KW - 1) / KW * KW;
+            if ((nseg + spp - 1) / spp != ks) continue;  // fewer parts than asked
+            const long groups = (tiles + tb - 1) / tb;
+            if (groups * ks > cus) continue;
+            const long units = (long)tb * (spp / KW);
+            if (units + 8 <= base && units * 100 <= base * 80 && units < best) {
+                best = units;
+                plan = SkinnyPlan{tb, ks, spp};
+            }
+        }
+    return plan;
+}
+
 template <int SR, int MB, int TB>
 hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
-                     void *C, int c_dt, int groups, int G, int wl, hipStream_t s) {
+                     void *C, int c_dt, int groups, int G, const SkinnyPlan &plan, float *kpart,
+                     int wl, hipStream_t s) {
     // Ring depth TB*RS of about 8 units (8 KiB of weights in flight per wave).
     constexpr int RS = TB == 1 ? 8 : TB == 2 ? 4 : TB <= 4 ? 2 : 1;
     constexpr int UF = (RS * TB) % 2 == 0 ? RS : 2 * RS;
@@ -599,11 +669,13 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // The ring entry and decode buffer of a chunk's first unit are fixed at
     // compile time: a workgroup with several chunks needs chunks of whole
     // loop iterations.
-    const int spw = ((K + 127) / 128 + KW - 1) / KW;
+    const int spw = (plan.spp + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
+    if (plan.ks > 1 && (MB != 1 || G != groups * plan.ks || !kpart)) return hipErrorInvalidValue;
 #define Q4_LAUNCH_KERNEL(B, L)                                                          \
     fused_mfma_kernel<SR, TB, RS, UF, P, MB, B, L><<<dim3(G), dim3(64 * KW), 0, s>>>( \
-        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, C, c_dt)
+        A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, plan.ks, plan.spp, kpart, C, \
+        c_dt)
     if (bs_log2 == 6) {
         if (wl) Q4_LAUNCH_KERNEL(true, 1);
         else Q4_LAUNCH_KERNEL(true, 0);
@@ -612,24 +684,29 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
         else Q4_LAUNCH_KERNEL(false, 0);
     }
 #undef Q4_LAUNCH_KERNEL
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.ks == 1) return e;
+    return launch_sum_planes(kpart, plan.ks, M, N, bias, C, c_dt, s);
 }
 
 template <int SR, int MB>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
-                     void *C, int c_dt, int wl, hipStream_t s) {
+                     void *C, int c_dt, float *kpart, int wl, hipStream_t s) {
     // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS).
     // TB = the tiles each CU must cover, up to 8, so that every chunk but the
     // last holds TB live tiles; a workgroup loops over ceil(groups / CUs)
-    // chunks.
-    const int tb = tiles_per_chunk(N);
+    // chunks.  With K parts (a buffer given and the plan asks for them) the
+    // grid is groups * ks workgroups of one chunk each.
+    SkinnyPlan plan = SkinnyPlan{tiles_per_chunk(N), 1, (K + 127) / 128};
+    if (kpart) plan = skinny_plan(M, N, K);
+    const int tb = plan.tb;
     const int tiles = (N + 15) / 16;
     const int cus = device_info().num_cus;
     const int groups = (tiles + tb - 1) / tb;
-    const int G = groups < cus ? groups : cus;
+    const int G = plan.ks > 1 ? groups * plan.ks : groups < cus ? groups : cus;
 #define Q4_LAUNCH_TB(T) \
-    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, wl, s)
+    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, plan, kpart, wl, s)
     switch (tb) {
     case 1: Q4_LAUNCH_TB(1);
     case 2: Q4_LAUNCH_TB(2);
@@ -656,6 +733,8 @@ bool q4_fused_mfma_two_blocks(int N) { return tiles_per_chunk(N) < 8; }
 
 int q4_fused_tiles_per_chunk(int N) { return tiles_per_chunk(N); }
 
+int q4_fused_kparts(int M, int N, int K) { return skinny_plan(M, N, K).ks; }
+
 bool q4_fused_mfma_fits(int M, int N, int K) {
     (void)M;
     return ((uint64_t)N + 256) * (uint64_t)K / 2 < (1ull << 32) &&
@@ -665,12 +744,12 @@ bool q4_fused_mfma_fits(int M, int N, int K) {
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt, int wl,
-                                hipStream_t s) {
+                                hipStream_t s, float *kpart) {
     if (a_dt != kBf16 || M > 32 || (wl && (N % 16 != 0 || K % 128 != 0)))
         return hipErrorInvalidValue;
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
 #define Q4_LAUNCH_SR(R, B) \
-    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, wl, s)
+    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, kpart, wl, s)
     if (M <= 1) Q4_LAUNCH_SR(1, 1);
     if (M <= 2) Q4_LAUNCH_SR(2, 1);
     if (M <= 16) Q4_LAUNCH_SR(4, 1);
@@ -686,12 +765,12 @@ hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
 // vector-ALU kernel in passes of 16 rows.
 hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, const void *bias, int M, int N, int K,
-                           int bs_log2, void *C, int c_dt, int wl, hipStream_t s) {
+                           int bs_log2, void *C, int c_dt, int wl, hipStream_t s, float *kpart) {
     const bool mfma = a_dt == kBf16 && bs_log2 >= 6 && q4_fused_mfma_fits(M, N, K);
     if (wl && !mfma) return hipErrorInvalidValue;  // the vector-ALU kernel reads rows
     if (mfma && (M <= 16 || tiles_per_chunk(N) < 8))
         return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
-                                    C, c_dt, wl, s);
+                                    C, c_dt, wl, s, M <= 16 ? kpart : nullptr);
     const size_t a_row = (size_t)K * (a_dt == kF32 ? 4 : 2);
     const size_t c_row = (size_t)N * (c_dt == kF32 ? 4 : 2);
     for (int m0 = 0; m0 < M; m0 += 16) {
@@ -700,7 +779,7 @@ hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, cons
         void *Cm = static_cast<char *>(C) + (size_t)m0 * c_row;
         const hipError_t e =
             mfma ? launch_q4_fused_mfma(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
-                                        Cm, c_dt, wl, s)
+                                        Cm, c_dt, wl, s, nullptr)
                  : launch_q4_fused_simt(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
                                         Cm, c_dt, s);
         if (e != hipSuccess) return e;

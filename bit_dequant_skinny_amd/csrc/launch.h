@@ -32,21 +32,26 @@ hipError_t launch_bf16_repack_tiles(const uint16_t *W, uint16_t *Wtiles, int N, 
 // Fused 4-bit GEMM, C = A * dequant(W)^T (+ bias), A of type a_dt, bias and C
 // of type c_dt.  Dispatches to the matrix-core kernel (bf16 or fp16
 // activations, blocksize >= 64) or the vector-ALU kernel (blocksize 32, fp32
-// activations, offsets beyond 32 bits).
+// activations, offsets beyond 32 bits).  kpart: room for
+// q4_fused_kparts(M, N, K) * M * N fp32 partial sums, which lets the skinny
+// kernel split K over workgroups (then a second kernel adds the parts).
 hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, const float *absmax,
                            const float *codebook, const void *bias, int M, int N, int K,
-                           int bs_log2, void *C, int c_dt, int wl, hipStream_t s);
+                           int bs_log2, void *C, int c_dt, int wl, hipStream_t s,
+                           float *kpart = nullptr);
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt, int wl,
-                                hipStream_t s);
+                                hipStream_t s, float *kpart = nullptr);
+// K parts the skinny kernel would use for M bf16 token rows (1 = none).
+int q4_fused_kparts(int M, int N, int K);
 hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt,
                                 hipStream_t s);
 
 // fp16 / fp32 activations as 2 / 3 exact bf16 planes ([np][n]) and the sum of
-// np (2..4) fp32 partials ([np][M][N]) plus bias, rounded once to c_dt.
+// np (2..8) fp32 partials ([np][M][N]) plus bias, rounded once to c_dt.
 int activation_planes(int a_dt);
 hipError_t launch_split_planes(const void *A, int a_dt, size_t n, uint16_t *planes,
                                hipStream_t s);

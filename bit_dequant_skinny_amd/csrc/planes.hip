@@ -60,9 +60,9 @@ __global__ __launch_bounds__(kThreads) void sum_planes_kernel(const float *__res
                                                                void *__restrict__ C, int c_dt) {
     for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < mn;
          i += (size_t)gridDim.x * kThreads) {
-        float v = P[i] + P[mn + i];
-        if constexpr (NP >= 3) v += P[2 * mn + i];
-        if constexpr (NP >= 4) v += P[3 * mn + i];
+        float v = P[i];
+#pragma unroll
+        for (int q = 1; q < NP; ++q) v += P[q * mn + i];  // in slab order
         if (bias) v += load_elem(bias, i % (size_t)N, c_dt);  // before the single rounding
         store_elem(C, i, v, c_dt);
     }
@@ -91,10 +91,18 @@ hipError_t launch_sum_planes(const float *P, int np, int M, int N, const void *b
                              int c_dt, hipStream_t s) {
     const size_t mn = (size_t)M * (size_t)N;
     if (mn == 0) return hipSuccess;
-    if (np == 4) sum_planes_kernel<4><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
-    else if (np == 3) sum_planes_kernel<3><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
-    else if (np == 2) sum_planes_kernel<2><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt);
-    else return hipErrorInvalidValue;
+#define Q4_SUM(NP) sum_planes_kernel<NP><<<grid_for(mn), kThreads, 0, s>>>(P, mn, N, bias, C, c_dt)
+    switch (np) {
+    case 2: Q4_SUM(2); break;
+    case 3: Q4_SUM(3); break;
+    case 4: Q4_SUM(4); break;
+    case 5: Q4_SUM(5); break;
+    case 6: Q4_SUM(6); break;
+    case 7: Q4_SUM(7); break;
+    case 8: Q4_SUM(8); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef Q4_SUM
     return hipGetLastError();
 }
 

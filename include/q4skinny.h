@@ -405,6 +405,21 @@ q4_status q4_set_crossover_m(int m);
  */
 q4_status q4_set_crossover_shape(int N, int K, int m);
 int q4_get_crossover_shape(int N, int K);
+
+/*
+ * q4_skinny_kparts: how many parts the fused skinny kernel cuts K into for
+ * M bf16 token rows (1..16) and an N x K weight on the current device (1 =
+ * none; 1 for arguments outside those ranges).  The pages' kernel gives each
+ * output row to one thread group over all of K (bitsandbytes pull request
+ * "[ROCm] Optimize kgemm_4bit_inference_naive ...", section "Technical
+ * details"); here a row's K may be split over workgroups when the 16-row
+ * tiles alone would leave compute units idle (N = 5120: 320 tiles on 256
+ * CUs) and the split saves enough of each workgroup's walk to pay for a
+ * second launch: the parts' fp32 sums go to the per-stream workspace (or
+ * the fixed scratch of the allocation-free entry point) and a second kernel
+ * adds them in part order, adds the bias and rounds once (deterministic).
+ */
+int q4_skinny_kparts(int M, int N, int K);
 q4_status q4_clear_crossover_shapes(void);
 
 /*

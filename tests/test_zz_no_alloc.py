@@ -58,14 +58,16 @@ def _case(M, N, K, bs, adt, cdt, path, with_bias, config):
 
 
 # (M, N, K, adt, cdt, path, bias): the fp16 / fp32 activation planes, the
-# split path's dequantized weights, the tiled kernel's fp32 K parts, and a
-# call that needs no scratch at all.
+# split path's dequantized weights, the tiled kernel's fp32 K parts, a call
+# that needs no scratch at all, and the skinny kernel's K parts.
 CASES = [
     ((8, 600, 2048, "fp32", "fp32", "auto", True), (3, 200, 1024, "fp32", "fp32", "auto", True)),
     ((5, 512, 1536, "fp16", "bf16", "auto", True), (2, 96, 512, "fp16", "fp16", "auto", False)),
     ((16, 1024, 2048, "bf16", "bf16", "split", False), (4, 256, 1024, "bf16", "bf16", "split", False)),
     ((200, 256, 4096, "bf16", "bf16", "fused", True), (70, 128, 2048, "bf16", "bf16", "fused", True)),
     ((4, 1024, 4096, "bf16", "bf16", "fused", False), (1, 512, 1024, "bf16", "bf16", "fused", False)),
+    # the skinny kernel's K parts: their fp32 sums in the array
+    ((4, 1536, 16384, "bf16", "bf16", "fused", True), (1, 1536, 16448, "bf16", "fp32", "fused", False)),
 ]
 
 
