@@ -13,13 +13,17 @@
 // in fp64), the code is the number of i with m_i * absmax < w.  That product
 // is exact in fp64; the kernel rounds it up to U_i, the smallest fp32 above
 // it, once per block, after which "m_i * absmax < w" is exactly "w >= U_i" for
-// every fp32 w: fifteen fp32 compares per weight.
+// every fp32 w.  The U_i do not decrease with i, so "w >= U_i" holds for a
+// prefix of i and the code (the length of that prefix) is found by a binary
+// search: four compares per weight, each against a threshold picked by the
+// earlier answers.
 //
 // Layout: one lane takes 8 consecutive weights (one packed 32-bit word of
-// codes); bs/8 neighbouring lanes hold one block (K % bs == 0, so blocks of
-// the flattened matrix are blocks of its rows) and combine their maxima with
-// a butterfly of lane swaps.  HBM-bound for fp32 input (4.5 bytes per
-// weight); for 16-bit inputs the compares bound it.
+// codes); LPB = bs/8 neighbouring lanes hold one block (K % bs == 0, so
+// blocks of the flattened matrix are blocks of its rows), combine their
+// maxima with a butterfly of lane swaps, and share the work of the fifteen
+// thresholds: lane q of a block computes U_i for i = q mod LPB and reads the
+// others from its neighbours.
 #include "device.h"
 #include "launch.h"
 
@@ -65,12 +69,33 @@ __device__ __forceinline__ void load8w(const void *W, uint64_t word, float (&w)[
     }
 }
 
-template <int WT>
+// Value select (a conditional on two array elements would select their
+// addresses and index the array, which then lives in scratch memory).
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
+
+// Number of i in 0..14 with x >= U[i], for non-decreasing U (NaN: 0).
+__device__ __forceinline__ uint32_t code_of(float x, const float (&U)[15]) {
+    const bool b3 = x >= U[7];
+    const bool b2 = x >= sel(b3, U[11], U[3]);
+    const bool b1 = x >= sel(b3, sel(b2, U[13], U[9]), sel(b2, U[5], U[1]));
+    const float t0 = sel(b3, sel(b2, sel(b1, U[14], U[12]), sel(b1, U[10], U[8])),
+                         sel(b2, sel(b1, U[6], U[4]), sel(b1, U[2], U[0])));
+    const bool b0 = x >= t0;
+    return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+template <int WT, int LPB>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const void *__restrict__ W, uint64_t words, int bs_log2, QuantizeTable tab,
+    const void *__restrict__ W, uint64_t words, QuantizeTable tab,
     uint32_t *__restrict__ packed, float *__restrict__ absmax) {
+    constexpr int lpb = LPB;  // lanes per block (4..32)
+    constexpr int bs_log2 = LPB == 4 ? 5 : LPB == 8 ? 6 : LPB == 16 ? 7 : 8;
+    constexpr int S = (15 + LPB - 1) / LPB;  // thresholds each lane computes
+    __shared__ double s_mid[16];
+    if (threadIdx.x < 15) s_mid[threadIdx.x] = tab.mid[threadIdx.x];
+    __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int lpb = 1 << (bs_log2 - 3);  // lanes per block (4..32)
+    const int q = lane & (LPB - 1), base_lane = lane & ~(LPB - 1);
     const uint64_t wave = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     const uint64_t nwaves = (uint64_t)gridDim.x * (kThreads / 64);
     // The loop bound is uniform across the wave (64 words = 512 weights, a
@@ -89,19 +114,22 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(w[j]));
         for (int off = 1; off < lpb; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+        // U[i] is computed by lane i % LPB of the block (every lane runs the
+        // shuffles, so they happen with all lanes on)
+        float mine[S];
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            const int i = q + LPB * k;
+            mine[k] = i < 15 ? next_fp32_above(s_mid[i] * (double)a) : 0.f;
+        }
+        float U[15];
+#pragma unroll
+        for (int i = 0; i < 15; ++i) U[i] = __shfl(mine[i / LPB], base_lane + i % LPB, 64);
         uint32_t out;
         if (a > 0.f) {
-            float U[15];
-#pragma unroll
-            for (int i = 0; i < 15; ++i) U[i] = next_fp32_above(tab.mid[i] * (double)a);
             out = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint32_t c = 0;
-#pragma unroll
-                for (int i = 0; i < 15; ++i) c += w[j] >= U[i] ? 1u : 0u;
-                out |= c << (4 * j);
-            }
+            for (int j = 0; j < 8; ++j) out |= code_of(w[j], U) << (4 * j);
         } else {
             out = tab.zero_code * 0x11111111u;
         }
@@ -125,15 +153,25 @@ hipError_t launch_quantize(const void *W, int w_dt, int N, int K, int bs_log2,
     if (blocks > cap) blocks = cap;
     if (blocks == 0) blocks = 1;
     uint32_t *packed = reinterpret_cast<uint32_t *>(Wpacked);
-    if (w_dt == kF32)
-        quantize_kernel<kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            W, words, bs_log2, tab, packed, absmax);
-    else if (w_dt == kF16)
-        quantize_kernel<kF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            W, words, bs_log2, tab, packed, absmax);
-    else
-        quantize_kernel<kBf16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            W, words, bs_log2, tab, packed, absmax);
+#define Q4_QUANT(T, L) \
+    quantize_kernel<T, L><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(W, words, tab, packed, absmax)
+#define Q4_QUANT_BS(T)                         \
+    switch (bs_log2) {                         \
+    case 5: Q4_QUANT(T, 4); break;             \
+    case 6: Q4_QUANT(T, 8); break;             \
+    case 7: Q4_QUANT(T, 16); break;            \
+    case 8: Q4_QUANT(T, 32); break;            \
+    default: return hipErrorInvalidValue;      \
+    }
+    if (w_dt == kF32) {
+        Q4_QUANT_BS(kF32)
+    } else if (w_dt == kF16) {
+        Q4_QUANT_BS(kF16)
+    } else {
+        Q4_QUANT_BS(kBf16)
+    }
+#undef Q4_QUANT_BS
+#undef Q4_QUANT
     return hipGetLastError();
 }
 
