@@ -632,7 +632,8 @@ def copy_probe(d, nbytes=1 << 30):
 def profile_case(d, which, launches=12):
     """A few launches of one call for counter and trace runs: the split path
     (dequantize + bf16 GEMM) on the FFN at M = 16 and 256, or the bf16 skinny
-    GEMM on the 248320 x 2560 projection at M = 1 (row-major or tile layout);
+    GEMM on the 248320 x 2560 projection at M = 1 (row-major or tile layout),
+    or the fused skinny kernel with K parts on 5120 x 17408 at M = 1;
     weights rotate as in the timed runs."""
     import bit_dequant_skinny_amd as q4
     t = d.t
@@ -647,6 +648,18 @@ def profile_case(d, which, launches=12):
         for i in range(launches):
             Wp, am = sets[i % len(sets)]
             q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path="split")
+    elif which == "kparts":
+        # the skinny kernel with K split over workgroups, then the part sum
+        N, K, M = 5120, 17408, 1
+        p = synth.q4_problem(1, N, K, BS, config=2, shape=2)
+        sets = d.copies((q4.q4_repack_tiles(d.raw(p["Wpacked"])), d.raw(p["absmax"])),
+                        q4_bytes(1, N, K))
+        cb = d.raw(p["codebook"])
+        A = d.bf16(synth.activations_bf16(M, K, synth.seed(2, 2, 10 * M + 1)))
+        C = t.empty((M, N), dtype=t.bfloat16, device=d.dev)
+        for i in range(launches):
+            Wt, am = sets[i % len(sets)]
+            q4.q4_gemm_skinny(A, Wt, am, cb, BS, out=C, layout="tiles")
     elif which in ("bf16c5", "bf16c5tiles"):
         N, K, M = 248320, 2560, 1
         W = d.bf16(synth.bf16_weights(N, K, synth.seed(4, 1, 2)))
@@ -676,7 +689,8 @@ def main():
                     help="packed-weight layout of the timed step (q4_repack_tiles or row-major)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel (counter calibration)")
-    ap.add_argument("--profile-case", choices=("split16", "split256", "bf16c5", "bf16c5tiles"),
+    ap.add_argument("--profile-case",
+                    choices=("split16", "split256", "bf16c5", "bf16c5tiles", "kparts"),
                     help="only run a few launches of one call (for rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1:
