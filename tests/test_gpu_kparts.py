@@ -47,13 +47,13 @@ def _problem(M, N, K, bs, config):
 @pytest.mark.parametrize("layout", ["rows", "tiles"])
 @pytest.mark.parametrize("M,N,K,bs", [
     (1, 1536, 16384, 64), (4, 1536, 16384, 64), (16, 768, 32768, 64), (1, 1536, 16448, 64),
-    (3, 1536, 16512, 128), (2, 1536, 16384, 256), (5, 768, 32768, 64),
+    (3, 1536, 16512, 128), (2, 1536, 16384, 256), (5, 768, 32768, 64), (2, 1544, 16384, 64),
 ])
 def test_kparts_parity(M, N, K, bs, layout):
     g = _gpu()
     assert q4.q4_skinny_kparts(M, N, K) > 1
-    if layout == "tiles" and K % 128:
-        pytest.skip("the tile layout needs K % 128 == 0")
+    if layout == "tiles" and (K % 128 or N % 16):
+        pytest.skip("the tile layout needs K % 128 == 0 and N % 16 == 0")
     p, (A, Wp, am, cb) = _problem(M, N, K, bs, 700 + M)
     W = q4.q4_repack_tiles(Wp) if layout == "tiles" else Wp
     C = q4.q4_gemm_skinny(A, W, am, cb, bs, path="fused", layout=layout)
