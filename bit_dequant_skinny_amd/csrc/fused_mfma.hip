@@ -34,8 +34,13 @@
 // by loading the two 8-byte halves in place) so that every MFMA step draws
 // from a single 64-wide block, which keeps the absmax scaling exact per
 // block.
-// Tokens feed the A operand (lane % 16 = token; lanes of tokens >= M are
-// computed and discarded).
+// Tokens feed the A operand, one per row; rows without a token read zeros
+// and their outputs are discarded.  Output row 4g + r of an MFMA lands in
+// lane group g, accumulator r, so with one token block token t takes row
+// 4 (t % 4) + t / 4: up to 4 tokens then need one accumulator per lane
+// (SR = 1), up to 8 two, up to 16 four, which saves the scaling and the
+// cross-wave sums of the empty rows.  Two token blocks (up to 32 tokens)
+// keep token t at row t of block t / 16.
 //
 // Schedule.  One persistent 8-wave workgroup per CU.  Tiles form groups of
 // TB (1..8, the tiles each CU must cover, chosen per shape so that only the
@@ -88,7 +93,7 @@ constexpr int KW = 8;  // waves per workgroup
 
 // Activations are bf16 (fp16 and fp32 activations reach this kernel as
 // exact bf16 planes).  SR: accumulator rows kept per lane
-// (min(M, 4)).  TB: tiles per chunk.  RS:
+// (ceil(M / 4) rounded up to 1, 2 or 4).  TB: tiles per chunk.  RS:
 // segment slots the weight ring runs ahead, so every wave keeps TB*RS weight
 // loads in flight.  UF: slots per loop iteration, a multiple of RS with UF*TB
 // even, which makes the ring entry and the decode double-buffer index of
@@ -314,7 +319,9 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // the four loads.  K is a multiple of 64 here: dwords 0, 1 (k < kk + 64)
     // are live when kk + 64 <= K and dwords 2, 3 when kk + 128 <= K, the same
     // for every lane.
-    const uint32_t a_lane = (uint32_t)j * (uint32_t)K * 2 +  // past the end of A for j >= M
+    // token of A row j (past the end of A when it is >= M)
+    const uint32_t tok_j = MB == 1 ? 4u * (uint32_t)(j & 3) + (uint32_t)(j >> 2) : (uint32_t)j;
+    const uint32_t a_lane = tok_j * (uint32_t)K * 2 +
                             2u * (32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1));
     uint4 anext[MB][4];
     auto load_a = [&](int qr) {  // qr: the slot's index along the part, (q + rot) % spw
@@ -589,7 +596,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
 #pragma unroll
                     for (int w2 = 1; w2 < KW; ++w2) v += red[w2][p][lane];
                     const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
-                    const int tok = 16 * b + 4 * g + r;
+                    const int tok = MB == 1 ? 4 * r + g : 16 * b + 4 * g + r;
                     if (n < N && tok < M) {
                         if (MB == 1 && ks > 1) {
                             kpart[((size_t)kpart_ix * M + tok) * N + n] = v;  // this part's sum
@@ -750,8 +757,8 @@ hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
 #define Q4_LAUNCH_SR(R, B) \
     return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, kpart, wl, s)
-    if (M <= 1) Q4_LAUNCH_SR(1, 1);
-    if (M <= 2) Q4_LAUNCH_SR(2, 1);
+    if (M <= 4) Q4_LAUNCH_SR(1, 1);
+    if (M <= 8) Q4_LAUNCH_SR(2, 1);
     if (M <= 16) Q4_LAUNCH_SR(4, 1);
     Q4_LAUNCH_SR(4, 2);
 #undef Q4_LAUNCH_SR
