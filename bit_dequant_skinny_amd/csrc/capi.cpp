@@ -433,6 +433,23 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
     if (st != Q4_OK) return st;
     const int np = q4::activation_planes(a_dt);
     const int rows = np * M;
+    // Few tokens (np planes per group of 4 tokens fit one lane's 4 output
+    // rows): the skinny kernel adds each token's planes itself, so no fp32
+    // partials and no second pass.
+    if (np * ((M + 3) / 4) <= 4 && q4::q4_fused_mfma_fits(rows, N, K)) {
+        void *ws = nullptr;
+        st = workspace(device, s, (size_t)rows * (size_t)K * 2, &ws);
+        if (st != Q4_OK) return st;
+        uint16_t *planes = static_cast<uint16_t *>(ws);
+        st = launch_checked("planes", [&] {
+            return q4::launch_split_planes(A, a_dt, (size_t)M * (size_t)K, planes, s);
+        });
+        if (st != Q4_OK) return st;
+        return launch_checked("fused", [&] {
+            return q4::launch_q4_fused_mfma(planes, Q4_DTYPE_BF16, Wp, am, cb, bias, M, N, K,
+                                            bs_log2, C, c_dt, wl, s, nullptr, np);
+        });
+    }
     const bool tiled = fused_tiled(rows, N, K, bs_log2);
     // at most 4 partial slabs in all (planes times K parts)
     const q4::TiledPlan plan =

@@ -40,7 +40,10 @@
 // 4 (t % 4) + t / 4: up to 4 tokens then need one accumulator per lane
 // (SR = 1), up to 8 two, up to 16 four, which saves the scaling and the
 // cross-wave sums of the empty rows.  Two token blocks (up to 32 tokens)
-// keep token t at row t of block t / 16.
+// keep token t at row t of block t / 16.  fp16 / fp32 activations arrive as
+// NP = 2 / 3 exact bf16 planes ([NP][M][K]); plane p of token t then takes
+// row 4 (t % 4) + NP (t / 4) + p, so a token's planes land in one lane and
+// are added there, in plane order, before the bias and the rounding.
 //
 // Schedule.  One persistent 8-wave workgroup per CU.  Tiles form groups of
 // TB (1..8, the tiles each CU must cover, chosen per shape so that only the
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
     const void *__restrict__ bias, int M, int N, int K, int bs_log2, int groups, int ks,
-    int spp, float *__restrict__ kpart, void *__restrict__ C, int c_dt) {
+    int spp, float *__restrict__ kpart, void *__restrict__ C, int c_dt, int np) {
     static_assert(UF % RS == 0 && (UF * TB) % 2 == 0, "static ring and decode-buffer indices");
     static_assert(64 * KW == 512, "two threads per table entry");
     static_assert(MB == 1 || (MB == 2 && SR == 4), "two blocks of full rows");
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
 
     const __amdgpu_buffer_rsrc_t wres = make_rsrc(Wp, (uint32_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t sres = make_rsrc(absmax, (uint32_t)N * nb * 4);
-    const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
+    const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)(np * M) * (uint32_t)K * 2);
 
     // Chunk c of this workgroup is tile group blockIdx.x + c*G; tile tr of
     // group q is q + tr*groups, so at any time neighbouring workgroups read
@@ -319,9 +322,12 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // the four loads.  K is a multiple of 64 here: dwords 0, 1 (k < kk + 64)
     // are live when kk + 64 <= K and dwords 2, 3 when kk + 128 <= K, the same
     // for every lane.
-    // token of A row j (past the end of A when it is >= M)
-    const uint32_t tok_j = MB == 1 ? 4u * (uint32_t)(j & 3) + (uint32_t)(j >> 2) : (uint32_t)j;
-    const uint32_t a_lane = tok_j * (uint32_t)K * 2 +
+    // A row j = 4 (t % 4) + np q + p holds plane p of token t (q = t / 4);
+    // rows without a token read past the end of A
+    const int j_r = j & 3, j_q = j_r / np, j_p = j_r - j_q * np, tok_j = 4 * j_q + (j >> 2);
+    const uint32_t a_rowoff = MB == 2 ? (uint32_t)j * (uint32_t)K * 2
+                              : tok_j < M ? (uint32_t)(j_p * M + tok_j) * (uint32_t)K * 2 : kPastEnd;
+    const uint32_t a_lane = a_rowoff +
                             2u * (32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1));
     uint4 anext[MB][4];
     auto load_a = [&](int qr) {  // qr: the slot's index along the part, (q + rot) % spw
@@ -587,6 +593,31 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                     acc[tr][b][r] = 0.f;
                 }
             lds_barrier();
+            if (MB == 1 && np > 1) {
+                // output (tile, token group q): each plane's row summed over
+                // the waves in wave order, then the planes in plane order
+                const int qg = SR / np;
+                for (int o0 = 0; o0 < TB * qg; o0 += KW) {
+                    const int o = o0 + wave;
+                    if (o < TB * qg) {
+                        const int tr = o / qg, q = o - tr * qg;
+                        float v = 0.f;
+                        for (int pl = 0; pl < np; ++pl) {
+                            const int p = tr * SR + q * np + pl;
+                            float vp = red[0][p][lane];
+#pragma unroll
+                            for (int w2 = 1; w2 < KW; ++w2) vp += red[w2][p][lane];
+                            v = pl == 0 ? vp : v + vp;
+                        }
+                        const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
+                        const int tok = 4 * q + g;
+                        if (n < N && tok < M) {
+                            if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
+                            store_elem(C, (size_t)tok * N + n, v, c_dt);
+                        }
+                    }
+                }
+            } else {
 #pragma unroll
             for (int p0 = 0; p0 < TB * SR; p0 += KW) {
                 const int p = p0 + wave;
@@ -606,6 +637,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                         }
                     }
                 }
+            }
             }
         }
         if (++pc == my_chunks) break;
@@ -664,7 +696,7 @@ template <int SR, int MB, int TB>
 hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
                      void *C, int c_dt, int groups, int G, const SkinnyPlan &plan, float *kpart,
-                     int wl, hipStream_t s) {
+                     int np, int wl, hipStream_t s) {
     // Ring depth TB*RS of about 8 units (8 KiB of weights in flight per wave).
     constexpr int RS = TB == 1 ? 8 : TB == 2 ? 4 : TB <= 4 ? 2 : 1;
     constexpr int UF = (RS * TB) % 2 == 0 ? RS : 2 * RS;
@@ -678,11 +710,13 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // loop iterations.
     const int spw = (plan.spp + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
-    if (plan.ks > 1 && (MB != 1 || G != groups * plan.ks || !kpart)) return hipErrorInvalidValue;
+    if (plan.ks > 1 && (MB != 1 || G != groups * plan.ks || !kpart || np != 1))
+        return hipErrorInvalidValue;
+    if (np > 1 && MB != 1) return hipErrorInvalidValue;
 #define Q4_LAUNCH_KERNEL(B, L)                                                          \
     fused_mfma_kernel<SR, TB, RS, UF, P, MB, B, L><<<dim3(G), dim3(64 * KW), 0, s>>>( \
         A, Wp, absmax, codebook, bias, M, N, K, bs_log2, groups, plan.ks, plan.spp, kpart, C, \
-        c_dt)
+        c_dt, np)
     if (bs_log2 == 6) {
         if (wl) Q4_LAUNCH_KERNEL(true, 1);
         else Q4_LAUNCH_KERNEL(true, 0);
@@ -699,7 +733,7 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
 template <int SR, int MB>
 hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
                      const float *codebook, const void *bias, int M, int N, int K, int bs_log2,
-                     void *C, int c_dt, float *kpart, int wl, hipStream_t s) {
+                     void *C, int c_dt, float *kpart, int np, int wl, hipStream_t s) {
     // One 8-wave workgroup per CU (the replicated table takes 64 KiB of LDS).
     // TB = the tiles each CU must cover, up to 8, so that every chunk but the
     // last holds TB live tiles; a workgroup loops over ceil(groups / CUs)
@@ -713,7 +747,7 @@ hipError_t launch_sr(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     const int groups = (tiles + tb - 1) / tb;
     const int G = plan.ks > 1 ? groups * plan.ks : groups < cus ? groups : cus;
 #define Q4_LAUNCH_TB(T) \
-    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, plan, kpart, wl, s)
+    return launch_tb<SR, MB, T>(A, Wp, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, groups, G, plan, kpart, np, wl, s)
     switch (tb) {
     case 1: Q4_LAUNCH_TB(1);
     case 2: Q4_LAUNCH_TB(2);
@@ -751,15 +785,18 @@ bool q4_fused_mfma_fits(int M, int N, int K) {
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt, int wl,
-                                hipStream_t s, float *kpart) {
+                                hipStream_t s, float *kpart, int np) {
     if (a_dt != kBf16 || M > 32 || (wl && (N % 16 != 0 || K % 128 != 0)))
         return hipErrorInvalidValue;
+    // accumulator rows a lane needs: np planes per group of 4 tokens
+    const int rows = np * ((M + 3) / 4);
+    if (np < 1 || np > 3 || (np > 1 && (rows > 4 || kpart))) return hipErrorInvalidValue;
     const uint16_t *A16 = static_cast<const uint16_t *>(A);
 #define Q4_LAUNCH_SR(R, B) \
-    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, kpart, wl, s)
-    if (M <= 4) Q4_LAUNCH_SR(1, 1);
-    if (M <= 8) Q4_LAUNCH_SR(2, 1);
-    if (M <= 16) Q4_LAUNCH_SR(4, 1);
+    return launch_sr<R, B>(A16, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, C, c_dt, kpart, np, wl, s)
+    if (rows <= 1) Q4_LAUNCH_SR(1, 1);
+    if (rows <= 2) Q4_LAUNCH_SR(2, 1);
+    if (rows <= 4) Q4_LAUNCH_SR(4, 1);
     Q4_LAUNCH_SR(4, 2);
 #undef Q4_LAUNCH_SR
 }
@@ -777,7 +814,7 @@ hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, cons
     if (wl && !mfma) return hipErrorInvalidValue;  // the vector-ALU kernel reads rows
     if (mfma && (M <= 16 || tiles_per_chunk(N) < 8))
         return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
-                                    C, c_dt, wl, s, M <= 16 ? kpart : nullptr);
+                                    C, c_dt, wl, s, M <= 16 ? kpart : nullptr, 1);
     const size_t a_row = (size_t)K * (a_dt == kF32 ? 4 : 2);
     const size_t c_row = (size_t)N * (c_dt == kF32 ? 4 : 2);
     for (int m0 = 0; m0 < M; m0 += 16) {
@@ -786,7 +823,7 @@ hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, cons
         void *Cm = static_cast<char *>(C) + (size_t)m0 * c_row;
         const hipError_t e =
             mfma ? launch_q4_fused_mfma(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
-                                        Cm, c_dt, wl, s, nullptr)
+                                        Cm, c_dt, wl, s, nullptr, 1)
                  : launch_q4_fused_simt(Am, a_dt, Wpacked, absmax, codebook, bias, mm, N, K, bs_log2,
                                         Cm, c_dt, s);
         if (e != hipSuccess) return e;

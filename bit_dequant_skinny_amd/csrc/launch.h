@@ -39,10 +39,13 @@ hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, cons
                            const float *codebook, const void *bias, int M, int N, int K,
                            int bs_log2, void *C, int c_dt, int wl, hipStream_t s,
                            float *kpart = nullptr);
+// The skinny matrix-core kernel alone.  np = 2 / 3: A holds the exact bf16
+// planes [np][M][K] of fp16 / fp32 activations, summed per token inside the
+// kernel before the bias and the rounding (np * ceil(M / 4) <= 4, no kpart).
 hipError_t launch_q4_fused_mfma(const void *A, int a_dt, const uint8_t *Wpacked,
                                 const float *absmax, const float *codebook, const void *bias,
                                 int M, int N, int K, int bs_log2, void *C, int c_dt, int wl,
-                                hipStream_t s, float *kpart = nullptr);
+                                hipStream_t s, float *kpart = nullptr, int np = 1);
 // K parts the skinny kernel would use for M bf16 token rows (1 = none).
 int q4_fused_kparts(int M, int N, int K);
 hipError_t launch_q4_fused_simt(const void *A, int a_dt, const uint8_t *Wpacked,
