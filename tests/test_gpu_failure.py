@@ -54,15 +54,19 @@ if case in ("fused", "dequant_split", "gemm_split"):
     torch.cuda.synchronize()
     Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
     assert_within_tolerance(bf16_host(C), Cr, S, case)
-elif case == "plane_sum":
-    A32 = synth.activations(M, K, 71, "fp32")
-    C = torch.full((M, N), 7.0, dtype=torch.float32, device=dev)
+elif case in ("plane_sum", "planes"):
+    # fp32 activations: 3 tokens have their planes summed inside the skinny
+    # kernel (launches "planes", "fused"); 6 go through fp32 partials and the
+    # plane sum (launches "planes", "fused", "plane sum")
+    Mp = 6 if case == "plane_sum" else M
+    A32 = synth.activations(Mp, K, 71, "fp32")
+    C = torch.full((Mp, N), 7.0, dtype=torch.float32, device=dev)
     dA = to_dev(A32, "f32")
     expect_failure(lambda: q4.q4_gemm_skinny(dA, Wp, am, cb, bs, out=C, out_dtype=torch.float32),
-                   C, "plane sum")
+                   C, "plane sum" if case == "plane_sum" else "planes")
     q4.q4_gemm_skinny(dA, Wp, am, cb, bs, out=C, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    Cr, S = oracle.q4_gemm_ex(A32, "fp32", p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
+    Cr, S = oracle.q4_gemm_ex(A32, "fp32", p["Wpacked"], p["absmax"], p["codebook"], Mp, N, K, bs)
     assert_within_tolerance(None, Cr, S, case, out="fp32", values=host_f64(C))
 elif case == "dequant":
     out = torch.full((N, K), 3.0, dtype=torch.bfloat16, device=dev)
@@ -89,6 +93,7 @@ CASES = {
     "dequant_split": "dequant:1",
     "gemm_split": "gemm:1",
     "plane_sum": "plane sum:1",
+    "planes": "planes:1",
     "dequant": "dequant:1",
     "gemm": "gemm:1",
 }
