@@ -469,6 +469,21 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
         };
         const float *scs = &scl[qp & 1][j * kScaleStride + (s_blk & ~1)];
         am[(us * TB) & 1] = DB == 2 ? read_scales(scs) : picked(read_scales(scs));
+        // Block sums of the previous tile and their scales: with one token
+        // block a tile's sums are scaled into its accumulators one unit
+        // later, after the next tile's MFMAs are issued, so the wave does not
+        // wait for its own MFMAs to finish (measured 2-3 % at M = 1..4; same
+        // values, same order).  Two token blocks have no registers to spare
+        // for it and scale at once.
+        floatx4 P0[MB], P1[MB];
+        float psc[2];
+        auto scale_into = [&](float (&a)[MB][SR]) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+#pragma unroll
+                for (int r = 0; r < SR; ++r)
+                    a[b][r] = fmaf(psc[1], P1[b][r], fmaf(psc[0], P0[b][r], a[b][r]));
+        };
 #pragma unroll
         for (int tr = 0; tr < TB; ++tr) {
             const int cur = (us * TB + tr) & 1;
@@ -543,12 +558,23 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
             // the table reads of the next unit issued just before it.
             float sc[2] = {am[cur][0], am[cur][1]};
             if constexpr (DB == 2) pick_scales(am[cur], s_pick, sc);
+            if constexpr (MB == 1) {
+                if (tr > 0) scale_into(acc[tr > 0 ? tr - 1 : 0]);
+            }
 #pragma unroll
-            for (int b = 0; b < MB; ++b)
-#pragma unroll
-                for (int r = 0; r < SR; ++r)
-                    acc[tr][b][r] = fmaf(sc[1], D1[b][r], fmaf(sc[0], D0[b][r], acc[tr][b][r]));
+            for (int b = 0; b < MB; ++b) {
+                P0[b] = D0[b];
+                P1[b] = D1[b];
+                // Keep all four MFMA result registers live until here: the
+                // rows past SR are unused, and reusing their registers right
+                // after the MFMA makes the wave wait for its write-back.
+                if constexpr (MB == 1) __asm__ volatile("" ::"v"(D0[b]), "v"(D1[b]));
+            }
+            psc[0] = sc[0];
+            psc[1] = sc[1];
+            if constexpr (MB == 2) scale_into(acc[tr]);
         }
+        if constexpr (MB == 1) scale_into(acc[TB - 1]);
         // At the end of a period, publish the next period's scales.  The
         // buffer written here was last read in the previous period, which
         // every wave finished before the previous barrier.
