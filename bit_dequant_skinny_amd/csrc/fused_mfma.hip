@@ -154,14 +154,18 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     const int seg_lim = nseg - seg0 < spp ? nseg - seg0 : spp;
     const int spw = (spp + KW - 1) / KW;  // segment slots per wave per chunk
     const uint32_t row_bytes = (uint32_t)K >> 1;
-    // Workgroups start their walk along K at different slots (whole scale
-    // periods), chosen by b / 8 so that the workgroups on one XCD do too:
-    // neighbouring workgroups then read different parts of their rows at any
-    // time, which spreads the loads over more DRAM banks and channels than a
-    // walk in lockstep (measured 10 % faster at 28672 x 8192).  Slot q of a
-    // chunk is slot (q + rot) % spw of the row.
+    // Over rows, workgroups start their walk along K at different slots
+    // (whole scale periods), chosen by b / 8 so that the workgroups on one XCD
+    // do too: neighbouring workgroups then read different parts of their rows
+    // at any time, which spreads the loads over more DRAM banks and channels
+    // than a walk in lockstep, where every CU reads the same 64-byte column
+    // window of rows K/2 bytes apart (measured 10 % faster at 28672 x 8192).
+    // Slot q of a chunk is slot (q + rot) % spw of the row.  Over tiles,
+    // where each unit is 1 KiB of contiguous memory, the lockstep walk
+    // measured 3-4 % faster than the rotated one (same shape, M = 1..16), so
+    // tiles walk from slot 0.
     const int nper = spw / P;  // whole periods per chunk
-    const int rot = spw % P == 0 ? (int)((blockIdx.x / 8u) % (uint32_t)nper) * P : 0;
+    const int rot = WL == 0 && spw % P == 0 ? (int)((blockIdx.x / 8u) % (uint32_t)nper) * P : 0;
     const uint32_t nb = (uint32_t)K >> bs_log2;
 
     const __amdgpu_buffer_rsrc_t wres = make_rsrc(Wp, (uint32_t)N * row_bytes);

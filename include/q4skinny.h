@@ -214,8 +214,13 @@ q4_status q4_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
  *
  * Arguments, dispatch (fused kernels up to the crossover, split path above)
  * and results are those of q4_gemm_skinny_ex on the row-major weights the
- * tiles were made from; the outputs are bit-identical to it (every kernel
- * sees the same bytes in the same registers and sums in the same order).
+ * tiles were made from.  Above 32 token rows and on the split path the
+ * outputs are bit-identical to it (every kernel sees the same bytes in the
+ * same registers and sums in the same order); up to 32 rows the skinny
+ * kernel walks K from the first segment over tiles but from a rotated
+ * segment per workgroup over rows (which spreads row-major loads over the
+ * DRAM channels), so the fp32 sums of the same products may round
+ * differently; both meet the same tolerance and each is deterministic.
  *
  *  Q4_ERR_INVALID_ARGUMENT: as q4_gemm_skinny_ex, plus N % 16 != 0 or
  *    K % 128 != 0.
