@@ -164,7 +164,10 @@ def traffic_from_profile():
     for line in text.splitlines():
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
-            fields[k.strip()] = v.strip().strip("`")
+            k = k.strip()
+            if k.startswith("kernel source sha256"):  # "(the files it covers)" may follow
+                k = "kernel source sha256"
+            fields[k] = v.strip().strip("`")
     if fields.get("kernel source sha256") != fused_source_hash():
         return None
     try:
