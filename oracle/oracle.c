@@ -396,9 +396,12 @@ void oracle_quantize(const void *W, int w_dtype, const float *codebook, int64_t 
  * Rows form tiles of 16 (tile t = rows 16t..16t+15); a row's bytes form
  * segments of 64 (segment s = bytes 64s..64s+63, i.e. k = 128s..128s+127);
  * the 16 rows x 64 bytes of (t, s) become one unit of 1024 bytes, stored
- * unit after unit in the order (t, s) with s fastest; inside a unit, piece
- * p = 0..63 of 16 bytes holds bytes 16*(p / 16) .. +15 of segment s of row
- * 16t + p % 16.  Requires N % 16 == 0 and K % 128 == 0.
+ * unit after unit in the order (t, s) with s fastest.  Inside a unit, the
+ * 64 bytes of a row's segment are 8 quarters of 8 bytes (quarter c = bytes
+ * 8c..8c+7, k = 128s + 16c .. +15); piece p = 0..63 of 16 bytes belongs to
+ * row 16t + p % 16 and holds quarter a then quarter a + 4 (one piece of each
+ * 64-wide half of the segment), where a = 0, 2, 1, 3 for p / 16 = 0, 1, 2,
+ * 3.  Requires N % 16 == 0 and K % 128 == 0.
  * oracle_tile_offset gives where byte j of row n goes; oracle_repack_tiles
  * moves every byte there. */
 int64_t oracle_tile_offset(int64_t N, int64_t K, int64_t n, int64_t j)
@@ -407,8 +410,9 @@ int64_t oracle_tile_offset(int64_t N, int64_t K, int64_t n, int64_t j)
     int64_t segs = K / 128;     /* segments per row */
     int64_t t = n / 16, r = n % 16;
     int64_t s = j / 64, q = j % 64;
-    int64_t piece = r + 16 * (q / 16);
-    return (t * segs + s) * 1024 + piece * 16 + q % 16;
+    int64_t quarter = q / 8, half = quarter / 4, a = quarter % 4;
+    int64_t piece = r + 16 * (2 * (a % 2) + a / 2);
+    return (t * segs + s) * 1024 + piece * 16 + half * 8 + q % 8;
 }
 
 void oracle_repack_tiles(const uint8_t *Wpacked, int64_t N, int64_t K, uint8_t *out)

@@ -540,16 +540,22 @@ def pin_tile_layout_golden(orc):
 
 def pin_bf16_tile_layout(orc):
     """O13: element indices worked by hand (tests/golden/bf16_tile_layout.txt),
-    a bijection of whole units, and the byte tiling of O12 on 2*K-byte rows."""
+    a bijection, 16-row tiles of consecutive units, and pieces of 8
+    consecutive k of one row."""
     for line in golden_lines("bf16_tile_layout.txt"):
         n, k, idx = (int(v) for v in line.split())
         assert orc.bf16_tile_index(32, 64, n, k) == idx, ("bf16 tile", n, k)
     N, K = 32, 96
     idx = np.array([[orc.bf16_tile_index(N, K, n, k) for k in range(K)] for n in range(N)])
     assert sorted(idx.ravel().tolist()) == list(range(N * K))
-    for n in range(N):
-        for k in range(K):
-            assert orc.tile_offset(N, 4 * K, n, 2 * k) == 2 * idx[n, k]
+    # 8 consecutive k of a row stay consecutive (one piece) ...
+    assert np.all(np.diff(idx.reshape(N, K // 8, 8), axis=2) == 1)
+    # ... and the 16 rows x 32 k of (tile t, step s) fill units of 512
+    # elements, (t, s) in row order with s fastest
+    for t in range(N // 16):
+        for s_ in range(K // 32):
+            u = idx[16 * t:16 * t + 16, 32 * s_:32 * s_ + 32]
+            assert u.min() == (t * (K // 32) + s_) * 512 and u.max() == u.min() + 511
     W = np.arange(N * K, dtype=np.uint16).reshape(N, K)
     T = orc.bf16_repack_tiles(W, N, K).ravel()
     assert np.array_equal(T[idx.ravel()], W.ravel())

@@ -4,8 +4,8 @@ bf16_gemm_skinny_tiles).
 CPU: the oracle's layout (O13) is pinned by indices worked by hand
 (tests/golden/bf16_tile_layout.txt), by being a bijection onto [0, N*K), by
 each tile occupying its own contiguous 16*K elements and each unit holding
-exactly the 16 rows x 32 k of its step, and by agreeing byte for byte with
-the 4-bit tile layout (O12, written in bytes) on rows of 2*K bytes.  The
+exactly the 16 rows x 32 k of its step, and by each 16-byte piece holding 8
+consecutive k of one row (the row of the lane that loads it).  The
 entry points reject shapes the layout cannot hold before touching the GPU
 runtime.
 
@@ -61,14 +61,15 @@ def test_bf16_tile_layout_is_a_bijection_of_whole_tiles_and_units(N, K):
 
 
 @pytest.mark.parametrize("N,K", [(16, 32), (32, 96), (48, 64)])
-def test_bf16_layout_is_the_byte_tiling_of_the_4bit_layout(N, K):
-    # O12 tiles rows of K4/2 bytes in 64-byte columns; bf16 rows are 2*K bytes,
-    # so O12 at K4 = 4*K must move bytes 2k, 2k+1 of row n to 2*idx, 2*idx+1.
+def test_bf16_pieces_are_8_consecutive_k_of_one_row(N, K):
+    # a lane's 16 bytes are 8 consecutive k of one row, and piece p of a unit
+    # belongs to row p % 16 of the tile, k = 8 (p / 16) .. +7 of the step
+    idx = np.array([[oracle.bf16_tile_index(N, K, n, k) for k in range(K)] for n in range(N)])
+    assert np.all(np.diff(idx.reshape(N, K // 8, 8), axis=2) == 1)
+    piece = (idx % 512) // 8
     for n in range(N):
-        for k in range(K):
-            i = oracle.bf16_tile_index(N, K, n, k)
-            assert oracle.tile_offset(N, 4 * K, n, 2 * k) == 2 * i
-            assert oracle.tile_offset(N, 4 * K, n, 2 * k + 1) == 2 * i + 1
+        for k in range(0, K, 8):
+            assert piece[n, k] % 16 == n % 16 and piece[n, k] // 16 == (k % 32) // 8
 
 
 def test_bf16_repack_moves_elements_not_values():

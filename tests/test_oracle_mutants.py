@@ -58,7 +58,12 @@ MUTANTS = {
                              "for (int64_t k = b * bs + 1; k < (b + 1) * bs && k < K; k++) {\n                double w = fabs"),
     "w16_not_rounded": ("double p = a * bf16_to_double(w16);",
                         "double p = a * (double)oracle_w32(Wpacked, absmax, codebook, K, bs, n, k) + 0.0 * w16;"),
-    "tile_lanes_transposed": ("int64_t piece = r + 16 * (q / 16);", "int64_t piece = 4 * r + q / 16;"),
+    "tile_lanes_transposed": ("int64_t piece = r + 16 * (2 * (a % 2) + a / 2);",
+                              "int64_t piece = 4 * r + (2 * (a % 2) + a / 2);"),
+    "tile_quarters_in_row_order": ("int64_t piece = r + 16 * (2 * (a % 2) + a / 2);",
+                                   "int64_t piece = r + 16 * a;"),
+    "tile_halves_swapped": ("return (t * segs + s) * 1024 + piece * 16 + half * 8 + q % 8;",
+                            "return (t * segs + s) * 1024 + piece * 16 + (1 - half) * 8 + q % 8;"),
     "tile_segment_of_128_bytes": ("int64_t s = j / 64, q = j % 64;", "int64_t s = j / 128, q = j % 128;"),
     "bf16_tile_lanes_transposed": ("int64_t piece = r + 16 * (q / 8);", "int64_t piece = 4 * r + q / 8;"),
     "bf16_tile_step_of_64": ("int64_t s = k / 32, q = k % 32;", "int64_t s = k / 64, q = k % 64;"),

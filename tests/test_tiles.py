@@ -3,8 +3,9 @@ q4_dequant_tiles).
 
 CPU: the oracle's layout is pinned by offsets worked by hand
 (tests/golden/tile_layout.txt), by being a bijection onto [0, N*K/2), by each
-tile occupying its own contiguous 16*K/2 bytes, and by each 1 KiB unit holding
-exactly the 16 rows x 64 bytes of its segment.  The entry points reject
+tile occupying its own contiguous 16*K/2 bytes, by each 1 KiB unit holding
+exactly the 16 rows x 64 bytes of its segment, and by each 16-byte piece
+holding 8 bytes of each 64-wide half of one row's segment.  The entry points reject
 shapes the layout cannot hold before touching the GPU runtime.
 
 GPU: the repack kernel equals the oracle byte for byte; GEMMs over tiles and
@@ -57,8 +58,14 @@ def test_tile_layout_is_a_bijection_of_whole_tiles_and_units(N, K):
         for s in range(K // 128):  # one 1 KiB unit per (tile, segment)
             u = blk[:, 64 * s:64 * s + 64]
             assert u.min() % 1024 == 0 and u.max() == u.min() + 1023
-            # 16 consecutive bytes of a row stay consecutive (one 16-byte piece)
-            assert np.all(np.diff(u.reshape(16, 4, 16), axis=2) == 1)
+            # 8 consecutive bytes of a row stay consecutive (half a piece),
+            # and a piece holds bytes c*8.. of the segment's first 32 bytes
+            # then (c+4)*8.. of its second 32 (one 16-byte piece per lane,
+            # each half from its own 64-wide block of k)
+            q = u.reshape(16, 8, 8)
+            assert np.all(np.diff(q, axis=2) == 1)
+            assert np.all(q[:, 4:, 0] == q[:, :4, 0] + 8)
+            assert np.all(q[:, :4, 0] % 16 == 0)
 
 
 def test_repack_moves_bytes_not_values():
@@ -72,8 +79,10 @@ def test_repack_moves_bytes_not_values():
             back[n, j] = T[oracle.tile_offset(N, K, n, j)]
     assert np.array_equal(back, W)
     assert np.array_equal(np.sort(T), np.sort(W.ravel()))
-    # piece 17 of unit (0, 0) is row 1, bytes 16..31 (lane 17 of a 16-row tile)
-    assert np.array_equal(T[17 * 16:18 * 16], W[1, 16:32])
+    # piece 17 of unit (0, 0) (lane 17 of a 16-row tile) is row 1, bytes
+    # 16..23 and 48..55: quarter 2 of each 64-wide half of the segment
+    assert np.array_equal(T[17 * 16:17 * 16 + 8], W[1, 16:24])
+    assert np.array_equal(T[17 * 16 + 8:18 * 16], W[1, 48:56])
 
 
 @pytest.mark.parametrize("args,expect", [
