@@ -14,11 +14,12 @@
 // absmax[i >> bs_log2].
 //
 // Weights in the tile layout (16-row tiles of 1 KiB units, see
-// repack_tiles_kernel) take dequant_tiles_kernel: the same arithmetic in the
-// order of the tiles, each lane turning one 16-byte piece (32 weights of one
-// row, inside one scale block since bs >= 64) into 32 outputs; 16-bit outputs
-// go through LDS so that the stores run along rows (1 KiB per row and
-// store), fp32 outputs are stored from the lanes (128 bytes each).
+// repack_q4_tiles_kernel) take dequant_tiles_kernel: the same arithmetic in
+// the order of the tiles, each lane turning one 16-byte piece (16 weights of
+// each 64-wide half of one row's segment, each run inside one scale block
+// since bs >= 64) into 32 outputs; 16-bit outputs go through LDS so that the
+// stores run along rows (1 KiB per row and store), fp32 outputs are stored
+// from the lanes (two runs of 64 bytes each).
 #include "device.h"
 #include "launch.h"
 
@@ -109,23 +110,28 @@ __global__ __launch_bounds__(kThreads) void dequant_tiles_kernel(
         const uint32_t unit = p >> 6, l = p & 63;
         const uint32_t t = unit / nseg, seg = unit - t * nseg;
         const uint32_t n = 16 * t + (l & 15);
-        const uint32_t k0 = 128 * seg + 32 * (l >> 4);  // first of the piece's 32 weights
+        // the piece holds 16 weights of each 64-wide half of the segment,
+        // starting at k0 and k0 + 64 (quarter a = 0, 2, 1, 3 by lane group)
+        const uint32_t gl = l >> 4, a = 2 * (gl & 1) + (gl >> 1);
+        const uint32_t k0 = 128 * seg + 16 * a;
         const uint4 v = tiles[p];
-        const float am = absmax[n * nb + (k0 >> bs_log2)];
+        const float am0 = absmax[n * nb + (k0 >> bs_log2)];
+        const float am1 = absmax[n * nb + ((k0 + 64) >> bs_log2)];
         const uint32_t d[4] = {v.x, v.y, v.z, v.w};
         float w[32];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) w[8 * u + j] = cb_lookup(table, d[u] >> (4 * j)) * am;
+            for (int j = 0; j < 8; ++j)
+                w[8 * u + j] = cb_lookup(table, d[u] >> (4 * j)) * (u < 2 ? am0 : am1);
         const bool live = p0 < pieces;
-        const size_t e0 = (size_t)n * (size_t)K + k0;  // first output element
+        const size_t e0 = (size_t)n * (size_t)K + k0;  // first output element of each half
         if constexpr (OT == kF32) {
             float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + e0);
             if (live)
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
-                    o[q] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                    o[q + (q < 4 ? 0 : 12)] = make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
         } else {
             if constexpr (OT == kF16) {
 #pragma unroll
@@ -138,14 +144,14 @@ __global__ __launch_bounds__(kThreads) void dequant_tiles_kernel(
             // 16-byte chunk c % 64 of the four units' runs (one 1 KiB run per
             // row when the four units are consecutive segments of one tile).
             const int wv = threadIdx.x >> 6;
-            char *mine = stage + wv * kUnitLds + (l & 15) * kRowLds + 64 * (l >> 4);
+            char *mine = stage + wv * kUnitLds + (l & 15) * kRowLds + 32 * a;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 uint32_t h[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     h[j] = OT == kBf16 ? f32_to_bf16_rne(w[8 * q + j]) : f32_to_f16_rne(w[8 * q + j]);
-                *reinterpret_cast<uint4 *>(mine + 16 * q) =
+                *reinterpret_cast<uint4 *>(mine + 16 * q + (q < 2 ? 0 : 96)) =
                     make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                                h[6] | (h[7] << 16));
             }
@@ -170,10 +176,31 @@ __global__ __launch_bounds__(kThreads) void dequant_tiles_kernel(
 
 // Row-major packed codes -> tile layout.  Tile t holds rows 16t..16t+15;
 // (tile t, segment s) is the 1 KiB unit (t * K/128 + s): 64 pieces of 16
-// bytes, piece l being bytes 64s + 16(l / 16) .. +16 of row 16t + l % 16 (the
-// 16 bytes a matrix-core lane l decodes for one 128-wide segment).  A pure
-// permutation of 16-byte pieces; each thread moves one piece per step, so
-// the writes are contiguous and each wave reads 64-byte runs of 16 rows.
+// bytes, piece l holding row 16t + l % 16, bytes 64s + 8a .. +8 and
+// 64s + 32 + 8a .. +8 with a = 0, 2, 1, 3 for l / 16 = 0..3 (the 16 bytes a
+// matrix-core lane l decodes for one 128-wide segment: 8 from each 64-wide
+// block).  Each thread writes one piece per step, so the writes are
+// contiguous.
+__global__ __launch_bounds__(kThreads) void repack_q4_tiles_kernel(const uint2 *__restrict__ src,
+                                                                   uint4 *__restrict__ dst,
+                                                                   uint32_t pieces, uint32_t nseg,
+                                                                   uint32_t row_halves) {
+    const uint32_t stride = gridDim.x * kThreads;
+    for (uint32_t p = blockIdx.x * kThreads + threadIdx.x; p < pieces; p += stride) {
+        const uint32_t unit = p >> 6, l = p & 63;
+        const uint32_t t = unit / nseg, seg = unit - t * nseg;
+        const uint32_t n = 16 * t + (l & 15), gl = l >> 4, a = 2 * (gl & 1) + (gl >> 1);
+        const uint2 h0 = src[n * row_halves + 8 * seg + a];
+        const uint2 h1 = src[n * row_halves + 8 * seg + a + 4];
+        dst[p] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+    }
+}
+
+// Row-major bf16 weights -> their tile layout: (tile t, step s) is one unit
+// of 64 pieces of 16 bytes, piece l being bytes 64s + 16(l / 16) .. +16 of
+// row 16t + l % 16 (8 consecutive k).  A pure permutation of 16-byte pieces;
+// each thread moves one piece per step, so the writes are contiguous and each
+// wave reads 64-byte runs of 16 rows.
 __global__ __launch_bounds__(kThreads) void repack_tiles_kernel(const uint4 *__restrict__ src,
                                                                 uint4 *__restrict__ dst,
                                                                 uint32_t pieces, uint32_t nseg,
@@ -191,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void repack_tiles_kernel(const uint4 *__r
 
 namespace {
 
-// The 16-row tiling of both weight types: rows of row_bytes bytes (a
-// multiple of 64) cut into 64-byte columns; (tile, column) is one 1 KiB unit.
+// The 16-row tiling of bf16 weights: rows of row_bytes bytes (a multiple of
+// 64) cut into 64-byte columns; (tile, column) is one 1 KiB unit.
 hipError_t repack_rows16(const void *src, void *dst, int N, uint64_t row_bytes, hipStream_t s) {
     if (N % 16 != 0 || row_bytes % 64 != 0 || (uint64_t)N * row_bytes >= (1ull << 32))
         return hipErrorInvalidValue;
@@ -212,8 +239,18 @@ hipError_t repack_rows16(const void *src, void *dst, int N, uint64_t row_bytes, 
 
 hipError_t launch_repack_tiles(const uint8_t *Wpacked, uint8_t *Wtiles, int N, int K,
                                hipStream_t s) {
-    if (K % 128 != 0) return hipErrorInvalidValue;
-    return repack_rows16(Wpacked, Wtiles, N, (uint64_t)K / 2, s);
+    const uint64_t row_bytes = (uint64_t)K / 2;
+    if (K % 128 != 0 || N % 16 != 0 || (uint64_t)N * row_bytes >= (1ull << 32))
+        return hipErrorInvalidValue;
+    const uint32_t pieces = (uint32_t)((uint64_t)N * row_bytes / 16);
+    uint32_t blocks = (pieces + kThreads - 1) / kThreads;
+    const uint32_t cap = (uint32_t)device_info().num_cus * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks == 0) return hipSuccess;
+    repack_q4_tiles_kernel<<<dim3(blocks), dim3(kThreads), 0, s>>>(
+        reinterpret_cast<const uint2 *>(Wpacked), reinterpret_cast<uint4 *>(Wtiles), pieces,
+        (uint32_t)(row_bytes / 64), (uint32_t)(row_bytes / 8));
+    return hipGetLastError();
 }
 
 // bf16 weights: a unit is 16 rows x 32 k (the 64 bytes of a row one

@@ -25,15 +25,15 @@
 // builds that address from the packed byte and the lane's offset.
 //
 // Tiles.  A tile is 16 output features (the B-operand columns, lane % 16)
-// over all of K, walked in 128-wide segments: lane group g = lane / 16 reads
-// 16 bytes (32 codes) of its feature's row at byte 16*g of the segment, so a
-// feature row is read 64 contiguous bytes per segment and one load
-// instruction brings 1 KiB.  Groups 0,1 hold the segment's first 64-wide
-// block and groups 2,3 the second; half of each lane's dwords are exchanged
-// with the lane 32 away (over rows by one v_permlane32_swap pair, over tiles
-// by loading the two 8-byte halves in place) so that every MFMA step draws
-// from a single 64-wide block, which keeps the absmax scaling exact per
-// block.
+// over all of K, walked in 128-wide segments: each lane takes 16 bytes (32
+// codes) of its feature's row per segment, 8 from the segment's first
+// 64-wide block (dwords 0, 1) and 8 from the second (dwords 2, 3), so that
+// every MFMA step draws from a single 64-wide block, which keeps the absmax
+// scaling exact per block; one load instruction brings 1 KiB.  The tile
+// layout stores the bytes in that order.  Over rows lane group g = lane / 16
+// reads the 16 bytes at byte 16*g of the segment (groups 0,1 hold the first
+// block, groups 2,3 the second) and half of each lane's dwords are exchanged
+// with the lane 32 away by one v_permlane32_swap pair.
 // Tokens feed the A operand, one per row; rows without a token read zeros
 // and their outputs are discarded.  Output row 4g + r of an MFMA lands in
 // lane group g, accumulator r, so with one token block token t takes row
@@ -182,23 +182,18 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // offset.  Row-major: segment s of row n is the 64 bytes at
     // n*row_bytes + 64*s, lane (j, g) reads 16 of them at 16*g.  Tile layout:
     // the 16 rows x 64 bytes of (tile, segment) are one 1 KiB unit at
-    // (tile*nseg + s) * 1024 that holds lane l's 16 bytes at 16*l.  A tile
-    // spans 16*row_bytes bytes in both.
-    //
-    // Over tiles a lane loads its 16 bytes as two 8-byte halves already in the
-    // order the MFMA steps use (see swapped_k_offset): lanes 0-31 the first
-    // half of their own piece and the first half of the piece of the lane 32
-    // above, lanes 32-63 the second half of the piece of the lane 32 below and
-    // the second half of their own.  The halves are 512 bytes apart, so each
-    // load instruction still reads 512 contiguous bytes and no lane exchange
-    // follows (measured 2-4 % faster at M = 1..4).  Over rows the same halves
-    // would be 32-byte pieces of 16 rows per instruction, which the memory
-    // serves far worse (40 against 28 us at M = 1 on the FFN): there each lane
-    // loads its own 16 bytes and one v_permlane32_swap pair regroups them.
-    const uint32_t w_lane =
-        (WL ? (lane < 32 ? 16u * (uint32_t)lane : 16u * (uint32_t)(lane - 32) + 8u)
-            : (uint32_t)j * row_bytes + 16u * (uint32_t)g) +
-        ((uint32_t)seg0 << (WL ? 10 : 6));
+    // (tile*nseg + s) * 1024 that holds lane l's 16 bytes at 16*l, already in
+    // the order the MFMA steps use (8 bytes of the segment's first 64-wide
+    // block, then 8 of its second): one 128-bit load per lane and unit, 1 KiB
+    // of contiguous memory per instruction, no lane exchange (measured 3-4 %
+    // faster at M = 1..4 than two 64-bit loads of 512 bytes each from the
+    // earlier tile order).  Over rows each lane loads its own 16 bytes (half
+    // from each block would make each instruction read 32-byte pieces of 16
+    // rows, which measured 40 against 28 us at M = 1 on the FFN) and one
+    // v_permlane32_swap pair regroups them.  A tile spans 16*row_bytes bytes
+    // in both layouts.
+    const uint32_t w_lane = (WL ? 16u * (uint32_t)lane : (uint32_t)j * row_bytes + 16u * (uint32_t)g) +
+                            ((uint32_t)seg0 << (WL ? 10 : 6));
     const int seg_sh = WL ? 10 : 6;
 
     // Weight issue cursor: the (chunk, slot) whose loads are issued next.
@@ -228,13 +223,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
     // at M = 1..8 (neutral over rows).
     auto issue = [&](uint4 &dst, int tr) {
         const uint32_t wo = w_live ? w_row0 + (uint32_t)tr * w_tile_step : kPastEnd;
-        if constexpr (WL == 1) {
-            const auto h0 = __builtin_amdgcn_raw_buffer_load_b64(wres, (int)wo, 0, 2);
-            const auto h1 = __builtin_amdgcn_raw_buffer_load_b64(wres, (int)(wo + 512u), 0, 2);
-            dst = make_uint4(h0[0], h0[1], h1[0], h1[1]);
-        } else {
-            dst = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 2));
-        }
+        dst = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, (int)wo, 0, 2));
     };
 
     // Scales are staged through LDS one period (P slots) ahead: per period

@@ -1,8 +1,9 @@
 // Fused 4-bit dequantize + GEMM on the matrix cores for tens to hundreds of
 // token rows: C[M,N] = A[M,K] * dequant(W)^T (+ bias), bf16 activations,
 // blocksize >= 64.  The packed weights are row-major or in the tile layout
-// (wl = 1: 16-row tiles of 1 KiB units); a lane loads the same 16 bytes
-// either way, only its offset and the segment stride differ.
+// (wl = 1: 16-row tiles of 1 KiB units); a lane gets the same 16 bytes
+// either way: one 128-bit load over rows, two 64-bit loads 512 bytes apart
+// over tiles (which hold a row's 16 bytes as two halves in different pieces).
 //
 // The bitsandbytes pull request "[ROCm] Optimize kgemm_4bit_inference_naive
 // for ROCm, use it for batch sizes other than 1" finds (section "Fused path
@@ -84,6 +85,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void *base, uint3
     return make_rsrc(static_cast<const char *>(base) + st, nr);
 }
 
+// The 16 bytes lane (j, g) decodes per segment: bytes 16g..16g+15 of its
+// row's segment.  Over tiles those are two 8-byte halves 512 bytes apart
+// (the tile layout holds 8 bytes of each 64-wide half of a row's segment per
+// piece: the first half of the lane's bytes sits at 16j + 256 (g % 2) +
+// 8 (g / 2) of the unit, the second 512 bytes further), so each of the two
+// loads still reads 512 contiguous bytes over the wave.
+__device__ __forceinline__ uint32_t tile_lane_offset(int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    return 16u * (uint32_t)j + 256u * (uint32_t)(g & 1) + 8u * (uint32_t)(g >> 1);
+}
+
+__device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t wr, uint32_t off, int wl) {
+    if (wl) {
+        const auto h0 = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)off, 0, 0);
+        const auto h1 = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)(off + 512u), 0, 0);
+        return make_uint4(h0[0], h0[1], h1[0], h1[1]);
+    }
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, 0));
+}
+
 // The tile of workgroup b.  The hardware deals workgroups to the 8 XCDs
 // round-robin (b % 8).  In both mappings the token blocks of a feature
 // block run on one XCD, where the later ones read the packed weights from
@@ -155,6 +176,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
     const int j = lane & 15, g = lane >> 4;
+    const uint32_t tile_lane_off = tile_lane_offset(lane);
     const char *tab = reinterpret_cast<const char *>(table);
     const uint32_t lane_off = (uint32_t)(lane & 31) * 4;  // hi copies
     const uint32_t lane_off_lo = lane_off + 128;          // lo copies
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
     for (int b = 0; b < 4; ++b) {
         const uint32_t n = (uint32_t)(n0 + 16 * b + j);
         w_off[b] = n >= (uint32_t)N ? kPastEnd
-                   : wl ? (n - (uint32_t)j) * row_bytes + 16 * (uint32_t)lane
+                   : wl ? (n - (uint32_t)j) * row_bytes + tile_lane_off
                         : n * row_bytes + 16 * (uint32_t)g;
         s_off[b] = n < (uint32_t)N ? n * nbk * 4 : kPastEnd;
     }
@@ -199,7 +221,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
         const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg << seg_sh, live);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-            d.w[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)w_off[b], 0, 0));
+            d.w[b] = load_piece(wr, w_off[b], wl);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t k = seg * 128 + 64 * h;
@@ -384,6 +406,7 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, g = lane >> 4;
+    const uint32_t tile_lane_off = tile_lane_offset(lane);
     const char *tab = reinterpret_cast<const char *>(table);
     const uint32_t lane_off = (uint32_t)(lane & 31) * 4;  // hi copies
     const uint32_t lane_off_lo = lane_off + 128;          // lo copies
@@ -403,7 +426,7 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     for (int b = 0; b < kTN; ++b) {
         const uint32_t n = (uint32_t)(n0 + wave * 16 * kTN + 16 * b + j);
         w_off[b] = n >= (uint32_t)N ? kPastEnd
-                   : wl ? (n - (uint32_t)j) * row_bytes + 16 * (uint32_t)lane
+                   : wl ? (n - (uint32_t)j) * row_bytes + tile_lane_off
                         : n * row_bytes + 16 * (uint32_t)g;
         s_off[b] = n < (uint32_t)N ? n * nbk * 4 : kPastEnd;
     }
@@ -429,7 +452,7 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
         const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg << seg_sh, live);
 #pragma unroll
         for (int b = 0; b < kTN; ++b)
-            d.w[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)w_off[b], 0, 0));
+            d.w[b] = load_piece(wr, w_off[b], wl);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t k = seg * 128 + 64 * h;

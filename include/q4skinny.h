@@ -184,16 +184,20 @@ q4_status q4_gemm_skinny_ex_noalloc(const void *A, int a_dtype, const uint8_t *W
  * optimizations); the arrangement below is this library's.
  *
  *   Tile t = rows 16t .. 16t+15; segment s = bytes 64s .. 64s+63 of a row
- *   (k = 128s .. 128s+127).  Unit (t, s) is the 1024 bytes at offset
- *   (t * K/128 + s) * 1024; its 16-byte piece l (l = 0..63) holds bytes
- *   64s + 16 * (l / 16) .. +16 of row 16t + l % 16.
+ *   (k = 128s .. 128s+127), cut into quarters of 8 bytes (quarter c = bytes
+ *   64s + 8c .. +8, k = 128s + 16c .. +16).  Unit (t, s) is the 1024 bytes at
+ *   offset (t * K/128 + s) * 1024; its 16-byte piece l (l = 0..63) holds
+ *   quarter a then quarter a + 4 of row 16t + l % 16, with a = 0, 2, 1, 3
+ *   for l / 16 = 0, 1, 2, 3: 16 weights of each 64-wide half of the segment,
+ *   the order in which matrix-core lane l consumes them.
  *
- * Within a piece the bytes, nibble order and codes are those of the
+ * Within a quarter the bytes, nibble order and codes are those of the
  * row-major layout, and absmax keeps its row-major [N, K/blocksize] layout.
  * Requires N % 16 == 0, K % 128 == 0 and N*K/2 below 4 GiB.  Reading each
  * tile as one contiguous run gives the DRAM longer bursts than 64-byte
  * pieces of 16 rows 4 KiB or more apart (a read-only pattern test on MI355X:
- * 22.2 against 24.4 us for 117 MB).
+ * 22.2 against 24.4 us for 117 MB), and the piece order lets each lane of the
+ * skinny kernel load its 16 bytes with one 128-bit load.
  */
 
 /*
