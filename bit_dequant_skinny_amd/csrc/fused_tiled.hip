@@ -96,8 +96,9 @@ __device__ __forceinline__ uint32_t tile_lane_offset(int lane) {
     return 16u * (uint32_t)j + 256u * (uint32_t)(g & 1) + 8u * (uint32_t)(g >> 1);
 }
 
-__device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t wr, uint32_t off, int wl) {
-    if (wl) {
+template <int WL>
+__device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t wr, uint32_t off) {
+    if constexpr (WL == 1) {
         const auto h0 = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)off, 0, 0);
         const auto h1 = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)(off + 512u), 0, 0);
         return make_uint4(h0[0], h0[1], h1[0], h1[1]);
@@ -156,11 +157,11 @@ struct SegW {
 };
 
 // K-split layout.  TM: 16-row token blocks per tile (2 or 4).
-template <int TM>
-__global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
+template <int TM, int WL>
+__global__ __launch_bounds__(64 * kWaves, 2) void fused_tiled_ks_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int wl, int m_blocks,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int m_blocks,
     int n_blocks, int ksplit, int segs_per_part, void *__restrict__ C, int c_dt) {
     // Entry e (a packed byte) fills bytes [256 e, 256 e + 256): 32 copies of
     // its hi pair, then 32 copies of its lo pair; lane l reads copy l % 32.
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
     for (int b = 0; b < 4; ++b) {
         const uint32_t n = (uint32_t)(n0 + 16 * b + j);
         w_off[b] = n >= (uint32_t)N ? kPastEnd
-                   : wl ? (n - (uint32_t)j) * row_bytes + tile_lane_off
+                   : WL ? (n - (uint32_t)j) * row_bytes + tile_lane_off
                         : n * row_bytes + 16 * (uint32_t)g;
         s_off[b] = n < (uint32_t)N ? n * nbk * 4 : kPastEnd;
     }
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
             a_off[t][p] = m < (uint32_t)M ? (m * (uint32_t)K + swapped_k_offset(g, p)) * 2 : kPastEnd;
     }
     const uint32_t w_bytes = (uint32_t)N * row_bytes, s_bytes = (uint32_t)N * nbk * 4;
-    const int seg_sh = wl ? 10 : 6;  // segment -> byte offset (1 KiB units or 64-byte pieces)
+    const int seg_sh = WL ? 10 : 6;  // segment -> byte offset (1 KiB units or 64-byte pieces)
     const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2;
 
     auto load_w = [&](int i, SegW &d) {
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64 * kWaves) void fused_tiled_ks_kernel(
         const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg << seg_sh, live);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-            d.w[b] = load_piece(wr, w_off[b], wl);
+            d.w[b] = load_piece<WL>(wr, w_off[b]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t k = seg * 128 + 64 * h;
@@ -388,11 +389,11 @@ struct SegWN {
 };
 
 // N-split layout.  TM: 16-row token blocks per tile (2 or 4).
-template <int TM>
+template <int TM, int WL>
 __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ Wp,
     const float *__restrict__ absmax, const float *__restrict__ codebook,
-    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int wl, int m_blocks,
+    const void *__restrict__ bias, int M, int N, int K, int bs_log2, int m_blocks,
     int n_blocks, int ksplit, uint32_t per_xcd, int segs_per_part, void *__restrict__ C,
     int c_dt) {
     __shared__ uint32_t table[256 * 64];                 // as in the K-split layout
@@ -419,14 +420,14 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
     const uint32_t row_bytes = (uint32_t)K >> 1;
     const uint32_t nbk = (uint32_t)K >> bs_log2;
     const uint32_t w_bytes = (uint32_t)N * row_bytes, s_bytes = (uint32_t)N * nbk * 4;
-    const int seg_sh = wl ? 10 : 6;  // segment -> byte offset (1 KiB units or 64-byte pieces)
+    const int seg_sh = WL ? 10 : 6;  // segment -> byte offset (1 KiB units or 64-byte pieces)
     const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2;
     uint32_t w_off[kTN], s_off[kTN];
 #pragma unroll
     for (int b = 0; b < kTN; ++b) {
         const uint32_t n = (uint32_t)(n0 + wave * 16 * kTN + 16 * b + j);
         w_off[b] = n >= (uint32_t)N ? kPastEnd
-                   : wl ? (n - (uint32_t)j) * row_bytes + tile_lane_off
+                   : WL ? (n - (uint32_t)j) * row_bytes + tile_lane_off
                         : n * row_bytes + 16 * (uint32_t)g;
         s_off[b] = n < (uint32_t)N ? n * nbk * 4 : kPastEnd;
     }
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(64 * kWavesN) void fused_tiled_ns_kernel(
         const __amdgpu_buffer_rsrc_t wr = window(Wp, w_bytes, seg << seg_sh, live);
 #pragma unroll
         for (int b = 0; b < kTN; ++b)
-            d.w[b] = load_piece(wr, w_off[b], wl);
+            d.w[b] = load_piece<WL>(wr, w_off[b]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t k = seg * 128 + 64 * h;
@@ -662,27 +663,35 @@ hipError_t launch_q4_fused_tiled(const uint16_t *A, const uint8_t *Wpacked, cons
         const uint32_t per_xcd = (uint32_t)(((int64_t)m_blocks * n_blocks * ksplit + 7) / 8);
         const int spp = (nseg + ksplit - 1) / ksplit;
         const unsigned grid = 8u * per_xcd;
-        if (bm == 64)
-            fused_tiled_ns_kernel<4><<<dim3(grid), dim3(64 * kWavesN), 0, s>>>(
-                A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks,
-                ksplit, per_xcd, spp, C, c_dt);
-        else
-            fused_tiled_ns_kernel<2><<<dim3(grid), dim3(64 * kWavesN), 0, s>>>(
-                A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks,
-                ksplit, per_xcd, spp, C, c_dt);
+#define Q4_TILED_NS(T, L)                                                                     \
+    fused_tiled_ns_kernel<T, L><<<dim3(grid), dim3(64 * kWavesN), 0, s>>>(                  \
+        A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, m_blocks, n_blocks, ksplit, per_xcd, \
+        spp, C, c_dt)
+        if (bm == 64) {
+            if (wl) Q4_TILED_NS(4, 1);
+            else Q4_TILED_NS(4, 0);
+        } else {
+            if (wl) Q4_TILED_NS(2, 1);
+            else Q4_TILED_NS(2, 0);
+        }
+#undef Q4_TILED_NS
         return hipGetLastError();
     }
     const int n_blocks = (N + kTileN - 1) / kTileN;
     const int spp = ((nseg + ksplit - 1) / ksplit + kWaves - 1) / kWaves * kWaves;
     const unsigned grid = (unsigned)(8 * m_blocks * ((n_blocks + 7) / 8) * ksplit);
-    if (bm == 64)
-        fused_tiled_ks_kernel<4><<<dim3(grid), dim3(64 * kWaves), 0, s>>>(
-            A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks, ksplit,
-            spp, C, c_dt);
-    else
-        fused_tiled_ks_kernel<2><<<dim3(grid), dim3(64 * kWaves), 0, s>>>(
-            A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, wl, m_blocks, n_blocks, ksplit,
-            spp, C, c_dt);
+#define Q4_TILED_KS(T, L)                                                                    \
+    fused_tiled_ks_kernel<T, L><<<dim3(grid), dim3(64 * kWaves), 0, s>>>(                  \
+        A, Wpacked, absmax, codebook, bias, M, N, K, bs_log2, m_blocks, n_blocks, ksplit, spp, C, \
+        c_dt)
+    if (bm == 64) {
+        if (wl) Q4_TILED_KS(4, 1);
+        else Q4_TILED_KS(4, 0);
+    } else {
+        if (wl) Q4_TILED_KS(2, 1);
+        else Q4_TILED_KS(2, 0);
+    }
+#undef Q4_TILED_KS
     return hipGetLastError();
 }
 
