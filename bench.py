@@ -323,8 +323,12 @@ def headline(d, args):
     # 30.3 us, then 25.2-26.1 us for the same launches timed again, in any
     # order of M), so one pass over the M values is timed and discarded.
     d.time_launches([lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)
-    per_m_us = dict(zip(M_list, d.time_launches(
-        [lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)))
+    # Then four passes over the M values, each M's launch time the mean of
+    # its four (one pass alone varied by ~1 us between the M = 1 and M = 4
+    # launches, which run the same kernel).
+    passes = [d.time_launches([lambda i, M=M: launch(M, i) for M in M_list], reps=12 * R)
+              for _ in range(4)]
+    per_m_us = {M: sum(p[x] for p in passes) / len(passes) for x, M in enumerate(M_list)}
     # (not with --quick: profiling runs launch one layout only)
     other = "rows" if args.layout == "tiles" else "tiles"
     other_us = {} if args.quick else dict(zip(M_list, d.time_launches(
