@@ -23,18 +23,17 @@
 // tiles through LDS in a fixed order (deterministic, no atomics).
 //
 // Up to 16 token rows (the skinny case and the split path's slabs of 16) take
-// the streaming kernel: each wave keeps kRing steps of weights (1 KiB per step)
-// and their activations in flight in a register ring, with buffer loads whose
-// hardware range check returns zeros past the end of a buffer, so absent token
-// rows, weight rows past N and steps past the wave's share of K cost no memory
-// traffic and need no branches.  Wider slabs take the plain kernel below.
-//
-// The streaming kernel also reads weights in this library's tile layout
-// (bf16_repack_tiles): the 16 rows x 32 k one instruction consumes stored as
-// one contiguous 1 KiB unit in lane order, so each load instruction reads
-// 1 KiB of contiguous memory instead of 64-byte pieces of 16 rows.  Lanes
-// receive the same values in the same registers, so the results are
-// bit-identical to the row-major call.
+// one of two streaming kernels, which use buffer loads whose hardware range
+// check returns zeros past the end of a buffer, so absent token rows, weight
+// rows past N and steps past the wave's share of K cost no memory traffic
+// and need no branches.  Over this library's tile layout (bf16_repack_tiles:
+// the 16 rows x 32 k one instruction consumes stored as one contiguous 1 KiB
+// unit in lane order) each wave keeps kRing steps of weights and their
+// activations in flight in a register ring, one 1 KiB load per step.  Over
+// row-major weights each load instruction reads whole 512-byte runs of two
+// rows, and the wave reorders them through LDS into the same operands.
+// Lanes receive the same values in the same registers in both, so the two
+// layouts give bit-identical results.  Wider slabs take the plain kernel.
 //
 // fp16 activations (split path of the 4-bit GEMM) are split exactly into
 // bf16 hi + lo and take two MFMAs per step.  The bias (optional) has the
@@ -70,12 +69,12 @@ __device__ __forceinline__ floatx4 mfma_step(uint4 av, uint4 wv, floatx4 acc) {
     }
 }
 
-// Streaming kernel for M <= 16: wave (tile, k part) as in bf16_gemm_kernel,
-// every step one 16-byte weight load and one 16-byte activation load per
-// lane, kRing steps ahead of the MFMA that consumes them.  WL = 1: weights in
-// the tile layout (unit (tile, step) at (tile * K/32 + step) * 1 KiB, lane l's
-// 16 bytes at 16 l; needs N % 16 == 0 and K % 32 == 0).
-template <int AT, int WL>
+// Streaming kernel for M <= 16 over the tile layout (unit (tile, step) at
+// (tile * K/32 + step) * 1 KiB, lane l's 16 bytes at 16 l; needs N % 16 == 0
+// and K % 32 == 0): wave (tile, k part) as in bf16_gemm_kernel, every step
+// one 16-byte weight load and one 16-byte activation load per lane, kRing
+// steps ahead of the MFMA that consumes them.
+template <int AT>
 __global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
     const void *__restrict__ bias, int M, int N, int K, int ksplit,
@@ -96,27 +95,21 @@ __global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
 
     const __amdgpu_buffer_rsrc_t wres = make_rsrc(W, (uint32_t)N * (uint32_t)K * 2);
     const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
-    // rows past N and tokens past M lie beyond their buffers
-    const uint32_t w_row = (uint32_t)(n0 + j) * (uint32_t)K * 2;
+    // tokens past M lie beyond the activations
     const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;
     auto offs = [&](int st, uint32_t row) -> uint32_t {
         const uint32_t k = (uint32_t)(st << 5) + (uint32_t)(g << 3);
         return (st < s_end && k < (uint32_t)K) ? row + 2 * k : kPastEnd;
     };
-    // tiles past the last one lie beyond the buffer as well
+    // tiles past the last one lie beyond the weights as well
     const uint32_t w_tile = (uint32_t)tile * (uint32_t)K * 32u + (uint32_t)lane * 16u;
     auto woffs = [&](int st) -> uint32_t {
-        if constexpr (WL == 1)
-            return st < s_end ? w_tile + ((uint32_t)st << 10) : kPastEnd;
-        else
-            return offs(st, w_row);
+        return st < s_end ? w_tile + ((uint32_t)st << 10) : kPastEnd;
     };
-    // Over tiles each weight load reads 1 KiB of contiguous memory once: the
-    // non-temporal hint (cache policy bit 1) measured 9-11 % faster there
-    // (K = 2560, N = 16384 / 31040 / 248320, M = 1 and 5).  Over rows a load
-    // reads 64-byte halves of 128-byte lines and the hint made the second
-    // half miss, so rows load without it.
-    constexpr int kWPolicy = WL == 1 ? 2 : 0;
+    // Each weight load reads 1 KiB of contiguous memory once: the
+    // non-temporal hint (cache policy bit 1) measured 9-11 % faster
+    // (K = 2560, N = 16384 / 31040 / 248320, M = 1 and 5).
+    constexpr int kWPolicy = 2;
     uint4 wv[kRing], av[kRing];
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
@@ -135,6 +128,118 @@ __global__ __launch_bounds__(kThreads) void bf16_stream_kernel(
             // keep each refill right after the MFMA that frees its registers,
             // so every step waits only for loads issued kRing steps earlier
             __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if (ksplit > 1) {
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (kpart != 0) return;
+        for (int p = 1; p < ksplit; ++p) {
+            const floatx4 o = red[wave + p][lane];
+            acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+        }
+    }
+    if (n0 + j >= N) return;
+    const float b = bias ? load_elem(bias, n0 + j, c_dt) : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tok = g * 4 + r;
+        if (tok < M) store_elem(C, (size_t)tok * N + n0 + j, acc[r] + b, c_dt);
+    }
+}
+
+// Row-major weights staged through LDS, for M <= 16.  The operand layout
+// wants 16 rows x 64 bytes per load instruction, which reads each 128-byte
+// line in two halves from two instructions; here every load instruction
+// reads whole 512-byte runs of two rows instead (lane l of load i takes 16
+// bytes of chunk row 2i + l / 32 at 16 (l % 32)), the wave writes them into
+// its own LDS region and reads them back in operand order.  A chunk is
+// kChunk = 8 steps of 32 k: 16 rows x 512 bytes, 8 KiB, one chunk of loads
+// in flight per wave.  Piece p (16 bytes) of chunk row r sits in slot
+// 32 r + (p & 16) + ((p + r) & 15): the 16 lanes of a load that share a row,
+// and the 16 lanes of an operand read that share a piece, fall in 16
+// different 16-byte bank groups.  Each weight byte is read once, whole lines
+// at a time, so the loads carry the non-temporal hint.  Every lane ends with
+// the same operands in the same MFMA order as bf16_stream_kernel (steps past
+// the wave's part included, with zero operands), so the results are
+// bit-identical to it and to the tile-layout call.
+constexpr int kChunk = 8;
+
+template <int AT>
+__global__ __launch_bounds__(kThreads) void bf16_rows_lds_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W,
+    const void *__restrict__ bias, int M, int N, int K, int ksplit,
+    void *__restrict__ C, int c_dt) {
+    constexpr int PPR = 4 * kChunk;  // 16-byte pieces per chunk row
+    __shared__ uint4 stage[kWaves][16 * PPR];
+    __shared__ floatx4 red[kWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tiles_per_block = kWaves / ksplit;
+    const int tile = blockIdx.x * tiles_per_block + wave / ksplit;
+    const int kpart = wave % ksplit;
+    const int n0 = tile * 16;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    const int steps = (K + 31) >> 5;
+    const int s_begin = (kpart * steps) / ksplit;
+    const int s_end = ((kpart + 1) * steps) / ksplit;
+    const int nch = (s_end - s_begin + kChunk - 1) / kChunk;
+
+    const __amdgpu_buffer_rsrc_t wres = make_rsrc(W, (uint32_t)N * (uint32_t)K * 2);
+    const __amdgpu_buffer_rsrc_t ares = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2);
+    // Loads: lane l of load i reads piece lp = l % 32 of chunk row 2i + l / 32
+    // (rows past N lie beyond the buffer and read zeros).
+    const int lp = lane & 31, lr = lane >> 5;
+    const uint32_t w_lane = (uint32_t)(n0 + lr) * (uint32_t)K * 2 + 16u * (uint32_t)lp;
+    const uint32_t w_load_step = 2u * (uint32_t)K * 2;  // two rows per load
+    // Chunk c of the wave's part: the lane's offset for load 0, or past the
+    // end when its step lies past the part or its k past K.  Past the end
+    // plus up to 7 row pairs stays past the end and below 2^32 (callers keep
+    // 16 rows of K below 2^31 bytes).
+    auto w_off = [&](int c) -> uint32_t {
+        const int st0 = s_begin + c * kChunk;
+        const uint32_t k = (uint32_t)st0 * 32u + 8u * (uint32_t)lp;
+        return (st0 + (lp >> 2) < s_end && k < (uint32_t)K) ? w_lane + 2u * (uint32_t)st0 * 32u
+                                                           : kPastEnd;
+    };
+    // Activations of step st: token j's 8 values at k = 32 st + 8 g.
+    const uint32_t a_row = (uint32_t)j * (uint32_t)K * 2;
+    auto a_off = [&](int st) -> uint32_t {
+        const uint32_t k = (uint32_t)(st << 5) + (uint32_t)(g << 3);
+        return (st < s_end && k < (uint32_t)K) ? a_row + 2 * k : kPastEnd;
+    };
+    uint4 *my = stage[wave];
+    auto slot = [](int r, int p) { return r * PPR + (p & 16) + ((p + r) & 15); };
+
+    uint4 wv[kChunk], av[kChunk];
+    auto load_w = [&](int c) {
+        const uint32_t o = w_off(c);
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            wv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                wres, (int)(o + (uint32_t)i * w_load_step), 0, 2));
+    };
+    load_w(0);
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s)
+        av[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, (int)a_off(s_begin + s), 0, 0));
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nch; ++c) {
+        // LDS operations of one wave run in order: these writes follow the
+        // previous chunk's reads, and the reads below see these writes.
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) my[slot(2 * i + lr, lp)] = wv[i];
+        load_w(c + 1);
+        // each step's activation registers are refilled for the next chunk
+        // right after the MFMA that reads them
+#pragma unroll
+        for (int s = 0; s < kChunk; ++s) {
+            acc = mfma_step<AT>(av[s], my[slot(j, 4 * s + g)], acc);
+            av[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                ares, (int)a_off(s_begin + (c + 1) * kChunk + s), 0, 0));
         }
     }
 
@@ -246,11 +351,11 @@ hipError_t launch_mt(const uint16_t *A, const uint16_t *W, const void *bias, int
     if (wl) {
         // the tile layout is read by the streaming kernel only
         if (AT != kBf16 || !stream || N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
-        bf16_stream_kernel<kBf16, 1><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
+        bf16_stream_kernel<kBf16><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
                                                                              ksplit, C, c_dt);
     } else if (stream)
-        bf16_stream_kernel<AT, 0><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
-                                                                          ksplit, C, c_dt);
+        bf16_rows_lds_kernel<AT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
+                                                                            ksplit, C, c_dt);
     else
         bf16_gemm_kernel<AT, MT><<<dim3(blocks), dim3(kThreads), 0, s>>>(A, W, bias, M, N, K,
                                                                          ksplit, C, c_dt);

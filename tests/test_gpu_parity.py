@@ -337,6 +337,22 @@ def test_bf16_skinny_parity(M, N, K, with_bias):
     assert_within_tolerance(bf16_host(C), Cr, S, "bf16 M=%d N=%d K=%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("N,K", [(160, 3016), (16, 264), (4096, 8200)])
+def test_bf16_skinny_rows_chunks_and_k_parts(M, N, K):
+    """Row-major weights are read in 8-step chunks per K part: parts that
+    start inside a chunk (K = 3016: 95 steps over 4 parts), a last step with
+    one live lane group (3016 = 94*32 + 8), a single chunk (264), and one
+    part per tile on 256 tiles (4096 x 8200)."""
+    p = synth.bf16_problem(M, N, K, True, config=63, shape=N % 3)
+    A, W = to_dev(p["A"], "bf16"), to_dev(p["W"], "bf16")
+    b = to_dev(p["bias"], "bf16")
+    C = q4.bf16_gemm_skinny(A, W, b)
+    _sync()
+    Cr, S = oracle.bf16_gemm(p["A"], p["W"], p["bias"], M, N, K)
+    assert_within_tolerance(bf16_host(C), Cr, S, "bf16 rows M=%d N=%d K=%d" % (M, N, K))
+
+
 def test_bf16_skinny_rejects_six_tokens():
     t = torch()
     d = dev()
