@@ -267,10 +267,10 @@ q4_status bf16_gemm_skinny(const void *A, const void *W, const void *bias, int M
  * elements of (t, s) are one 1 KiB unit at element (t * K/32 + s) * 512;
  * piece l = 0..63 of a unit (8 elements) holds k = 32s + 8*(l/16) .. +7 of
  * row 16t + l % 16, the 16 bytes matrix-core lane l takes for that step.
- * Each load instruction then reads 1 KiB of contiguous memory instead of
- * 64-byte pieces of 16 rows 2*K bytes apart (on MI355X 8-16 % faster on the
- * K = 2560 shapes).  Requires N % 16 == 0, K % 32 == 0 and (N + 64)*K*2
- * below 2 GiB.
+ * Each load instruction then reads 1 KiB of contiguous memory in operand
+ * order, with no reordering pass (the row-major call reorders its loads
+ * through LDS; on MI355X the tile layout is 3-9 % faster on the K = 2560
+ * shapes).  Requires N % 16 == 0, K % 32 == 0 and (N + 64)*K*2 below 2 GiB.
  */
 
 /*
