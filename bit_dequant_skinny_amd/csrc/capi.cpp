@@ -363,9 +363,10 @@ q4_status run_fused_planes(const void *A, int a_dt, const uint8_t *Wp, const flo
 // bf16 activations: the tiled kernel above fused_tiled_min_m rows, else the
 // skinny kernels in passes of up to Q4_FUSED_PASS_M token rows over
 // consecutive row slabs, each streaming the packed weights once more (more
-// than one pass only where the tiled kernel cannot run).  Up to 16 rows the
-// skinny kernel may split K over workgroups (kparts_ok: the workspace is
-// free for its partial sums, i.e. not holding activation planes).
+// than one pass only where the tiled kernel cannot run).  Up to 32 rows (one
+// pass) the skinny kernel may split K over workgroups (kparts_ok: the
+// workspace is free for its partial sums, i.e. not holding activation
+// planes).
 q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am, const float *cb,
                     const void *bias, int M, int N, int K, int bs_log2, int wl, void *C, int c_dt,
                     hipStream_t s, bool kparts_ok = true) {
@@ -392,7 +393,7 @@ q4_status run_fused(const void *A, int a_dt, const uint8_t *Wp, const float *am,
         });
     }
     float *kpart = nullptr;
-    if (kparts_ok && a_dt == Q4_DTYPE_BF16 && bs_log2 >= 6 && M <= 16 &&
+    if (kparts_ok && a_dt == Q4_DTYPE_BF16 && bs_log2 >= 6 && M <= 32 &&
         q4::q4_fused_mfma_fits(M, N, K)) {
         const int ks = q4::q4_fused_kparts(M, N, K);
         if (ks > 1) {
@@ -881,7 +882,7 @@ q4_status q4_set_crossover_shape(int N, int K, int m) {
 int q4_get_crossover_shape(int N, int K) { return crossover_for(N, K); }
 
 int q4_skinny_kparts(int M, int N, int K) {
-    if (M < 1 || M > 16 || N < 1 || K < 1) return 1;
+    if (M < 1 || M > 32 || N < 1 || K < 1) return 1;
     return q4::q4_fused_kparts(M, N, K);
 }
 

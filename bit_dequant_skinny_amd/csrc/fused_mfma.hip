@@ -648,7 +648,7 @@ __global__ __launch_bounds__(64 * KW) void fused_mfma_kernel(
                     const int n = (int)((grp + (uint32_t)tr * (uint32_t)groups) * 16) + j;
                     const int tok = MB == 1 ? 4 * r + g : 16 * b + 4 * g + r;
                     if (n < N && tok < M) {
-                        if (MB == 1 && ks > 1) {
+                        if (ks > 1) {
                             kpart[((size_t)kpart_ix * M + tok) * N + n] = v;  // this part's sum
                         } else {
                             if (bias) v += load_elem(bias, n, c_dt);  // before the single rounding
@@ -677,25 +677,27 @@ struct SkinnyPlan {
 };
 
 // Without K parts a workgroup walks ceil(groups / CUs) chunks of tb tiles
-// times ceil(segments / 8) slots.  With up to 16 token rows, K parts are
-// used when some (tb, ks) with groups * ks <= CUs (one chunk per workgroup)
-// saves at least 8 units per wave and 20 % of them: the second launch that
-// adds the parts costs about as much as 4 units (a unit is ~0.42 us at
-// 17408 x 5120), so 17408 x 5120 goes from 34 to 24 units per wave while
-// 5120 x 5120 (10 to 7) keeps one part.  Parts are whole slots of the 8
-// waves (spp a multiple of 8 segments), so every part starts on a scale
-// block boundary for blocksizes up to 1024.
+// times ceil(segments / 8) slots.  With up to 32 token rows in one pass, K
+// parts are used when some (tb, ks) with groups * ks <= CUs (one chunk per
+// workgroup) saves at least 8 units per wave and 20 % of them: the second
+// launch that adds the parts costs about as much as 4 units (a unit is
+// ~0.42 us at 17408 x 5120 with one token block), so 17408 x 5120 goes from
+// 34 to 24 units per wave while 5120 x 5120 (10 to 7) keeps one part.  Two
+// token blocks (17..32 rows) take the same plans without 8-tile chunks
+// (which run as two 16-row passes).  Parts are whole slots of the 8 waves
+// (spp a multiple of 8 segments), so every part starts on a scale block
+// boundary for blocksizes up to 1024.
 SkinnyPlan skinny_plan(int M, int N, int K) {
     const int tb0 = tiles_per_chunk(N);
     const int nseg = (K + 127) / 128;
     SkinnyPlan plan{tb0, 1, nseg};
-    if (M > 16) return plan;  // two token blocks: one part
+    if (M > 32 || (M > 16 && tb0 >= 8)) return plan;  // 8-tile chunks run 16-row passes
     const int tiles = (N + 15) / 16;
     const int cus = device_info().num_cus;
     const long groups0 = (tiles + tb0 - 1) / tb0;
     const long base = (groups0 + cus - 1) / cus * tb0 * ((nseg + KW - 1) / KW);
     long best = base;
-    for (int tb = 1; tb <= 8; ++tb)
+    for (int tb = 1; tb <= (M > 16 ? 7 : 8); ++tb)
         for (int ks = 2; ks <= 8; ++ks) {
             const int per = (nseg + ks - 1) / ks;
             const int spp = (per + KW - 1) / KW * KW;
@@ -729,7 +731,7 @@ hipError_t launch_tb(const uint16_t *A, const uint8_t *Wp, const float *absmax,
     // loop iterations.
     const int spw = (plan.spp + KW - 1) / KW;
     if (groups > G && spw % UF != 0) return hipErrorInvalidValue;
-    if (plan.ks > 1 && (MB != 1 || G != groups * plan.ks || !kpart || np != 1))
+    if (plan.ks > 1 && (G != groups * plan.ks || !kpart || np != 1))
         return hipErrorInvalidValue;
     if (np > 1 && MB != 1) return hipErrorInvalidValue;
 #define Q4_LAUNCH_KERNEL(B, L)                                                          \
@@ -833,7 +835,7 @@ hipError_t launch_q4_fused(const void *A, int a_dt, const uint8_t *Wpacked, cons
     if (wl && !mfma) return hipErrorInvalidValue;  // the vector-ALU kernel reads rows
     if (mfma && (M <= 16 || tiles_per_chunk(N) < 8))
         return launch_q4_fused_mfma(A, a_dt, Wpacked, absmax, codebook, bias, M, N, K, bs_log2,
-                                    C, c_dt, wl, s, M <= 16 ? kpart : nullptr, 1);
+                                    C, c_dt, wl, s, kpart, 1);
     const size_t a_row = (size_t)K * (a_dt == kF32 ? 4 : 2);
     const size_t c_row = (size_t)N * (c_dt == kF32 ? 4 : 2);
     for (int m0 = 0; m0 < M; m0 += 16) {

@@ -417,8 +417,9 @@ int q4_get_crossover_shape(int N, int K);
 
 /*
  * q4_skinny_kparts: how many parts the fused skinny kernel cuts K into for
- * M bf16 token rows (1..16) and an N x K weight on the current device (1 =
- * none; 1 for arguments outside those ranges).  The pages' kernel gives each
+ * M bf16 token rows (1..32) and an N x K weight on the current device (1 =
+ * none; 1 for arguments outside those ranges, and for 17..32 rows where
+ * they run as two 16-row passes).  The pages' kernel gives each
  * output row to one thread group over all of K (bitsandbytes pull request
  * "[ROCm] Optimize kgemm_4bit_inference_naive ...", section "Technical
  * details"); here a row's K may be split over workgroups when the 16-row

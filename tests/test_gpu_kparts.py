@@ -26,8 +26,10 @@ CB = synth.random_codebook(77)
 @pytest.mark.parametrize("M,N,K,parts", [
     (1, 5120, 17408, 3), (16, 5120, 17408, 3), (1, 5120, 5120, 1), (8, 5120, 5120, 1),
     (1, 28672, 8192, 1), (1, 8192, 5120, 1), (1, 8192, 8192, 1), (1, 4096, 4096, 1),
-    (1, 248320, 2560, 1), (17, 5120, 17408, 1), (1, 1536, 16384, 8), (1, 1536, 16448, 5),
-    (1, 768, 32768, 5), (0, 5120, 17408, 1), (1, 0, 17408, 1),
+    (1, 248320, 2560, 1), (17, 5120, 17408, 3), (32, 5120, 17408, 3), (33, 5120, 17408, 1),
+    (24, 248320, 2560, 1), (17, 1536, 16384, 8), (32, 768, 32768, 5), (20, 1544, 16384, 2),
+    (1, 1536, 16384, 8), (1, 1536, 16448, 5), (1, 768, 32768, 5), (0, 5120, 17408, 1),
+    (1, 0, 17408, 1),
 ])
 def test_kparts_plan(M, N, K, parts):
     assert q4.q4_skinny_kparts(M, N, K) == parts
@@ -49,6 +51,8 @@ def _problem(M, N, K, bs, config):
 @pytest.mark.parametrize("M,N,K,bs", [
     (1, 1536, 16384, 64), (4, 1536, 16384, 64), (16, 768, 32768, 64), (1, 1536, 16448, 64),
     (3, 1536, 16512, 128), (2, 1536, 16384, 256), (5, 768, 32768, 64), (2, 1544, 16384, 64),
+    (17, 1536, 16384, 64), (32, 768, 32768, 64), (20, 1544, 16384, 64), (32, 1536, 16448, 64),
+    (24, 1536, 16512, 128),
 ])
 def test_kparts_parity(M, N, K, bs, layout):
     g = _gpu()
@@ -65,10 +69,11 @@ def test_kparts_parity(M, N, K, bs, layout):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("cdt", ["bf16", "fp16", "fp32"])
-def test_kparts_bias_and_output_types(cdt):
+@pytest.mark.parametrize("M", [3, 24])
+def test_kparts_bias_and_output_types(cdt, M):
     g = _gpu()
     t = g.torch()
-    M, N, K, bs = 3, 1536, 16384, 64
+    N, K, bs = 1536, 16384, 64
     assert q4.q4_skinny_kparts(M, N, K) > 1
     p, (A, Wp, am, cb) = _problem(M, N, K, bs, 710)
     b_h = synth.bias(N, 711, cdt)
@@ -78,7 +83,8 @@ def test_kparts_bias_and_output_types(cdt):
     t.cuda.synchronize()
     Cr, S = oracle.q4_gemm_ex(p["A"], "bf16", p["Wpacked"], p["absmax"], p["codebook"], M, N, K,
                               bs, bias=b_h, bias_dtype=cdt)
-    g.assert_within_tolerance(None, Cr, S, "kparts bias %s" % cdt, out=cdt, values=g.host_f64(C))
+    g.assert_within_tolerance(None, Cr, S, "kparts bias %s M=%d" % (cdt, M), out=cdt,
+                              values=g.host_f64(C))
 
 
 @pytest.mark.gpu
@@ -104,7 +110,8 @@ def test_kparts_special_scales():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M,N,K", [(1, 5120, 17408), (16, 5120, 17408)])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 17408), (16, 5120, 17408), (17, 5120, 17408),
+                                   (32, 5120, 17408)])
 def test_kparts_deterministic_and_layouts_agree(M, N, K):
     g = _gpu()
     t = g.torch()
@@ -125,6 +132,25 @@ def test_kparts_deterministic_and_layouts_agree(M, N, K):
                            cols=cols)
     for name, runs in (("rows", rows), ("tiles", tiles)):
         g.assert_within_tolerance(g.bf16_host(runs[0])[:, cols], Cr, S, "kparts full size " + name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [20, 32])
+def test_kparts_two_token_blocks_equal_16_row_passes(M):
+    """With K parts, rows 0..15 and 16..M-1 in one two-block pass equal two
+    separate calls bit for bit (same plan, same MFMA sequence per output, the
+    parts added in the same order)."""
+    g = _gpu()
+    N, K, bs = 5120, 17408, 64
+    assert q4.q4_skinny_kparts(M, N, K) == q4.q4_skinny_kparts(16, N, K) > 1
+    A = g.to_dev(synth.activations_bf16(M, K, 751), "bf16")
+    Wp_h, am_h, cb_h = g.q4_weights(N, K, bs, 75, 1)
+    Wp, am, cb = g.to_dev(Wp_h, "u8"), g.to_dev(am_h, "f32"), g.to_dev(cb_h, "f32")
+    C = g.bf16_host(q4.q4_gemm_skinny(A, Wp, am, cb, bs, path="fused"))
+    C0 = g.bf16_host(q4.q4_gemm_skinny(A[:16].contiguous(), Wp, am, cb, bs, path="fused"))
+    C1 = g.bf16_host(q4.q4_gemm_skinny(A[16:].contiguous(), Wp, am, cb, bs, path="fused"))
+    g.torch().cuda.synchronize()
+    assert np.array_equal(C, np.concatenate([C0, C1], axis=0))
 
 
 @pytest.mark.gpu
