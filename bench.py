@@ -640,7 +640,7 @@ def profile_case(d, which, launches=12):
     """A few launches of one call for counter and trace runs: the split path
     (dequantize + bf16 GEMM) on the FFN at M = 16 and 256, or the bf16 skinny
     GEMM on the 248320 x 2560 projection at M = 1 (row-major or tile layout),
-    or the fused skinny kernel with K parts on 5120 x 17408 at M = 1;
+    or the fused skinny kernel with K parts on 5120 x 17408 at M = 1 or 32;
     weights rotate as in the timed runs."""
     import bit_dequant_skinny_amd as q4
     t = d.t
@@ -655,9 +655,10 @@ def profile_case(d, which, launches=12):
         for i in range(launches):
             Wp, am = sets[i % len(sets)]
             q4.q4_gemm_skinny(A, Wp, am, cb, BS, out=C, path="split")
-    elif which == "kparts":
+    elif which in ("kparts", "kparts32"):
         # the skinny kernel with K split over workgroups, then the part sum
-        N, K, M = 5120, 17408, 1
+        # (kparts32: 32 token rows, two token blocks per pass)
+        N, K, M = 5120, 17408, 32 if which == "kparts32" else 1
         p = synth.q4_problem(1, N, K, BS, config=2, shape=2)
         sets = d.copies((q4.q4_repack_tiles(d.raw(p["Wpacked"])), d.raw(p["absmax"])),
                         q4_bytes(1, N, K))
@@ -697,7 +698,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy kernel (counter calibration)")
     ap.add_argument("--profile-case",
-                    choices=("split16", "split256", "bf16c5", "bf16c5tiles", "kparts"),
+                    choices=("split16", "split256", "bf16c5", "bf16c5tiles", "kparts", "kparts32"),
                     help="only run a few launches of one call (for rocprofv3 runs)")
     args = ap.parse_args()
     if args.gpus != 1:
