@@ -66,8 +66,10 @@ CASES = [
     ((16, 1024, 2048, "bf16", "bf16", "split", False), (4, 256, 1024, "bf16", "bf16", "split", False)),
     ((200, 256, 4096, "bf16", "bf16", "fused", True), (70, 128, 2048, "bf16", "bf16", "fused", True)),
     ((4, 1024, 4096, "bf16", "bf16", "fused", False), (1, 512, 1024, "bf16", "bf16", "fused", False)),
-    # the skinny kernel's K parts: their fp32 sums in the array
+    # the skinny kernel's K parts: their fp32 sums in the array (also for a
+    # pass of two token blocks, then a one-block call)
     ((4, 1536, 16384, "bf16", "bf16", "fused", True), (1, 1536, 16448, "bf16", "fp32", "fused", False)),
+    ((24, 1536, 16384, "bf16", "bf16", "fused", True), (3, 1536, 16384, "bf16", "bf16", "fused", True)),
 ]
 
 
