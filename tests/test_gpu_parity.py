@@ -226,7 +226,8 @@ def test_split_parity(M, N, K, bs):
     # against the bf16-weight diagnostic: only fp32 accumulation and output rounding differ
     C7, S7 = oracle.q4_gemm_w16(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
     assert_within_tolerance(got, C7, S7, "split vs bf16-weight oracle")
-    # against the judged reference: bf16 weight rounding passes on random data
+    # against the fp32-weight reference the tolerance is stated on: the bf16
+    # weight rounding stays inside it on random data
     Cr, S = oracle.q4_gemm(p["A"], p["Wpacked"], p["absmax"], p["codebook"], M, N, K, bs)
     assert_within_tolerance(got, Cr, S, "split vs fused oracle")
 
