@@ -130,7 +130,7 @@ void oracle_dequant_bf16(const uint8_t *Wpacked, const float *absmax, const floa
             out[n * K + k] = oracle_f32_to_bf16(oracle_w32(Wpacked, absmax, codebook, K, bs, n, k));
 }
 
-/* ---- O5: the fused 4-bit GEMM, judged reference ------------------------- */
+/* ---- O5: the fused 4-bit GEMM, the reference of the tolerance ------------ */
 /* C[m, j] = sum over k of a[m,k] * w32(cols[j], k), summed in fp64 in
  * increasing k.  Every product is exact in fp64 (8-bit by 24-bit
  * significands), so the only rounding is in the running fp64 sum.  S[m, j] is
